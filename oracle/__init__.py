@@ -1,0 +1,181 @@
+"""Python loader for the CPU oracle (``moe_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the package smoke check and the
+benchmark's CPU-baseline leg are the only callers.  The oracle shares no
+code with the GPU library and never imports it.
+
+All floating-point arrays handed to the oracle are float64 copies of the
+exact bf16 / float32 inputs (see ``synth.bf16_bits_to_f64``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("D", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("score", ctypes.c_int32)]
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = ctypes.CDLL(_LIB)
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise RuntimeError(f"oracle {what} failed with status {rc}")
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+class Layer:
+    """One layer's inputs in float64 plus its dimensions.
+
+    x, dy: [T, D]; w_gate, w_up: [E, I, D]; w_down: [E, D, I].
+    """
+
+    def __init__(self, x, w_gate, w_up, w_down, K: int, score: int, dy=None):
+        self.x = _f64(x)
+        self.w_gate = _f64(w_gate)
+        self.w_up = _f64(w_up)
+        self.w_down = _f64(w_down)
+        self.dy = None if dy is None else _f64(dy)
+        T, D = self.x.shape
+        E, I, D2 = self.w_gate.shape
+        assert D2 == D and self.w_up.shape == (E, I, D) and self.w_down.shape == (E, D, I)
+        self.T, self.D, self.I, self.E, self.K, self.score = T, D, I, E, K, score
+
+    def dims(self, T=None) -> _Dims:
+        return _Dims(self.T if T is None else T, self.D, self.I, self.E, self.K, self.score)
+
+
+def route(logits: np.ndarray, K: int, score: int):
+    """Top-K selection and router weights -> (idx int32 [T,K], w float64 [T,K])."""
+    lib = _load()
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    d = _Dims(T, 1, 1, E, K, score)
+    idx = np.empty((T, K), dtype=np.int32)
+    w = np.empty((T, K), dtype=np.float64)
+    _check(lib.moe_oracle_route(ctypes.byref(d), _p(logits), _p(idx), _p(w)), "route")
+    return idx, w
+
+
+def sort(idx: np.ndarray, E: int):
+    """Stable sort by expert -> (counts [E], offsets [E+1], sorted_to_flat, flat_to_sorted)."""
+    lib = _load()
+    idx = _i32(idx)
+    T, K = idx.shape
+    d = _Dims(T, 1, 1, E, K, 0)
+    counts = np.empty(E, dtype=np.int32)
+    offsets = np.empty(E + 1, dtype=np.int32)
+    s2f = np.empty(T * K, dtype=np.int32)
+    f2s = np.empty(T * K, dtype=np.int32)
+    _check(lib.moe_oracle_sort(ctypes.byref(d), _p(idx), _p(counts), _p(offsets), _p(s2f),
+                               _p(f2s)), "sort")
+    return counts, offsets, s2f, f2s
+
+
+def _tokens(tokens):
+    if tokens is None:
+        return None, 0
+    t = np.ascontiguousarray(tokens, dtype=np.int64)
+    return t, t.size
+
+
+def forward(L: Layer, idx, w, tokens=None, want_o: bool = False):
+    """y [ntok, D] (and o [ntok, K, D] if want_o) for the given tokens (None = all)."""
+    lib = _load()
+    idx, w = _i32(idx), _f64(w)
+    tok, n = _tokens(tokens)
+    n = L.T if tok is None else n
+    y = np.empty((n, L.D), dtype=np.float64)
+    o = np.empty((n, L.K, L.D), dtype=np.float64) if want_o else None
+    d = L.dims()
+    _check(lib.moe_oracle_forward(ctypes.byref(d), _p(L.x), _p(L.w_gate), _p(L.w_up),
+                                  _p(L.w_down), _p(idx), _p(w), ctypes.c_int64(n), _p(tok),
+                                  _p(y), _p(o)), "forward")
+    return (y, o) if want_o else y
+
+
+def backward_tokens(L: Layer, idx, w, tokens=None):
+    """dX [ntok, D] and dRouterWeights [ntok, K] for the given tokens (None = all)."""
+    lib = _load()
+    idx, w = _i32(idx), _f64(w)
+    tok, n = _tokens(tokens)
+    n = L.T if tok is None else n
+    dx = np.empty((n, L.D), dtype=np.float64)
+    drw = np.empty((n, L.K), dtype=np.float64)
+    d = L.dims()
+    _check(lib.moe_oracle_backward_tokens(ctypes.byref(d), _p(L.x), _p(L.w_gate), _p(L.w_up),
+                                          _p(L.w_down), _p(idx), _p(w), _p(L.dy),
+                                          ctypes.c_int64(n), _p(tok), _p(dx), _p(drw)),
+           "backward_tokens")
+    return dx, drw
+
+
+def backward_dw(L: Layer, idx, w, tokens=None):
+    """(dW_gate [E,I,D], dW_up [E,I,D], dW_down [E,D,I]) over the given tokens (None = all)."""
+    lib = _load()
+    idx, w = _i32(idx), _f64(w)
+    tok, n = _tokens(tokens)
+    n = L.T if tok is None else n
+    dwg = np.empty((L.E, L.I, L.D), dtype=np.float64)
+    dwu = np.empty((L.E, L.I, L.D), dtype=np.float64)
+    dwd = np.empty((L.E, L.D, L.I), dtype=np.float64)
+    d = L.dims()
+    _check(lib.moe_oracle_backward_dw(ctypes.byref(d), _p(L.x), _p(L.w_gate), _p(L.w_up),
+                                      _p(L.w_down), _p(idx), _p(w), _p(L.dy),
+                                      ctypes.c_int64(n), _p(tok), _p(dwg), _p(dwu), _p(dwd)),
+           "backward_dw")
+    return dwg, dwu, dwd
+
+
+def dw_entries(L: Layer, idx, w, which, e, r, c):
+    """Single weight-gradient entries: which 0 = dW_gate[e,r,c], 1 = dW_up, 2 = dW_down."""
+    lib = _load()
+    idx, w = _i32(idx), _f64(w)
+    which, e, r, c = (_i32(np.atleast_1d(v)) for v in (which, e, r, c))
+    n = which.size
+    out = np.empty(n, dtype=np.float64)
+    d = L.dims()
+    _check(lib.moe_oracle_dw_entries(ctypes.byref(d), _p(L.x), _p(L.w_gate), _p(L.w_up),
+                                     _p(L.w_down), _p(idx), _p(w), _p(L.dy),
+                                     ctypes.c_int64(n), _p(which), _p(e), _p(r), _p(c),
+                                     _p(out)), "dw_entries")
+    return out
