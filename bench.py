@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed SwiGLU MoE layer on one MI355X.
+
+One step = the whole hot path over one batch: routing + sort by expert,
+forward (gather, gate/up GEMM + SwiGLU, down GEMM, weighted combine) and
+backward (re-gather, recompute, dA + SwiGLU backward, dX GEMM, dW GEMMs,
+dX/dRouterWeights reductions), all through the C ABI on device-resident
+inputs.  Workload: the Qwen3-30B-A3B layer shape (T=8192 tokens, D=2048,
+I=768, E=128 experts, top-8, softmax-renormalised routing), synthetic seeded
+inputs.
+
+value = counted FLOPs per step / step time, with 6*D*I FLOPs per routed row
+forward and 12*D*I backward (the activation recompute is not counted).
+
+Prints ONE JSON line.  Also reports the dominant kernel against its roofline
+(per-kernel durations from HIP events recorded on the launch stream over the
+timed steps) and the CPU oracle timed on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+METRIC = "MoE layer TFLOP/s fwd & bwd, Qwen3-30B-A3B shape, 8192 tokens, 1×MI355X"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak (no sparsity)
+PEAK_HBM_GBPS = 8000.0
+
+WORKLOADS = {"qwen3_30b_a3b": synth.QWEN3_30B_A3B, "llama4_scout": synth.LLAMA4_SCOUT,
+             "tiny": synth.TINY}
+
+
+def kernel_work(wl: synth.Workload) -> dict:
+    """Algorithmic work per launch: ('mfma', FLOPs) for GEMMs, ('hbm', bytes) for the rest."""
+    T, D, I, E, K, R = wl.T, wl.D, wl.I, wl.E, wl.K, wl.R
+    dir_ = float(D) * I * R
+    return {
+        "gemm_gateup_h": ("mfma", 4 * dir_), "gemm_gateup_gu": ("mfma", 4 * dir_),
+        "gemm_down": ("mfma", 2 * dir_), "gemm_da": ("mfma", 2 * dir_),
+        "gemm_dxs": ("mfma", 4 * dir_), "gemm_dw_down": ("mfma", 2 * dir_),
+        "gemm_dw_gateup": ("mfma", 4 * dir_),
+        # gather: read the routed rows of x (R*D*2) and write Xs (R*D*2), plus the index
+        "gather": ("hbm", 4.0 * R * D + 4 * R), "gather2": ("hbm", 8.0 * R * D + 4 * R),
+        # combine: read O (R*D*2), weights and indices (8R), write y (T*D*2)
+        "combine": ("hbm", 2.0 * R * D + 8 * R + 2.0 * T * D),
+        "reduce_rows": ("hbm", 2.0 * R * D + 4 * R + 2.0 * T * D),
+        "reduce_partials": ("hbm", 4.0 * R * (2 * math.ceil(I / 128)) + 8 * R),
+        "route_topk": ("hbm", 4.0 * T * E + 8 * R),
+        "route_hist": ("hbm", 4.0 * R), "route_scan": ("hbm", 8.0 * E),
+        "route_scatter": ("hbm", 12.0 * R), "tilemap": ("hbm", 8.0 * E),
+    }
+
+
+def cpu_baseline(wl: synth.Workload, data: dict, n_tokens: int) -> dict:
+    """The CPU oracle, as it stands, on the first n_tokens tokens of the workload:
+    forward, backward (dX, dRouterWeights) and the weight gradients over those
+    tokens.  Value in the metric's unit, counted with the same FLOP formula."""
+    import oracle
+    f = synth.bf16_bits_to_f64
+    L = oracle.Layer(f(data["x"]), f(data["w_gate"]), f(data["w_up"]), f(data["w_down"]),
+                     wl.K, wl.score, f(data["dy"]))
+    idx, w = oracle.route(data["logits"], wl.K, wl.score)
+    tok = np.arange(n_tokens, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.forward(L, idx, w, tokens=tok)
+    t1 = time.perf_counter()
+    oracle.backward_tokens(L, idx, w, tokens=tok)
+    oracle.backward_dw(L, idx, w, tokens=tok)
+    t2 = time.perf_counter()
+    rows = n_tokens * wl.K
+    flops = 18.0 * wl.D * wl.I * rows
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": flops / (t2 - t0) / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"first {n_tokens} tokens ({rows} routed rows) of the {wl.name} workload: "
+                       f"oracle forward {t1 - t0:.2f} s + backward incl. weight gradients "
+                       f"{t2 - t1:.2f} s, float64, {threads} OpenMP threads")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_30b_a3b", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-tokens", type=int, default=32,
+                    help="tokens in the CPU-oracle baseline sample (0: skip)")
+    ap.add_argument("--fwd-bwd-only", action="store_true",
+                    help="time only the full steps (skip the separate fwd/bwd timing)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not supported "
+              "(no sharding or collectives in this build).", file=sys.stderr)
+        return 2
+
+    import torch
+    import mixture_experts_layer_expert_amd as moe
+    from tests import gpu_common as G
+
+    moe.load_library()
+    wl = WORKLOADS[args.workload]
+    data = synth.generate(wl)
+    dev = G.DeviceInputs(data)
+    d = moe.dims(wl.T, wl.D, wl.I, wl.E, wl.K, wl.score)
+    ws = [torch.empty(moe.moe_workspace_bytes(d, ph), dtype=torch.uint8, device="cuda")
+          for ph in range(3)]
+    route = moe.moe_route_sort(dev.logits, wl.K, wl.score, ws=ws[0])
+    y = torch.empty((wl.T, wl.D), dtype=torch.bfloat16, device="cuda")
+    grads = moe.moe_bwd(dev.x, dev.w_gate, dev.w_up, dev.w_down, route, dev.dy, wl.K, wl.score,
+                        ws=ws[2])
+    stream = torch.cuda.current_stream()
+
+    def step(do_route=True, do_fwd=True, do_bwd=True):
+        if do_route:
+            moe.moe_route_sort(dev.logits, wl.K, wl.score, out=route, ws=ws[0])
+        if do_fwd:
+            moe.moe_fwd(dev.x, dev.w_gate, dev.w_up, dev.w_down, route, wl.K, wl.score, y=y, ws=ws[1])
+        if do_bwd:
+            moe.moe_bwd(dev.x, dev.w_gate, dev.w_up, dev.w_down, route, dev.dy, wl.K, wl.score,
+                        out=grads, ws=ws[2])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"bench: {wl.name} warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    # timed region: K full steps, per-kernel HIP events on the launch stream
+    moe.moe_prof_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = moe.moe_prof_read()
+    moe.moe_prof_enable(False)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    flops_step = wl.flops_fwd() + wl.flops_bwd()
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    # forward-only and backward-only rates (event-timed on the same stream)
+    extra = {}
+    if not args.fwd_bwd_only:
+        for name, kw in (("fwd", dict(do_route=False, do_bwd=False)),
+                         ("bwd", dict(do_route=False, do_fwd=False))):
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(args.steps):
+                step(**kw)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            ms = ev0.elapsed_time(ev1) / args.steps
+            fl = wl.flops_fwd() if name == "fwd" else wl.flops_bwd()
+            extra[f"{name}_ms"] = round(ms, 4)
+            extra[f"{name}_tflops"] = round(fl / (ms * 1e-3) / 1e12, 2)
+
+    work = kernel_work(wl)
+    kernels = {}
+    for name, (tot_ms, n) in kern.items():
+        avg_ms = tot_ms / n
+        bound, amount = work.get(name, ("hbm", 0.0))
+        rate = amount / (avg_ms * 1e-3)
+        if bound == "mfma":
+            kernels[name] = {"avg_us": round(avg_ms * 1e3, 2), "launches": n, "bound": "mfma",
+                             "tflops": round(rate / 1e12, 2),
+                             "frac": round(rate / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        else:
+            kernels[name] = {"avg_us": round(avg_ms * 1e3, 2), "launches": n, "bound": "hbm",
+                             "gbps": round(rate / 1e9, 1),
+                             "frac": round(rate / 1e9 / PEAK_HBM_GBPS, 4)}
+    gemms = {k: v for k, v in kern.items() if work.get(k, ("", 0))[0] == "mfma"}
+    dom = max(gemms, key=lambda k: gemms[k][0])
+    dom_avg_s = gemms[dom][0] / gemms[dom][1] * 1e-3
+    achieved = work[dom][1] / dom_avg_s / 1e12
+    gemm_total_ms = sum(v[0] for v in gemms.values()) / args.steps
+    gemm_flops = sum(work[k][1] * (v[1] / args.steps) for k, v in gemms.items())
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}_fwd_bwd", "T": wl.T, "D": wl.D, "I": wl.I, "E": wl.E,
+                   "K": wl.K, "routing": "softmax_topk_renorm" if wl.score == 0 else "sigmoid",
+                   "seed": wl.seed},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        **extra,
+        "gemm_tflops_all": round(gemm_flops / (gemm_total_ms * 1e-3) / 1e12, 2),
+        "gemm_frac_all": round(gemm_flops / (gemm_total_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kernels": kernels,
+    }
+    if args.cpu_tokens > 0:
+        print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, data, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,169 @@
+/*
+ * moe.h -- C ABI of the routed SwiGLU mixture-of-experts layer on one AMD
+ * Instinct MI355X (gfx950): routing + sort by expert, forward, backward.
+ *
+ * Method: the LigerCute package README (liger-cute-kernels 0.8.3), section
+ * "LigerMoE design" (sub-sections "Forward pass" and "Backward pass"): sort
+ * the routed tokens by expert, run every expert's MLP on its tokens, combine
+ * the expert results with the router weights; in the backward, form the
+ * routed output gradients, recompute the activations, compute input and
+ * expert-weight gradients (weight gradients summed over all of an expert's
+ * token tiles) and reduce the routed dX back onto the tokens.  The same
+ * README's overview section asks for buffers sized from the total routed
+ * capacity (no per-expert capacity, no dropped tokens) so that the calls stay
+ * capturable into a graph despite data-dependent routing; every call below
+ * therefore takes its sizes from the host-side dims only and never reads
+ * device data back to the host.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked "device" are HIP device pointers on the current device,
+ *     row-major (last index contiguous), 16-byte aligned.  bf16 arrays are
+ *     passed as `void*` (raw bfloat16 bits).
+ *   - The caller owns every buffer, including the workspace; the library never
+ *     allocates, frees or keeps a pointer after the call returns.
+ *   - `stream` is a hipStream_t passed as `void*` (NULL = the default stream).
+ *     Work is enqueued asynchronously; nothing synchronises with the host.
+ *   - Host-side validation only.  On any error nothing is launched and the
+ *     status tells why.  Device *contents* are not validated (expert ids out
+ *     of range, offsets that do not match the ids): that is undefined
+ *     behaviour, because checking it would need a device-to-host read.
+ *   - Outputs are overwritten (see `accumulate_dw` for the one exception).
+ *     Results are bitwise deterministic run to run (no floating-point atomics).
+ *   - Symbols: the library exports only `moe_*`.
+ *
+ * Weight layout (linear-layer convention [out_features, in_features]):
+ *   w_gate, w_up  [E, I, D]   gate/up projection of expert e: D -> I
+ *   w_down        [E, D, I]   down projection of expert e:    I -> D
+ * so that  h = silu(x W_gate[e]^T) * (x W_up[e]^T),  o = h W_down[e]^T.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* Router score functions. */
+#define MOE_SCORE_SOFTMAX_TOPK 0 /* softmax over E, keep top K, renormalise over the K */
+#define MOE_SCORE_SIGMOID 1      /* sigmoid of each selected logit, no renormalisation */
+
+/* Status codes. */
+#define MOE_OK 0
+#define MOE_ERR_BAD_ARG 1        /* null / misaligned pointer, bad dims, K > E, T*K >= 2^31 */
+#define MOE_ERR_UNSUPPORTED 2    /* valid but unsupported: D or I not a multiple of 64,
+                                    E > 1024, K > 64, or a grid too large for 32 bits */
+#define MOE_ERR_WORKSPACE 3      /* workspace smaller than moe_workspace_bytes() */
+#define MOE_ERR_HIP 4            /* a HIP launch or runtime call failed */
+
+/* Workspace phases for moe_workspace_bytes(). */
+#define MOE_PHASE_ROUTE 0
+#define MOE_PHASE_FWD 1
+#define MOE_PHASE_BWD 2
+
+typedef int32_t moe_status;
+
+/* Layer dimensions.  T tokens, model width D, expert hidden width I, E
+ * experts, K experts per token, score = MOE_SCORE_*.  R = T*K routed rows. */
+typedef struct moe_dims {
+    int32_t T, D, I, E, K;
+    int32_t score;
+} moe_dims;
+
+/* Bytes of device workspace that the given phase needs (pure host, touches
+ * no device).  Returns 0 for invalid dims or an unknown phase. */
+size_t moe_workspace_bytes(const moe_dims *dims, int32_t phase);
+
+/* Routing and sort by expert ("LigerMoE design / Forward pass": the routed
+ * tokens are sorted by expert before the expert loop).
+ *
+ *   logits          device fp32 [T, E]   router logits (finite)
+ *   topk_idx        device i32  [T, K]   out: selected experts; slot k holds the
+ *                                        rank-k expert (larger logit first, equal
+ *                                        logits toward the lower expert id)
+ *   topk_w          device fp32 [T, K]   out: router weights (per dims->score)
+ *   counts          device i32  [E]      out: routed rows per expert
+ *   offsets         device i32  [E+1]    out: exclusive prefix of counts, offsets[E] = T*K
+ *   sorted_to_flat  device i32  [T*K]    out: sorted row p -> flat slot f = t*K + k;
+ *                                        inside an expert rows are in ascending f
+ *   flat_to_sorted  device i32  [T*K]    out: inverse permutation
+ *   ws, ws_bytes    device workspace of at least moe_workspace_bytes(dims, MOE_PHASE_ROUTE)
+ * All index outputs are unique and must match a plain CPU reference bit for bit. */
+moe_status moe_route_sort(const moe_dims *dims, const float *logits, int32_t *topk_idx,
+                          float *topk_w, int32_t *counts, int32_t *offsets,
+                          int32_t *sorted_to_flat, int32_t *flat_to_sorted, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* Forward ("LigerMoE design / Forward pass"): gather the routed rows into
+ * expert order, grouped gate/up GEMM with the SwiGLU fused into its epilogue,
+ * grouped down GEMM, then the router-weighted combine
+ *     y[t] = sum_{k<K} topk_w[t,k] * o[t,k]      (fp32 accumulation, k ascending)
+ *
+ *   x               device bf16 [T, D]
+ *   w_gate, w_up    device bf16 [E, I, D]
+ *   w_down          device bf16 [E, D, I]
+ *   topk_w, offsets, sorted_to_flat, flat_to_sorted   as produced by moe_route_sort
+ *   y               device bf16 [T, D]   out
+ *   ws, ws_bytes    device workspace of at least moe_workspace_bytes(dims, MOE_PHASE_FWD)
+ * Intermediates (gathered rows, SwiGLU activations, unweighted expert outputs)
+ * are stored as bf16 in the workspace; all GEMMs accumulate in fp32. */
+moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, const void *w_up,
+                   const void *w_down, const float *topk_w, const int32_t *offsets,
+                   const int32_t *sorted_to_flat, const int32_t *flat_to_sorted, void *y,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* Backward ("LigerMoE design / Backward pass"), routing held fixed, for the
+ * loss L with dL/dy = dy:
+ *   dx        device bf16 [T, D]   out: dL/dx through the experts
+ *                                  (sum over the K routed copies, fp32, k ascending)
+ *   dw_gate   device fp32 [E, I, D] out: dL/dW_gate
+ *   dw_up     device fp32 [E, I, D] out: dL/dW_up
+ *   dw_down   device fp32 [E, D, I] out: dL/dW_down
+ *   d_topk_w  device fp32 [T, K]   out: dL/dtopk_w[t,k] = <dy[t], o[t,k]>
+ *   accumulate_dw  0: overwrite dw_*;  1: add into dw_* (fp32)
+ * The gate/up activations are recomputed (not read from the forward).  Each
+ * weight-gradient tile is produced by one workgroup that walks all of its
+ * expert's rows (no atomics); experts with no rows get exact zeros (or are
+ * left unchanged when accumulating).
+ *   ws, ws_bytes   device workspace of at least moe_workspace_bytes(dims, MOE_PHASE_BWD) */
+moe_status moe_bwd(const moe_dims *dims, const void *x, const void *w_gate, const void *w_up,
+                   const void *w_down, const float *topk_w, const int32_t *offsets,
+                   const int32_t *sorted_to_flat, const int32_t *flat_to_sorted,
+                   const void *dy, void *dx, float *dw_gate, float *dw_up, float *dw_down,
+                   float *d_topk_w, int32_t accumulate_dw, void *ws, size_t ws_bytes,
+                   void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *moe_status_string(moe_status status);
+
+/* MOE_ABI_VERSION of the loaded library. */
+int32_t moe_abi_version(void);
+
+/* Text of the HIP error behind the calling thread's last MOE_ERR_HIP (which
+ * launch, HIP's message and code); "" if the last call succeeded. */
+const char *moe_last_error(void);
+
+/* ---- Per-kernel timing (a measurement aid, off by default).
+ * moe_prof_enable(1) clears what was recorded and starts bracketing every
+ * kernel the library launches with two hipEvents recorded on that kernel's
+ * stream; moe_prof_enable(0) clears and stops.  moe_prof_read() waits for the
+ * recorded events and writes, for kernel ids 0..n-1, the summed elapsed time
+ * in milliseconds and the number of launches since the last enable.  Kernel
+ * ids run 0..moe_prof_num_kernels()-1; moe_prof_kernel_name() names them (NULL
+ * for an unknown id).  Timing state is process-wide; do not enable it while
+ * a stream is being captured into a graph.  Returns MOE_ERR_HIP if an event
+ * query fails, MOE_ERR_BAD_ARG for null arrays with n > 0. */
+int32_t moe_prof_enable(int32_t on);
+int32_t moe_prof_num_kernels(void);
+const char *moe_prof_kernel_name(int32_t kernel_id);
+moe_status moe_prof_read(double *total_ms, int64_t *launches, int32_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,386 @@
+// extern "C" entry points of libmoe: host-side validation, workspace
+// carving and the launch sequences of route+sort, forward and backward.
+// Nothing here reads device memory or synchronises with the host.
+#include <stdio.h>
+
+#include <algorithm>
+
+#include "kernels.hpp"
+
+#define MOE_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace moe {
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 64;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// A pointer argument is acceptable if its array is empty, or if it is non-null
+// and aligned to `a` bytes.
+bool ptr_ok(const void* p, size_t count, size_t a) { return count == 0 || (p && aligned(p, a)); }
+
+// MOE_OK, or why the dims are rejected.
+moe_status check_dims(const moe_dims* d) {
+  if (!d) return MOE_ERR_BAD_ARG;
+  if (d->T < 0 || d->D <= 0 || d->I <= 0 || d->E <= 0 || d->K <= 0 || d->K > d->E)
+    return MOE_ERR_BAD_ARG;
+  if (d->score != MOE_SCORE_SOFTMAX_TOPK && d->score != MOE_SCORE_SIGMOID) return MOE_ERR_BAD_ARG;
+  if ((int64_t)d->T * d->K >= (int64_t(1) << 31)) return MOE_ERR_BAD_ARG;
+  if (d->D % 64 || d->I % 64 || d->E > kMaxE || d->K > kMaxK) return MOE_ERR_UNSUPPORTED;
+  // tile counts of the grouped GEMMs must fit in 32-bit grids
+  const int64_t R = (int64_t)d->T * d->K;
+  const int64_t mt = (R + (int64_t)d->E * (kGemmBM - 1)) / kGemmBM;
+  const int64_t nt = std::max<int64_t>(d->I / 64, (d->D + kGemmBN - 1) / kGemmBN);
+  if (mt * nt >= (int64_t(1) << 31) - 8) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+struct Carve {
+  char* base;
+  size_t used = 0;
+  template <typename T>
+  T* take(size_t count) {
+    T* p = reinterpret_cast<T*>(base ? base + used : nullptr);
+    used += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+struct FwdWs {
+  int32_t* tstart;
+  bf16_t *xs, *h, *o;
+};
+struct BwdWs {
+  int32_t* tstart;
+  bf16_t *xs, *dou;
+  f16_t *dgu, *hw;  // fp16 operands of the gradient GEMMs
+  float *gu, *dxs, *part;
+};
+
+int partials_per_row(const moe_dims& d) { return 2 * ((d.I + kGemmBN - 1) / kGemmBN); }
+
+size_t route_ws(const moe_dims& d, int32_t** hist, void* base) {
+  Carve c{(char*)base};
+  const int R = d.T * d.K;
+  const int chunk = route_chunk(R);
+  const size_t nblk = (size_t)((R + chunk - 1) / chunk);
+  *hist = c.take<int32_t>(std::max<size_t>(1, nblk * d.E));
+  return c.used;
+}
+
+size_t fwd_ws(const moe_dims& d, FwdWs* w, void* base) {
+  Carve c{(char*)base};
+  const size_t R = (size_t)d.T * d.K;
+  w->tstart = c.take<int32_t>(d.E + 1);
+  w->xs = c.take<bf16_t>(R * d.D);
+  w->h = c.take<bf16_t>(R * d.I);
+  w->o = c.take<bf16_t>(R * d.D);
+  return c.used;
+}
+
+size_t bwd_ws(const moe_dims& d, BwdWs* w, void* base) {
+  Carve c{(char*)base};
+  const size_t R = (size_t)d.T * d.K;
+  w->tstart = c.take<int32_t>(d.E + 1);
+  w->xs = c.take<bf16_t>(R * d.D);
+  w->dou = c.take<bf16_t>(R * d.D);
+  w->gu = c.take<float>(R * 2 * d.I);
+  w->dgu = c.take<f16_t>(R * 2 * d.I);
+  w->hw = c.take<f16_t>(R * d.I);
+  w->dxs = c.take<float>(R * d.D);
+  w->part = c.take<float>(R * partials_per_row(d));
+  return c.used;
+}
+
+int rowgrouped_grid(const moe_dims& d, int n_tiles) {
+  const int64_t R = (int64_t)d.T * d.K;
+  const int64_t mt = (R + (int64_t)d.E * (kGemmBM - 1)) / kGemmBM;
+  const int64_t tiles = mt * n_tiles;
+  return (int)((tiles + kNumXcd - 1) / kNumXcd * kNumXcd);
+}
+
+int dw_grid(int nmat, int E, int M, int N) {
+  const int64_t tiles = (int64_t)nmat * E * ((M + kGemmBM - 1) / kGemmBM) *
+                        ((N + kGemmBN - 1) / kGemmBN);
+  return (int)((tiles + kNumXcd - 1) / kNumXcd * kNumXcd);
+}
+
+thread_local char last_error[256] = "";
+
+moe_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return MOE_OK;
+  snprintf(last_error, sizeof(last_error), "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+  return MOE_ERR_HIP;
+}
+
+// Entry points start from a clean error state: an error left by an earlier,
+// unrelated HIP call on this thread must not be reported as ours.
+void clear_stale_error() {
+  (void)hipGetLastError();
+  last_error[0] = 0;
+}
+
+#define MOE_TRY(expr)                                            \
+  do {                                                           \
+    hipError_t err_ = (expr);                                    \
+    if (err_ != hipSuccess) return hip_status(err_, #expr);      \
+  } while (0)
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+MOE_EXPORT size_t moe_workspace_bytes(const moe_dims* dims, int32_t phase) {
+  if (check_dims(dims) != MOE_OK) return 0;
+  switch (phase) {
+    case MOE_PHASE_ROUTE: {
+      int32_t* h;
+      return route_ws(*dims, &h, nullptr);
+    }
+    case MOE_PHASE_FWD: {
+      FwdWs w;
+      return fwd_ws(*dims, &w, nullptr);
+    }
+    case MOE_PHASE_BWD: {
+      BwdWs w;
+      return bwd_ws(*dims, &w, nullptr);
+    }
+    default:
+      return 0;
+  }
+}
+
+MOE_EXPORT moe_status moe_route_sort(const moe_dims* dims, const float* logits,
+                                     int32_t* topk_idx, float* topk_w, int32_t* counts,
+                                     int32_t* offsets, int32_t* sorted_to_flat,
+                                     int32_t* flat_to_sorted, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  moe_status s = check_dims(dims);
+  if (s != MOE_OK) return s;
+  const size_t R = (size_t)dims->T * dims->K;
+  if (!ptr_ok(logits, (size_t)dims->T * dims->E, 4) || !ptr_ok(topk_idx, R, 4) ||
+      !ptr_ok(topk_w, R, 4) || !ptr_ok(sorted_to_flat, R, 4) || !ptr_ok(flat_to_sorted, R, 4) ||
+      !ptr_ok(counts, dims->E, 4) || !ptr_ok(offsets, dims->E + 1, 4) || !ptr_ok(ws, 1, 16))
+    return MOE_ERR_BAD_ARG;
+  int32_t* hist;
+  if (ws_bytes < route_ws(*dims, &hist, ws)) return MOE_ERR_WORKSPACE;
+  clear_stale_error();
+  return hip_status(launch_route_sort(*dims, logits, topk_idx, topk_w, counts, offsets,
+                                      sorted_to_flat, flat_to_sorted, hist, (hipStream_t)stream),
+                    "route_sort");
+}
+
+MOE_EXPORT moe_status moe_fwd(const moe_dims* dims, const void* x, const void* w_gate,
+                              const void* w_up, const void* w_down, const float* topk_w,
+                              const int32_t* offsets, const int32_t* sorted_to_flat,
+                              const int32_t* flat_to_sorted, void* y, void* ws, size_t ws_bytes,
+                              void* stream) {
+  moe_status s = check_dims(dims);
+  if (s != MOE_OK) return s;
+  const size_t R = (size_t)dims->T * dims->K, TD = (size_t)dims->T * dims->D;
+  const size_t W = (size_t)dims->E * dims->I * dims->D;
+  if (!ptr_ok(x, TD, 16) || !ptr_ok(y, TD, 16) || !ptr_ok(w_gate, W, 16) ||
+      !ptr_ok(w_up, W, 16) || !ptr_ok(w_down, W, 16) || !ptr_ok(ws, 1, 16) ||
+      !ptr_ok(topk_w, R, 4) || !ptr_ok(offsets, dims->E + 1, 4) ||
+      !ptr_ok(sorted_to_flat, R, 4) || !ptr_ok(flat_to_sorted, R, 4))
+    return MOE_ERR_BAD_ARG;
+  FwdWs w;
+  if (ws_bytes < fwd_ws(*dims, &w, ws)) return MOE_ERR_WORKSPACE;
+  const moe_dims& d = *dims;
+  if (d.T == 0) return MOE_OK;
+  hipStream_t st = (hipStream_t)stream;
+  clear_stale_error();
+
+  MOE_TRY(launch_gather(x, nullptr, w.xs, nullptr, sorted_to_flat, (int)R, d.K, d.D, st));
+  MOE_TRY(launch_tilemap(offsets, d.E, kGemmBM, w.tstart, st));
+
+  GemmArgs g{};
+  g.offsets = offsets;
+  g.tstart = w.tstart;
+  g.E = d.E;
+  // gate/up + SwiGLU: H[R, I] = silu(Xs Wg^T) * (Xs Wu^T)
+  g.A = w.xs;
+  g.lda = d.D;
+  g.B0 = (const bf16_t*)w_gate;
+  g.B1 = (const bf16_t*)w_up;
+  g.ldb = d.D;
+  g.N = d.I;
+  g.K = d.D;
+  g.n_tiles = d.I / 64;
+  g.C0 = w.h;
+  g.ldc = d.I;
+  MOE_TRY(launch_gemm(kGateUpH, g, rowgrouped_grid(d, g.n_tiles), st));
+  // down: O[R, D] = H Wd^T
+  g.A = w.h;
+  g.lda = d.I;
+  g.B0 = (const bf16_t*)w_down;
+  g.B1 = nullptr;
+  g.ldb = d.I;
+  g.N = d.D;
+  g.K = d.I;
+  g.n_tiles = (d.D + kGemmBN - 1) / kGemmBN;
+  g.C0 = w.o;
+  g.ldc = d.D;
+  MOE_TRY(launch_gemm(kDown, g, rowgrouped_grid(d, g.n_tiles), st));
+
+  MOE_TRY(launch_combine(w.o, topk_w, flat_to_sorted, y, d.T, d.K, d.D, st));
+  return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w_gate,
+                              const void* w_up, const void* w_down, const float* topk_w,
+                              const int32_t* offsets, const int32_t* sorted_to_flat,
+                              const int32_t* flat_to_sorted, const void* dy, void* dx,
+                              float* dw_gate, float* dw_up, float* dw_down, float* d_topk_w,
+                              int32_t accumulate_dw, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_dims(dims);
+  if (s != MOE_OK) return s;
+  const size_t R = (size_t)dims->T * dims->K, TD = (size_t)dims->T * dims->D;
+  const size_t W = (size_t)dims->E * dims->I * dims->D;
+  if (!ptr_ok(x, TD, 16) || !ptr_ok(dy, TD, 16) || !ptr_ok(dx, TD, 16) ||
+      !ptr_ok(w_gate, W, 16) || !ptr_ok(w_up, W, 16) || !ptr_ok(w_down, W, 16) ||
+      !ptr_ok(dw_gate, W, 16) || !ptr_ok(dw_up, W, 16) || !ptr_ok(dw_down, W, 16) ||
+      !ptr_ok(ws, 1, 16) || !ptr_ok(topk_w, R, 4) || !ptr_ok(offsets, dims->E + 1, 4) ||
+      !ptr_ok(sorted_to_flat, R, 4) || !ptr_ok(flat_to_sorted, R, 4) || !ptr_ok(d_topk_w, R, 4))
+    return MOE_ERR_BAD_ARG;
+  if (accumulate_dw != 0 && accumulate_dw != 1) return MOE_ERR_BAD_ARG;
+  BwdWs w;
+  if (ws_bytes < bwd_ws(*dims, &w, ws)) return MOE_ERR_WORKSPACE;
+  const moe_dims& d = *dims;
+  hipStream_t st = (hipStream_t)stream;
+  clear_stale_error();
+
+  if (R > 0) {
+    // routed output gradients and the re-gathered inputs, in expert order
+    MOE_TRY(launch_gather(x, dy, w.xs, w.dou, sorted_to_flat, (int)R, d.K, d.D, st));
+    MOE_TRY(launch_tilemap(offsets, d.E, kGemmBM, w.tstart, st));
+  }
+  GemmArgs g{};
+  g.offsets = offsets;
+  g.tstart = w.tstart;
+  g.E = d.E;
+  if (R > 0) {
+    // recompute G, U (fp32) into GU[R, 2I]
+    g.A = w.xs;
+    g.lda = d.D;
+    g.B0 = (const bf16_t*)w_gate;
+    g.B1 = (const bf16_t*)w_up;
+    g.ldb = d.D;
+    g.N = d.I;
+    g.K = d.D;
+    g.n_tiles = d.I / 64;
+    g.Cf = w.gu;
+    g.Cf2 = w.gu + d.I;
+    g.ldc = 2 * d.I;
+    MOE_TRY(launch_gemm(kGateUpGU, g, rowgrouped_grid(d, g.n_tiles), st));
+    // dA = dOu Wd, SwiGLU backward, Hw, router-weight partials
+    g = GemmArgs{};
+    g.offsets = offsets;
+    g.tstart = w.tstart;
+    g.E = d.E;
+    g.A = w.dou;
+    g.lda = d.D;
+    g.B0 = (const bf16_t*)w_down;
+    g.ldb = d.I;
+    g.N = d.I;
+    g.K = d.D;
+    g.n_tiles = (d.I + kGemmBN - 1) / kGemmBN;
+    g.C0 = w.dgu;
+    g.C1 = w.dgu + d.I;
+    g.C2 = w.hw;
+    g.ldc = 2 * d.I;
+    g.GU = w.gu;
+    g.topk_w = topk_w;
+    g.s2f = sorted_to_flat;
+    g.part = w.part;
+    g.np = partials_per_row(d);
+    MOE_TRY(launch_gemm(kDA, g, rowgrouped_grid(d, g.n_tiles), st));
+    // dXs = dG Wg + dU Wu   (reduction over 2I)
+    g = GemmArgs{};
+    g.offsets = offsets;
+    g.tstart = w.tstart;
+    g.E = d.E;
+    g.A = w.dgu;
+    g.lda = 2 * d.I;
+    g.B0 = (const bf16_t*)w_gate;
+    g.B1 = (const bf16_t*)w_up;
+    g.ldb = d.D;
+    g.N = d.D;
+    g.K = 2 * d.I;
+    g.n_tiles = (d.D + kGemmBN - 1) / kGemmBN;
+    g.Cf = w.dxs;
+    g.ldc = d.D;
+    g.cvt_a = 0;  // dG | dU already fp16
+    g.cvt_b = 1;  // weights bf16 -> fp16
+    MOE_TRY(launch_gemm(kDXs, g, rowgrouped_grid(d, g.n_tiles), st));
+  }
+  // dW_down[e] = dOu_e^T Hw_e   ([D, I], reduction over the expert's rows)
+  g = GemmArgs{};
+  g.offsets = offsets;
+  g.E = d.E;
+  g.A = w.dou;
+  g.lda = d.D;
+  g.B0 = w.hw;
+  g.ldb = d.I;
+  g.M = d.D;
+  g.N = d.I;
+  g.nmat = 1;
+  g.cvt_a = 1;  // dOu bf16 -> fp16
+  g.cvt_b = 0;  // Hw fp16
+  g.Cf = dw_down;
+  g.accumulate = accumulate_dw;
+  MOE_TRY(launch_gemm(kDW, g, dw_grid(1, d.E, d.D, d.I), st));
+  // dW_gate[e] = dG_e^T Xs_e, dW_up[e] = dU_e^T Xs_e   ([I, D])
+  g.A = w.dgu;
+  g.A2 = w.dgu + d.I;
+  g.lda = 2 * d.I;
+  g.B0 = w.xs;
+  g.ldb = d.D;
+  g.M = d.I;
+  g.N = d.D;
+  g.nmat = 2;
+  g.cvt_a = 0;  // dG | dU fp16
+  g.cvt_b = 1;  // Xs bf16 -> fp16
+  g.Cf = dw_gate;
+  g.Cf2 = dw_up;
+  MOE_TRY(launch_gemm(kDW, g, dw_grid(2, d.E, d.I, d.D), st));
+
+  if (R > 0) {
+    MOE_TRY(launch_reduce_rows(w.dxs, flat_to_sorted, dx, d.T, d.K, d.D, st));
+    MOE_TRY(launch_reduce_partials(w.part, flat_to_sorted, d_topk_w, (int)R,
+                                   partials_per_row(d), st));
+  }
+  return MOE_OK;
+}
+
+MOE_EXPORT const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_BAD_ARG: return "bad argument (null/misaligned pointer, invalid dims, K > E or T*K >= 2^31)";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape (D and I must be multiples of 64, E <= 1024, K <= 64)";
+    case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes()";
+    case MOE_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+MOE_EXPORT int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+MOE_EXPORT const char* moe_last_error(void) { return last_error; }
+
+MOE_EXPORT int32_t moe_prof_enable(int32_t on) { return prof::set_enabled(on); }
+
+MOE_EXPORT int32_t moe_prof_num_kernels(void) { return kNumKernels; }
+
+MOE_EXPORT const char* moe_prof_kernel_name(int32_t kernel_id) { return prof::name(kernel_id); }
+
+MOE_EXPORT moe_status moe_prof_read(double* total_ms, int64_t* launches, int32_t n) {
+  if (n < 0 || (n > 0 && (!total_ms || !launches))) return MOE_ERR_BAD_ARG;
+  return prof::read(total_ms, launches, n) == 0 ? MOE_OK : MOE_ERR_HIP;
+}

@@ -1,0 +1,94 @@
+// Internal declarations of the MoE library's kernels and launchers.
+#pragma once
+
+#include "../../include/moe.h"
+#include "common.hpp"
+
+namespace moe {
+
+// ---- per-kernel timing (prof.hip)
+enum KernelId : int {
+  kKRouteTopk, kKRouteHist, kKRouteScan, kKRouteScatter, kKTilemap, kKGather,
+  kKGemmGateUpH, kKGemmGateUpGU, kKGemmDown, kKGemmDA, kKGemmDXs, kKGemmDWDown,
+  kKGemmDWGateUp, kKCombine, kKReduceRows, kKReducePartials, kKGather2, kNumKernels
+};
+namespace prof {
+void begin(int kid, hipStream_t st);  // no-ops unless timing is enabled
+void end(hipStream_t st);
+const char* name(int kid);
+int set_enabled(int on);
+int read(double* total_ms, int64_t* launches, int n);
+}  // namespace prof
+
+// Launch `kernel` bracketed by the optional timing events.
+#define MOE_LAUNCH(kid, kernel, grid, block, lds, stream, ...)              \
+  do {                                                                      \
+    ::moe::prof::begin((kid), (stream));                                    \
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);      \
+    ::moe::prof::end(stream);                                               \
+  } while (0)
+
+// ---- routing / sort (route.hip)
+int route_chunk(int R);
+hipError_t launch_route_sort(const moe_dims& d, const float* logits, int32_t* idx, float* w,
+                             int32_t* counts, int32_t* offsets, int32_t* s2f, int32_t* f2s,
+                             int32_t* hist, hipStream_t st);
+hipError_t launch_tilemap(const int32_t* offsets, int E, int bm, int32_t* tstart,
+                          hipStream_t st);
+
+// ---- permutes (permute.hip)
+hipError_t launch_gather(const void* src0, const void* src1, void* dst0, void* dst1,
+                         const int32_t* s2f, int R, int K, int D, hipStream_t st);
+hipError_t launch_combine(const void* O, const float* w, const int32_t* f2s, void* y, int T,
+                          int K, int D, hipStream_t st);
+hipError_t launch_reduce_rows(const void* dXs, const int32_t* f2s, void* dx, int T, int K, int D,
+                              hipStream_t st);
+hipError_t launch_reduce_partials(const float* part, const int32_t* f2s, float* out, int R,
+                                  int np, hipStream_t st);
+
+// ---- grouped GEMMs (gemm.hip)
+constexpr int kGemmBM = 128;  // rows of a workgroup tile (routed rows or dW rows)
+constexpr int kGemmBN = 128;  // columns of a workgroup tile (gate/up: 64 gate + 64 up)
+constexpr int kGemmBK = 64;   // reduction depth of one LDS stage
+
+enum GemmMode : int {
+  kGateUpH = 0,   // H  = silu(Xs Wg^T) * (Xs Wu^T)                       bf16 [R, I]
+  kGateUpGU = 1,  // G  = Xs Wg^T,  U = Xs Wu^T                          fp32 [R, 2I]
+  kDown = 2,      // O  = H Wd^T                                         bf16 [R, D]
+  kDA = 3,        // dA = dOu Wd; SwiGLU backward (dG, dU, Hw in fp16) and router-weight
+                  // partials in the epilogue
+  kDXs = 4,       // dXs = dG Wg + dU Wu                                  fp32 [R, D]
+  kDW = 5,        // dW[e] = A_e^T B_e over the expert's rows              fp32
+};
+
+struct GemmArgs {
+  const bf16_t* A;   // row-grouped modes: [R, lda] K-major.  kDW: token-major [R, lda]
+  const bf16_t* A2;  // kDW second matrix's A (dW_up), else unused
+  const bf16_t* B0;  // weights (row-grouped) or token-major activations (kDW)
+  const bf16_t* B1;  // up weights (kGateUp*, kDXs)
+  const int32_t* offsets;  // [E+1] expert row offsets
+  const int32_t* tstart;   // [E+1] per-expert m-tile prefix (row-grouped modes)
+  int E;
+  int M, N, K;  // kDW: output M x N per expert.  Row-grouped: N output cols, K reduction
+  int lda, ldb;
+  int n_tiles;  // row-grouped: column tiles per m-tile
+  int nmat;     // kDW: matrices in this launch (1 or 2)
+  int cvt_a, cvt_b;  // kDXs / kDW: operand stored as bf16, convert to fp16 when staging
+  // epilogue operands
+  bf16_t* C0;
+  bf16_t* C1;
+  bf16_t* C2;
+  int ldc;
+  float* Cf;
+  float* Cf2;
+  int accumulate;
+  const float* GU;   // kDA: recomputed G | U, fp32 [R, 2I]
+  const float* topk_w;
+  const int32_t* s2f;
+  float* part;  // kDA: router-weight-gradient partials [R, np]
+  int np;
+};
+
+hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st);
+
+}  // namespace moe

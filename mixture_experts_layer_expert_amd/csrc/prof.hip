@@ -1,0 +1,103 @@
+// Optional per-kernel timing: when enabled, every kernel launch of the
+// library is bracketed by two hipEvents recorded on the launch stream; the
+// host later sums the elapsed times per kernel.  Off by default; when off the
+// launch path does nothing extra.
+#include <mutex>
+#include <vector>
+
+#include "kernels.hpp"
+
+namespace moe {
+namespace prof {
+namespace {
+
+struct Rec {
+  int kid;
+  hipEvent_t start, stop;
+};
+
+std::mutex mu;
+bool enabled = false;
+std::vector<Rec> recs;        // recorded since the last enable
+std::vector<hipEvent_t> pool;  // reusable events
+int open_kid = -1;
+hipEvent_t open_start = nullptr;
+
+const char* const kNames[kNumKernels] = {
+    "route_topk",   "route_hist",    "route_scan",    "route_scatter", "tilemap",
+    "gather",       "gemm_gateup_h", "gemm_gateup_gu", "gemm_down",    "gemm_da",
+    "gemm_dxs",     "gemm_dw_down",  "gemm_dw_gateup", "combine",      "reduce_rows",
+    "reduce_partials", "gather2"};
+
+hipEvent_t take() {
+  if (!pool.empty()) {
+    hipEvent_t e = pool.back();
+    pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void recycle() {
+  for (const Rec& r : recs) {
+    pool.push_back(r.start);
+    pool.push_back(r.stop);
+  }
+  recs.clear();
+}
+
+}  // namespace
+
+void begin(int kid, hipStream_t st) {
+  if (!enabled) return;
+  std::lock_guard<std::mutex> g(mu);
+  hipEvent_t e = take();
+  if (!e) return;
+  hipEventRecord(e, st);
+  open_kid = kid;
+  open_start = e;
+}
+
+void end(hipStream_t st) {
+  if (!enabled) return;
+  std::lock_guard<std::mutex> g(mu);
+  if (open_kid < 0) return;
+  hipEvent_t e = take();
+  if (!e) return;
+  hipEventRecord(e, st);
+  recs.push_back(Rec{open_kid, open_start, e});
+  open_kid = -1;
+}
+
+const char* name(int kid) { return (kid >= 0 && kid < kNumKernels) ? kNames[kid] : nullptr; }
+
+int set_enabled(int on) {
+  std::lock_guard<std::mutex> g(mu);
+  recycle();
+  open_kid = -1;
+  enabled = on != 0;
+  return 0;
+}
+
+int read(double* total_ms, int64_t* launches, int n) {
+  std::lock_guard<std::mutex> g(mu);
+  for (int i = 0; i < n; ++i) {
+    total_ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  for (const Rec& r : recs) {
+    if (hipEventSynchronize(r.stop) != hipSuccess) return -1;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return -1;
+    if (r.kid < n) {
+      total_ms[r.kid] += ms;
+      launches[r.kid] += 1;
+    }
+  }
+  return 0;
+}
+
+}  // namespace prof
+}  // namespace moe

@@ -1,0 +1,247 @@
+// Routing and sort-by-expert kernels (gfx950).
+//
+// Method: LigerCute README (liger-cute-kernels 0.8.3), "LigerMoE design /
+// Forward pass": the routed tokens are sorted by expert before the expert
+// loop; buffers are sized from the total routed capacity (overview section),
+// so no per-expert capacity exists and no token is dropped.
+//
+// Routing rule (the page leaves it open; plainest reading): experts ranked by
+// fp32 logit, larger first, equal logits toward the lower expert id; weights
+// are the softmax over all experts restricted to the K selected and
+// renormalised (= exp(l_k - l_0) / sum_j exp(l_j - l_0)), or the sigmoid of
+// the selected logit.  Sorted order inside an expert = ascending flat slot
+// f = t*K + k (a stable counting sort), so the permutation is unique.
+#include "kernels.hpp"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Top-K: one wave per token.  Lane l holds experts l, l+64, ... (coalesced
+// loads).  K rounds of a wave-wide arg-max under the (value desc, id asc)
+// order; the winner's owner lane marks it taken.
+template <int NPL>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                   int K, int score, int32_t* __restrict__ idx,
+                                                   float* __restrict__ w) {
+  const int token = (blockIdx.x * 256 + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (token >= T) return;  // uniform per wave
+  const float* l = logits + (size_t)token * E;
+  float v[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? l[e] : 0.0f;
+  }
+  uint32_t taken = 0;
+  int my_e = 0;
+  float my_v = 0.0f, top_v = 0.0f;
+  for (int k = 0; k < K; ++k) {
+    float bv = 0.0f;
+    int be = -1;  // -1: no candidate
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E && !((taken >> j) & 1u)) {
+        if (be < 0 || v[j] > bv || (v[j] == bv && e < be)) {
+          bv = v[j];
+          be = e;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (oe >= 0 && (be < 0 || ov > bv || (ov == bv && oe < be))) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == k) {
+      my_e = be;
+      my_v = bv;
+    }
+    if (k == 0) top_v = bv;
+  }
+  float wk;
+  if (score == MOE_SCORE_SOFTMAX_TOPK) {
+    const float ex = lane < K ? expf(my_v - top_v) : 0.0f;
+    float s = ex;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    wk = ex / s;
+  } else {
+    wk = 1.0f / (1.0f + expf(-my_v));
+  }
+  if (lane < K) {
+    idx[(size_t)token * K + lane] = my_e;
+    w[(size_t)token * K + lane] = wk;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-block expert histogram of flat slots [b*chunk, (b+1)*chunk).
+// hist layout [E][nblk] so that one exclusive scan in (e, b) order gives
+// every block's first output row per expert.
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ idx, int R, int E,
+                                                   int chunk, int nblk, int32_t* __restrict__ hist) {
+  extern __shared__ int cnt[];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  const int f0 = blockIdx.x * chunk;
+  const int f1 = min(R, f0 + chunk);
+  for (int f = f0 + threadIdx.x; f < f1; f += blockDim.x) atomicAdd(&cnt[idx[f]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)e * nblk + blockIdx.x] = cnt[e];
+}
+
+// Block-wide exclusive scan of one int per thread (1024 threads), returns the
+// exclusive prefix; *total receives the sum.  Deterministic (integers).
+__device__ int block_exclusive_scan_1024(int v, int* total) {
+  __shared__ int wsum[16];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int i = 0; i < 16; ++i) {
+    if (i < wv) before += wsum[i];
+    all += wsum[i];
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+// Single block of 1024 threads: in-place exclusive scan of hist ([E][nblk],
+// E*nblk entries) -> per-(expert, block) base rows; offsets[e] = base[e][0],
+// offsets[E] = R, counts[e] = offsets[e+1] - offsets[e].
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ hist, int E, int nblk,
+                                                    int R, int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets) {
+  const long n = (long)E * nblk;
+  const long per = (n + 1023) / 1024;
+  const long b0 = min(n, per * threadIdx.x), b1 = min(n, b0 + per);
+  int s = 0;
+  for (long i = b0; i < b1; ++i) s += hist[i];
+  int total;
+  int run = block_exclusive_scan_1024(s, &total);
+  for (long i = b0; i < b1; ++i) {
+    const int c = hist[i];
+    hist[i] = run;
+    if (nblk > 0 && i % nblk == 0) offsets[i / nblk] = run;
+    run += c;
+  }
+  if (nblk == 0)
+    for (int e = threadIdx.x; e < E; e += 1024) offsets[e] = 0;
+  if (threadIdx.x == 0) offsets[E] = R;
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 1024) counts[e] = offsets[e + 1] - offsets[e];
+}
+
+// Stable scatter, one wave per block (block b owns flat slots of chunk b and
+// walks them in order, 64 at a time).  Lanes holding the same expert are
+// found with one ballot per expert-id bit; a lane's rank among them is the
+// count of lower lanes in that group.  Running positions live in LDS.
+__global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ idx, int R, int E,
+                                                     int chunk, int nblk,
+                                                     const int32_t* __restrict__ base,
+                                                     int32_t* __restrict__ s2f,
+                                                     int32_t* __restrict__ f2s) {
+  extern __shared__ int run[];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) run[e] = base[(size_t)e * nblk + b];
+  __syncthreads();
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const int fbeg = b * chunk, fend = min(R, fbeg + chunk);
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int f0 = fbeg; f0 < fend; f0 += 64) {
+    const int f = f0 + lane;
+    const bool valid = f < fend;
+    const int e = valid ? idx[f] : 0;
+    uint64_t m = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = (e >> bit) & 1;
+      const uint64_t bb = __ballot(on);
+      m &= on ? bb : ~bb;
+    }
+    const int rank = __popcll(m & lt);
+    int pos = 0;
+    if (valid) pos = run[e] + rank;
+    __syncthreads();  // every lane has read run[] before the group leaders advance it
+    if (valid && rank == 0) run[e] = pos + __popcll(m);
+    __syncthreads();
+    if (valid) {
+      s2f[pos] = f;
+      f2s[f] = pos;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tile map for the row-grouped GEMMs: tstart[e] = sum_{e'<e} ceil(count/BM).
+__global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t* __restrict__ offsets, int E,
+                                                       int bm, int32_t* __restrict__ tstart) {
+  int carry = 0;
+  for (int e0 = 0; e0 < E; e0 += 1024) {
+    const int e = e0 + threadIdx.x;
+    const int c = e < E ? (offsets[e + 1] - offsets[e] + bm - 1) / bm : 0;
+    int total;
+    const int ex = block_exclusive_scan_1024(c, &total);
+    if (e < E) tstart[e] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) tstart[E] = carry;
+}
+
+// ---------------------------------------------------------------------------
+int route_chunk(int R) {
+  int per = (R + 255) / 256;
+  per = (per + 63) / 64 * 64;
+  return per < 1024 ? 1024 : per;
+}
+
+hipError_t launch_route_sort(const moe_dims& d, const float* logits, int32_t* idx, float* w,
+                             int32_t* counts, int32_t* offsets, int32_t* s2f, int32_t* f2s,
+                             int32_t* hist, hipStream_t st) {
+  const int R = d.T * d.K;
+  if (d.T > 0) {
+    const int blocks = (d.T + 3) / 4;
+    const int npl = (d.E + 63) / 64;
+#define MOE_TOPK(N)                                                                      \
+  MOE_LAUNCH(kKRouteTopk, topk_kernel<N>, dim3(blocks), dim3(256), 0, st, logits, d.T, d.E, \
+             d.K, d.score, idx, w)
+    if (npl <= 1) MOE_TOPK(1);
+    else if (npl <= 2) MOE_TOPK(2);
+    else if (npl <= 4) MOE_TOPK(4);
+    else if (npl <= 8) MOE_TOPK(8);
+    else MOE_TOPK(16);
+#undef MOE_TOPK
+  }
+  const int chunk = route_chunk(R);
+  const int nblk = (R + chunk - 1) / chunk;
+  if (nblk > 0)
+    MOE_LAUNCH(kKRouteHist, hist_kernel, dim3(nblk), dim3(256), d.E * sizeof(int), st, idx, R,
+               d.E, chunk, nblk, hist);
+  MOE_LAUNCH(kKRouteScan, scan_kernel, dim3(1), dim3(1024), 0, st, hist, d.E, nblk, R, counts,
+             offsets);
+  if (nblk > 0)
+    MOE_LAUNCH(kKRouteScatter, scatter_kernel, dim3(nblk), dim3(64), d.E * sizeof(int), st, idx,
+               R, d.E, chunk, nblk, hist, s2f, f2s);
+  return hipGetLastError();
+}
+
+hipError_t launch_tilemap(const int32_t* offsets, int E, int bm, int32_t* tstart,
+                          hipStream_t st) {
+  MOE_LAUNCH(kKTilemap, tilemap_kernel, dim3(1), dim3(1024), 0, st, offsets, E, bm, tstart);
+  return hipGetLastError();
+}
+
+}  // namespace moe

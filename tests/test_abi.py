@@ -1,0 +1,118 @@
+"""CPU-only checks of the C-ABI library: it loads without a GPU, exports
+exactly the functions that include/moe.h declares, links no torch, and its
+host-side validation rejects bad arguments before anything is launched."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import mixture_experts_layer_expert_amd as moe
+from mixture_experts_layer_expert_amd import binding
+
+LIB = binding.LIB_PATH
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} not built (run python -m mixture_experts_layer_expert_amd.build)")
+    return moe.load_library()
+
+
+def test_exports_match_header(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert exported == binding.header_functions()
+    for name in exported:
+        assert hasattr(lib, name)
+
+
+def test_no_torch_dependency(lib):
+    out = subprocess.run(["readelf", "-d", LIB], capture_output=True, text=True, check=True).stdout
+    needed = [l for l in out.splitlines() if "NEEDED" in l]
+    assert not any("torch" in l or "c10" in l for l in needed), needed
+
+
+def test_version_and_status_strings(lib):
+    assert lib.moe_abi_version() == 1
+    for code in range(6):
+        assert moe.status_string(code)
+
+
+def test_workspace_bytes_host_only(lib):
+    q = moe.dims(8192, 2048, 768, 128, 8)
+    sizes = [moe.moe_workspace_bytes(q, ph) for ph in range(3)]
+    assert all(s > 0 for s in sizes)
+    # backward holds Xs, dOu, GU, dGU, Hw, dXs in bf16 + fp32 partials at least
+    R = 8192 * 8
+    assert sizes[2] >= R * (2048 * 2 * 3 + 768 * 2 * 5)
+    assert moe.moe_workspace_bytes(moe.dims(8192, 2048, 768, 128, 8), 7) == 0
+    assert moe.moe_workspace_bytes(moe.dims(16, 100, 64, 8, 2), 1) == 0          # D % 64
+    assert moe.moe_workspace_bytes(moe.dims(16, 64, 64, 4, 5), 1) == 0           # K > E
+    small = moe.moe_workspace_bytes(moe.dims(16, 64, 64, 4, 2), 2)
+    big = moe.moe_workspace_bytes(moe.dims(32, 64, 64, 4, 2), 2)
+    assert 0 < small <= big
+
+
+FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced: validation fails first
+
+
+def _fwd(lib, d, ws_bytes=1 << 40, x=FAKE):
+    return lib.moe_fwd(ctypes.byref(d), x, *([FAKE] * 8), FAKE, ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("dims,code", [
+    ((16, 100, 64, 8, 2, 0), 2),     # D not a multiple of 64
+    ((16, 64, 96, 8, 2, 0), 2),      # I not a multiple of 64
+    ((16, 64, 64, 2000, 2, 0), 2),   # E > 1024
+    ((16, 64, 64, 128, 65, 0), 2),   # K > 64
+    ((16, 64, 64, 4, 5, 0), 1),      # K > E
+    ((16, 64, 64, 4, 0, 0), 1),      # K = 0
+    ((-1, 64, 64, 4, 2, 0), 1),      # T < 0
+    ((16, 64, 64, 4, 2, 3), 1),      # unknown score
+    ((1 << 28, 64, 64, 16, 8, 0), 1),  # T*K >= 2^31
+])
+def test_bad_dims_rejected(lib, dims, code):
+    d = moe.dims(*dims)
+    assert _fwd(lib, d) == code
+    assert lib.moe_route_sort(ctypes.byref(d), *([FAKE] * 8), ctypes.c_size_t(1 << 40), None) == code
+
+
+def test_bad_pointers_and_workspace(lib):
+    d = moe.dims(16, 64, 64, 4, 2)
+    assert _fwd(lib, d, x=ctypes.c_void_p(0)) == 1                    # null
+    assert _fwd(lib, d, x=ctypes.c_void_p((1 << 20) + 8)) == 1        # bf16 matrix not 16-B aligned
+    assert _fwd(lib, d, ws_bytes=16) == 3                              # workspace too small
+    assert lib.moe_fwd(None, *([FAKE] * 10), ctypes.c_size_t(1 << 40), None) == 1
+    bwd_args = [FAKE] * 14
+    assert lib.moe_bwd(ctypes.byref(d), *bwd_args, ctypes.c_int32(2), FAKE,
+                       ctypes.c_size_t(1 << 40), None) == 1           # accumulate_dw not 0/1
+    assert lib.moe_bwd(ctypes.byref(d), *bwd_args, ctypes.c_int32(0), FAKE,
+                       ctypes.c_size_t(8), None) == 3
+
+
+def test_prof_names(lib):
+    n = lib.moe_prof_num_kernels()
+    names = [lib.moe_prof_kernel_name(i) for i in range(n)]
+    assert all(names) and len(set(names)) == n
+    assert lib.moe_prof_kernel_name(n) is None
+
+
+def test_product_path_never_touches_oracle():
+    """The HIP package and its binding do not import or name the CPU oracle."""
+    pkg = os.path.dirname(moe.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(root, f)).read()
+                assert "import oracle" not in text and "moe_oracle" not in text, f
+
+
+def test_single_hip_runtime(lib):
+    """libmoe binds to the HIP runtime that torch already loaded (same soname);
+    two runtimes in one process leave the second without a device."""
+    maps = open("/proc/self/maps").read().splitlines()
+    paths = {l.split()[-1] for l in maps if "libamdhip64" in l}
+    assert len(paths) == 1, paths

@@ -1,0 +1,275 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: routing indices, counts, offsets and both permutations bit-exact; every
+floating-point output element within |gpu - ref| <= 1e-2 + 1e-2 |ref| of the
+float64 oracle.  Small cases compare every element; full-size workloads
+compare sampled tokens and sampled weight-gradient entries that the oracle
+evaluates one by one, plus whole-array properties.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_common as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not G.gpu_available():
+        pytest.skip("no GPU")
+    import mixture_experts_layer_expert_amd as moe
+    moe.load_library()
+
+
+def _custom(T, D, I, E, K, score, seed, hot=None, dead=(), scale=1.0):
+    """Synthetic workload with optional routing skew: `hot` expert boosted,
+    `dead` experts never chosen."""
+    wl = synth.Workload(f"custom_{T}_{D}_{I}_{E}_{K}", T=T, D=D, I=I, E=E, K=K, score=score, seed=seed)
+    data = synth.generate(wl)
+    lg = data["logits"].astype(np.float64) * scale
+    if hot is not None:
+        lg[: T // 2, hot] += 5.0
+    for e in dead:
+        lg[:, e] = -30.0
+    data["logits"] = lg.astype(np.float32)
+    return wl, data
+
+
+def _full_compare(wl, data, backward=True):
+    dev = G.DeviceInputs(data)
+    route, y, grads = G.run_gpu(dev, wl.K, wl.score, backward=backward)
+    idx, w, counts = G.check_route_exact(route, data, wl.K, wl.score, wl.E)
+    L, _, _ = G.oracle_layer(data, wl.K, wl.score)
+    G.assert_close(G.bf16_dev_to_f64(y), oracle.forward(L, idx, w), "y")
+    if backward:
+        dx, drw = oracle.backward_tokens(L, idx, w)
+        dwg, dwu, dwd = oracle.backward_dw(L, idx, w)
+        G.assert_close(G.bf16_dev_to_f64(grads["dx"]), dx, "dx")
+        G.assert_close(G.host(grads["d_topk_w"]), drw, "d_topk_w")
+        G.assert_close(G.host(grads["dw_gate"]), dwg, "dw_gate")
+        G.assert_close(G.host(grads["dw_up"]), dwu, "dw_up")
+        G.assert_close(G.host(grads["dw_down"]), dwd, "dw_down")
+        for e in np.flatnonzero(counts == 0):
+            for nm in ("dw_gate", "dw_up", "dw_down"):
+                assert not G.host(grads[nm][e]).any(), f"{nm}[{e}] of an empty expert is not zero"
+    return route, y, grads
+
+
+# ----------------------------------------------------------------------------- small: every element
+
+SMALL = {
+    # the tiny workload itself
+    "tiny": lambda: (synth.TINY, synth.generate(synth.TINY)),
+    # several 128-row tiles per expert with a ragged tail, I not a multiple of 128
+    "ragged_tiles": lambda: _custom(T=600, D=256, I=192, E=8, K=2, score=0, seed=101),
+    # D not a multiple of 128 (masked column tail in the down/dXs tiles), many experts
+    "ragged_cols": lambda: _custom(T=300, D=320, I=64, E=16, K=4, score=0, seed=102),
+    # skewed routing: one hot expert, three experts never chosen
+    "skew_empty": lambda: _custom(T=500, D=128, I=128, E=8, K=2, score=0, seed=103, hot=1,
+                                  dead=(2, 5, 7)),
+    # a single expert, K = 1: the dense SwiGLU MLP
+    "one_expert": lambda: _custom(T=130, D=64, I=64, E=1, K=1, score=0, seed=104),
+    # every expert chosen by every token (K = E)
+    "k_equals_e": lambda: _custom(T=100, D=128, I=64, E=4, K=4, score=0, seed=105),
+    # sigmoid score, top-1 (the Scout reading) at a small size
+    "sigmoid_top1": lambda: _custom(T=257, D=192, I=128, E=4, K=1, score=1, seed=106),
+    # one token
+    "one_token": lambda: _custom(T=1, D=64, I=64, E=8, K=2, score=0, seed=107),
+}
+
+
+@pytest.mark.parametrize("case", list(SMALL))
+def test_layer_parity_small(case):
+    wl, data = SMALL[case]()
+    _full_compare(wl, data)
+
+
+# ----------------------------------------------------------------------------- routing only
+
+ROUTE_CASES = [(T, E, K) for (T, E, K) in [(1000, 128, 8), (513, 65, 3), (300, 1024, 64),
+                                           (64, 1, 1), (200, 7, 7), (4096, 16, 1)]]
+
+
+@pytest.mark.parametrize("T,E,K", ROUTE_CASES)
+@pytest.mark.parametrize("score", [0, 1])
+def test_route_adversarial(T, E, K, score):
+    import mixture_experts_layer_expert_amd as moe
+    rng = np.random.Generator(np.random.PCG64(T * 7 + E))
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[0] = 0.0                                                       # all equal
+    if T > 3:
+        lg[1] = np.float32(0.5)
+        lg[2, ::2] = -0.0                                             # signed zeros tie
+        lg[2, 1::2] = 0.0
+        lg[3: T // 4] = np.round(lg[3: T // 4] * 2) / 2               # many exact ties
+        lg[T // 4: T // 2, E - 1] += 8.0                              # one expert takes a quarter
+    data = {"logits": lg}
+    route = moe.moe_route_sort(G.to_dev(lg), K, score)
+    G.torch_mod().cuda.synchronize()
+    G.check_route_exact(route, data, K, score, E)
+
+
+def test_route_empty_batch():
+    import mixture_experts_layer_expert_amd as moe
+    torch = G.torch_mod()
+    lg = torch.empty((0, 16), dtype=torch.float32, device="cuda")
+    route = moe.moe_route_sort(lg, 2, 0)
+    torch.cuda.synchronize()
+    assert G.host(route["counts"]).tolist() == [0] * 16
+    assert G.host(route["offsets"]).tolist() == [0] * 17
+
+
+# ----------------------------------------------------------------------------- full size: sampled
+
+def _sampled_compare(wl, n_tokens=24, n_entries=40, seed=0):
+    data = synth.generate(wl)
+    dev = G.DeviceInputs(data)
+    route, y, grads = G.run_gpu(dev, wl.K, wl.score, backward=True)
+    idx, w, counts = G.check_route_exact(route, data, wl.K, wl.score, wl.E)
+    L, _, _ = G.oracle_layer(data, wl.K, wl.score)
+    tok = synth.sample_indices(wl.T, n_tokens, seed, must=(0, wl.T - 1))
+    y_ref = oracle.forward(L, idx, w, tokens=tok)
+    G.assert_close(G.bf16_dev_to_f64(y[tok]), y_ref, f"{wl.name} y")
+    dx_ref, drw_ref = oracle.backward_tokens(L, idx, w, tokens=tok)
+    G.assert_close(G.bf16_dev_to_f64(grads["dx"][tok]), dx_ref, f"{wl.name} dx")
+    G.assert_close(G.host(grads["d_topk_w"][tok]), drw_ref, f"{wl.name} d_topk_w")
+    # weight-gradient entries: the hottest expert, the coldest non-empty one, random ones,
+    # and the last row / column of each matrix
+    rng = np.random.Generator(np.random.PCG64(seed + 1))
+    hot = int(np.argmax(counts))
+    nz = np.flatnonzero(counts > 0)
+    cold = int(nz[np.argmin(counts[nz])])
+    for which, name, (R_, C_) in ((0, "dw_gate", (wl.I, wl.D)), (1, "dw_up", (wl.I, wl.D)),
+                                  (2, "dw_down", (wl.D, wl.I))):
+        e = rng.integers(0, wl.E, n_entries)
+        e[:4] = hot
+        e[4:6] = cold
+        r = rng.integers(0, R_, n_entries)
+        c = rng.integers(0, C_, n_entries)
+        r[0], c[0] = R_ - 1, C_ - 1
+        ref = oracle.dw_entries(L, idx, w, np.full(n_entries, which), e, r, c)
+        got = G.host(grads[name][e, r, c])
+        G.assert_close(got, ref, f"{wl.name} {name}")
+        for ee in np.flatnonzero(counts == 0):
+            assert not G.host(grads[name][ee]).any(), f"{name}[{ee}] of an empty expert"
+    # whole-array property at full size: outputs finite everywhere
+    torch = G.torch_mod()
+    for t in (y, grads["dx"], grads["dw_gate"], grads["dw_up"], grads["dw_down"], grads["d_topk_w"]):
+        assert bool(torch.isfinite(t.float()).all())
+
+
+@pytest.mark.slow
+def test_qwen3_30b_a3b_full_size():
+    _sampled_compare(synth.QWEN3_30B_A3B)
+
+
+@pytest.mark.slow
+def test_llama4_scout_full_size():
+    _sampled_compare(synth.LLAMA4_SCOUT, n_tokens=12, n_entries=24)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("T", synth.ZIPF_SWEEP_T)
+def test_qwen_zipf_sweep(T):
+    _sampled_compare(synth.qwen_zipf(T), n_tokens=16, n_entries=24)
+
+
+# ----------------------------------------------------------------------------- properties
+
+def test_bitwise_determinism_and_overwrite():
+    """Two runs give identical bits; NaN-poisoned outputs are fully overwritten;
+    accumulate_dw adds exactly."""
+    import mixture_experts_layer_expert_amd as moe
+    torch = G.torch_mod()
+    wl, data = _custom(T=700, D=192, I=128, E=12, K=3, score=0, seed=201, dead=(4,))
+    dev = G.DeviceInputs(data)
+    r1, y1, g1 = G.run_gpu(dev, wl.K, wl.score)
+    # poisoned outputs
+    out = {k: torch.full_like(v, float("nan")) for k, v in g1.items()}
+    route = {k: torch.full_like(v, -7) if v.dtype == torch.int32 else torch.full_like(v, float("nan"))
+             for k, v in r1.items()}
+    moe.moe_route_sort(dev.logits, wl.K, wl.score, out=route)
+    y2 = torch.full_like(y1, float("nan"))
+    moe.moe_fwd(dev.x, dev.w_gate, dev.w_up, dev.w_down, route, wl.K, wl.score, y=y2)
+    moe.moe_bwd(dev.x, dev.w_gate, dev.w_up, dev.w_down, route, dev.dy, wl.K, wl.score, out=out)
+    torch.cuda.synchronize()
+    for k in r1:
+        assert torch.equal(r1[k], route[k]), k
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    for k in g1:
+        a, b = g1[k], out[k]
+        if a.dtype == torch.bfloat16:
+            a, b = a.view(torch.int16), b.view(torch.int16)
+        assert torch.equal(a, b), k
+    # accumulate: dW += dW gives exactly 2 dW
+    moe.moe_bwd(dev.x, dev.w_gate, dev.w_up, dev.w_down, route, dev.dy, wl.K, wl.score, out=out,
+                accumulate_dw=True)
+    torch.cuda.synchronize()
+    for k in ("dw_gate", "dw_up", "dw_down"):
+        assert torch.equal(out[k], 2 * g1[k]), k
+
+
+def test_stream_and_graph_capture():
+    """Calls run on the caller's stream and can be captured into a graph; replays
+    (with eager work in between) reproduce the eager results bit for bit."""
+    import mixture_experts_layer_expert_amd as moe
+    torch = G.torch_mod()
+    wl, data = _custom(T=384, D=128, I=128, E=8, K=2, score=0, seed=202)
+    dev = G.DeviceInputs(data)
+    r_ref, y_ref, g_ref = G.run_gpu(dev, wl.K, wl.score)
+    s = torch.cuda.Stream()
+    route = {k: torch.empty_like(v) for k, v in r_ref.items()}
+    y = torch.empty_like(y_ref)
+    out = {k: torch.empty_like(v) for k, v in g_ref.items()}
+    ws = {ph: torch.empty(moe.moe_workspace_bytes(moe.dims(wl.T, wl.D, wl.I, wl.E, wl.K, wl.score), ph),
+                          dtype=torch.uint8, device="cuda") for ph in range(3)}
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe.moe_route_sort(dev.logits, wl.K, wl.score, out=route, ws=ws[0])
+        moe.moe_fwd(dev.x, dev.w_gate, dev.w_up, dev.w_down, route, wl.K, wl.score, y=y, ws=ws[1])
+        moe.moe_bwd(dev.x, dev.w_gate, dev.w_up, dev.w_down, route, dev.dy, wl.K, wl.score, out=out,
+                    ws=ws[2])
+    s.synchronize()
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        moe.moe_route_sort(dev.logits, wl.K, wl.score, out=route, ws=ws[0])
+        moe.moe_fwd(dev.x, dev.w_gate, dev.w_up, dev.w_down, route, wl.K, wl.score, y=y, ws=ws[1])
+        moe.moe_bwd(dev.x, dev.w_gate, dev.w_up, dev.w_down, route, dev.dy, wl.K, wl.score, out=out,
+                    ws=ws[2])
+    for rep in range(3):
+        for t in [y, *route.values(), *out.values()]:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), rep
+        for k in r_ref:
+            assert torch.equal(route[k], r_ref[k]), (rep, k)
+        for k in g_ref:
+            a, b = out[k], g_ref[k]
+            if a.dtype == torch.bfloat16:
+                a, b = a.view(torch.int16), b.view(torch.int16)
+            assert torch.equal(a, b), (rep, k)
+
+
+def test_empty_batch_layer():
+    """T = 0: forward is a no-op and the weight gradients are all zero."""
+    import mixture_experts_layer_expert_amd as moe
+    torch = G.torch_mod()
+    E, D, I, K = 4, 64, 64, 2
+    x = torch.empty((0, D), dtype=torch.bfloat16, device="cuda")
+    wg = torch.randn((E, I, D), device="cuda").to(torch.bfloat16)
+    wd = torch.randn((E, D, I), device="cuda").to(torch.bfloat16)
+    route = moe.moe_route_sort(torch.empty((0, E), dtype=torch.float32, device="cuda"), K, 0)
+    y = moe.moe_fwd(x, wg, wg, wd, route, K, 0)
+    out = moe.moe_bwd(x, wg, wg, wd, route, x, K, 0)
+    torch.cuda.synchronize()
+    assert y.shape == (0, D)
+    for k in ("dw_gate", "dw_up", "dw_down"):
+        assert not out[k].any()
