@@ -24,6 +24,9 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // and aligned to `a` bytes.
 bool ptr_ok(const void* p, size_t count, size_t a) { return count == 0 || (p && aligned(p, a)); }
 
+// Column tiles of the fused gate/up GEMM: 128 gate + 128 up rows per tile.
+int64_t gateup_tiles(int64_t I) { return (I + kGemmBN / 2 - 1) / (kGemmBN / 2); }
+
 // MOE_OK, or why the dims are rejected.
 moe_status check_dims(const moe_dims* d) {
   if (!d) return MOE_ERR_BAD_ARG;
@@ -35,8 +38,12 @@ moe_status check_dims(const moe_dims* d) {
   // tile counts of the grouped GEMMs must fit in 32-bit grids
   const int64_t R = (int64_t)d->T * d->K;
   const int64_t mt = (R + (int64_t)d->E * (kGemmBM - 1)) / kGemmBM;
-  const int64_t nt = std::max<int64_t>(d->I / 64, (d->D + kGemmBN - 1) / kGemmBN);
+  const int64_t nt = std::max<int64_t>(gateup_tiles(d->I), (d->D + kGemmBN - 1) / kGemmBN);
   if (mt * nt >= (int64_t(1) << 31) - 8) return MOE_ERR_UNSUPPORTED;
+  // the GEMMs address token-major operands with 32-bit buffer offsets
+  if (R * std::max<int64_t>(d->D, 2 * (int64_t)d->I) * 2 >= (int64_t(1) << 31) ||
+      (int64_t)d->I * d->D * 2 >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -58,10 +65,12 @@ struct FwdWs {
 struct BwdWs {
   int32_t* tstart;
   bf16_t *xs, *dou;
-  f16_t *dgu, *hw;  // fp16 operands of the gradient GEMMs
+  f16_t *dgu, *hw;        // fp16 operands of the gradient GEMMs (rounded values)
+  f16_t *dgu_lo, *hw_lo;  // their low parts (value - rounded value), for the dW GEMMs
   float *gu, *dxs, *part;
 };
 
+// router-weight-gradient partials per routed row: one per (column tile, wave column)
 int partials_per_row(const moe_dims& d) { return 2 * ((d.I + kGemmBN - 1) / kGemmBN); }
 
 size_t route_ws(const moe_dims& d, int32_t** hist, void* base) {
@@ -92,6 +101,8 @@ size_t bwd_ws(const moe_dims& d, BwdWs* w, void* base) {
   w->gu = c.take<float>(R * 2 * d.I);
   w->dgu = c.take<f16_t>(R * 2 * d.I);
   w->hw = c.take<f16_t>(R * d.I);
+  w->dgu_lo = c.take<f16_t>(R * 2 * d.I);
+  w->hw_lo = c.take<f16_t>(R * d.I);
   w->dxs = c.take<float>(R * d.D);
   w->part = c.take<float>(R * partials_per_row(d));
   return c.used;
@@ -212,7 +223,7 @@ MOE_EXPORT moe_status moe_fwd(const moe_dims* dims, const void* x, const void* w
   g.ldb = d.D;
   g.N = d.I;
   g.K = d.D;
-  g.n_tiles = d.I / 64;
+  g.n_tiles = (int)gateup_tiles(d.I);
   g.C0 = w.h;
   g.ldc = d.I;
   MOE_TRY(launch_gemm(kGateUpH, g, rowgrouped_grid(d, g.n_tiles), st));
@@ -274,7 +285,7 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
     g.ldb = d.D;
     g.N = d.I;
     g.K = d.D;
-    g.n_tiles = d.I / 64;
+    g.n_tiles = (int)gateup_tiles(d.I);
     g.Cf = w.gu;
     g.Cf2 = w.gu + d.I;
     g.ldc = 2 * d.I;
@@ -294,6 +305,9 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
     g.C0 = w.dgu;
     g.C1 = w.dgu + d.I;
     g.C2 = w.hw;
+    g.L0 = w.dgu_lo;
+    g.L1 = w.dgu_lo + d.I;
+    g.L2 = w.hw_lo;
     g.ldc = 2 * d.I;
     g.GU = w.gu;
     g.topk_w = topk_w;
@@ -332,7 +346,8 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   g.N = d.I;
   g.nmat = 1;
   g.cvt_a = 1;  // dOu bf16 -> fp16
-  g.cvt_b = 0;  // Hw fp16
+  g.cvt_b = 0;  // Hw fp16, split hi + lo
+  g.B_lo = w.hw_lo;
   g.Cf = dw_down;
   g.accumulate = accumulate_dw;
   MOE_TRY(launch_gemm(kDW, g, dw_grid(1, d.E, d.D, d.I), st));
@@ -345,8 +360,11 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   g.M = d.I;
   g.N = d.D;
   g.nmat = 2;
-  g.cvt_a = 0;  // dG | dU fp16
+  g.cvt_a = 0;  // dG | dU fp16, split hi + lo
   g.cvt_b = 1;  // Xs bf16 -> fp16
+  g.A_lo = w.dgu_lo;
+  g.A2_lo = w.dgu_lo + d.I;
+  g.B_lo = nullptr;
   g.Cf = dw_gate;
   g.Cf2 = dw_up;
   MOE_TRY(launch_gemm(kDW, g, dw_grid(2, d.E, d.I, d.D), st));

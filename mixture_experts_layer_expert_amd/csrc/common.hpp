@@ -39,6 +39,14 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
 }
 
+// fp16 bits of (lo - hi_lo, hi - hi_hi), rounded to nearest, where hi holds the
+// two fp16 roundings of (lo, hi): the low parts of a two-term fp16 split.
+__device__ __forceinline__ uint32_t f16x2_residual(float lo, float hi, uint32_t hi_bits) {
+  const float r0 = lo - (float)__builtin_bit_cast(_Float16, (uint16_t)(hi_bits & 0xFFFFu));
+  const float r1 = hi - (float)__builtin_bit_cast(_Float16, (uint16_t)(hi_bits >> 16));
+  return pack_f16x2(r0, r1);
+}
+
 // Two bf16 (one dword) -> two fp16 (one dword).  Exact for |v| in fp16's
 // normal range [2^-14, 65504]; below it the conversion truncates (absolute
 // error < 2^-24) and above it saturates to 65504.

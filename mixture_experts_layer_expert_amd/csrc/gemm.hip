@@ -1,5 +1,5 @@
-// Ragged grouped bf16 GEMMs on CDNA4 matrix cores (gfx950) for the expert MLP
-// and its backward.
+// Ragged grouped GEMMs on CDNA4 matrix cores (gfx950) for the expert MLP and
+// its backward.
 //
 // Method: LigerCute README (liger-cute-kernels 0.8.3), "LigerMoE design":
 // each expert runs its MLP on its (sorted) tokens on the tensor cores
@@ -9,142 +9,171 @@
 // (TMA, warp-specialised WGMMA/UMMA, TMA reduce stores) is prior art only;
 // here every GEMM is one CDNA4 kernel:
 //
-//   - a 256-thread workgroup owns a 128 x 128 output tile; 4 waves in 2 x 2,
-//     each wave 64 x 64 = 4 x 4 fragments of v_mfma_f32_16x16x32_bf16 with
-//     fp32 accumulators;
-//   - 64-deep K stages staged through LDS, double-buffered, with the next
-//     stage's global loads in flight while the matrix cores work on the
-//     current one (one barrier per stage);
-//   - LDS always holds operands k-contiguous ([row][k], rows padded to 144 B,
-//     so the 16 lanes of a 16-byte fragment read hit 16 distinct 4-bank
-//     groups).  Operands that are k-contiguous in HBM are copied as 16-byte
-//     chunks; operands that are row-contiguous (the token-major activations of
-//     the weight gradients, and the weights read transposed) are loaded as 4
-//     k-rows x 8 elements per thread and transposed in registers before the
-//     8-byte LDS writes;
-//   - the MFMA is issued with the B fragment as its first operand, so each
-//     lane ends with 4 consecutive output columns of one row, written as one
-//     8-byte (bf16) or 16-byte (fp32) store;
+//   - a 256-thread workgroup (4 waves) owns a 128 x 256 output tile; waves in
+//     2 (rows) x 2 (columns), each 64 x 128 = 4 x 8 fragments of
+//     v_mfma_f32_16x16x32_{bf16,f16} with fp32 accumulators;
+//   - operands go HBM -> LDS directly (buffer_load ... lds: no VGPR staging),
+//     three 32-deep K stages in flight, one barrier per stage; a buffer
+//     resource per operand bounds the loads, so rows past a ragged edge read as
+//     zeros in hardware.  72 KB of LDS per workgroup lets two workgroups share
+//     a CU, so one's memory-bound epilogue overlaps the other's MFMA loop;
+//   - LDS keeps each operand in its HBM orientation, XOR-swizzled instead of
+//     padded.  k-contiguous operands ([row][k], 64-byte rows, 16-byte chunk c
+//     of row r stored at c ^ (r/4 % 4)) are read with ds_read_b128;
+//     row-contiguous operands ([k][row], the token-major activations of the
+//     weight gradients and the weights read transposed; chunk c of k-row k
+//     stored at c ^ s(k), s(k) = 2 (k % 4) + 8 ((k/8 + k/16) % 2)) are read
+//     with the gfx950 transposing ds_read_b64_tr_b16, which hands each lane 4
+//     consecutive k of one row.  Both read patterns are free of bank
+//     conflicts (measured: SQ_LDS_BANK_CONFLICT = 0);
+//   - the MFMA takes the B fragment as its first operand, so each lane ends
+//     with 4 consecutive output columns of one row (8-byte bf16 or 16-byte
+//     fp32 stores);
 //   - precision: every product accumulates in fp32.  The forward multiplies
 //     bf16 (H is stored as bf16 for the down GEMM).  The recomputed G/U (used
 //     by the SwiGLU backward and the router-weight gradient) and the per-row
 //     dX partials (summed over the K routed copies) stay fp32.  The gradient
 //     GEMMs (dXs, dW) multiply fp16: dG/dU/Hw are rounded to fp16 (3 more
-//     mantissa bits than bf16, at the same matrix-core rate) and the bf16
-//     operands are converted exactly on their way into LDS.  With bf16
-//     gradient operands the cancellation in the sums over an expert's tokens
-//     leaves errors of several times the 1e-2 + 1e-2 |ref| bar; fp16 keeps
-//     them well inside it;
+//     mantissa bits than bf16, at the same matrix-core rate) and bf16 operand
+//     fragments are converted (exactly, for |v| in fp16's normal range) after
+//     the LDS read.  The dW GEMMs sum over all of an expert's rows, where
+//     rounding errors grow with the row count while the result can cancel to
+//     ~0, so there the rounded operand is split in fp16 hi + lo and
+//     multiplied in two passes into the same accumulators (error about
+//     2^-22 sum |terms|);
 //   - ragged expert segments: the tile list is built on the device from the
-//     expert offsets (no host read-back, graph-capturable); rows past an
-//     expert's segment are zero-filled on load and skipped on store;
+//     expert offsets (no host read-back, graph-capturable);
 //   - weight gradients: one workgroup owns one output tile and walks all of
 //     its expert's rows (no atomics, deterministic); an expert with no rows
 //     writes zeros;
 //   - XCD-aware tile order: workgroup b runs on XCD b % 8, so each XCD takes a
 //     contiguous range of the (expert, column tile, row tile) list and the
-//     tiles sharing one expert's weights share that XCD's L2.
+//     tiles sharing one expert's operands share that XCD's L2.
 #include <type_traits>
 
 #include "kernels.hpp"
 
 namespace moe {
 
-constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK, NTH = 256;
-constexpr int LDSR = BK + 8;       // LDS row stride, bf16 elements
-constexpr int TILE = 128 * LDSR;   // one operand tile (128 rows)
+constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
+constexpr int NW = 4, NTH = NW * kWave;  // 4 waves: 2 (rows) x 2 (columns)
+constexpr int WTN = BN / 2;              // columns per wave (128)
+constexpr int FN = WTN / 16;             // B fragments per wave (8)
+constexpr int NS = 3;                    // K stages resident in LDS
+constexpr int A_BYTES = BM * BK * 2;     // 8 KB: 128 rows x 32 k, or 32 k x 128 rows
+constexpr int B_BYTES = BN * BK * 2;     // 16 KB
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+constexpr int LOADS_PER_STAGE = (A_BYTES + B_BYTES) / 1024 / NW;  // per wave: 6
 
-static_assert(BM == 128 && BN == 128 && BK == 64, "loaders assume 128 x 64 operand tiles");
+static_assert(BM == 128 && BN == 256 && BK == 32, "tile geometry is fixed by the loaders");
+static_assert(LOADS_PER_STAGE == 6, "s_waitcnt immediates below assume 6 loads per stage");
 
-__device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-// K-major operand tile: 128 rows x 64 k from rows whose k-run is contiguous.
-// Chunk c = tid + 256 i covers row c / 8, k-chunk c % 8 (16 B each).
-template <typename RowPtr>
-__device__ __forceinline__ void load_kmajor(u32x4 (&r)[4], RowPtr row_ptr, int rows_valid,
-                                            int k0) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = threadIdx.x + NTH * i;
-    const int row = c >> 3, kc = c & 7;
-    r[i] = row < rows_valid ? *(const u32x4*)(row_ptr(row) + k0 + kc * 8) : zero4();
-  }
-}
-__device__ __forceinline__ void store_kmajor(bf16_t* lds, const u32x4 (&r)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = threadIdx.x + NTH * i;
-    const int row = c >> 3, kc = c & 7;
-    *(u32x4*)(lds + row * LDSR + kc * 8) = r[i];
-  }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  const int n = bytes > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
-// bf16 -> fp16 in place (for operands of the fp16 gradient GEMMs).
-__device__ __forceinline__ void to_f16(u32x4 (&r)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int d = 0; d < 4; ++d) r[i][d] = bf16x2_to_f16x2(r[i][d]);
+// One wave-wide direct-to-LDS load: lane i's 16 bytes at voffset land at
+// lds_wave_base + 16 i (lds_wave_base must be wave-uniform).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_wave_base, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, lds_wave_base), 16, voffset, 0, 0, 0);
 }
 
-// Row-contiguous operand tile: global element (k, mn) at base[k * ld + mn].
-// Thread (kq = tid % 16, mc = tid / 16) loads k-rows 4kq..4kq+3 of the 8
-// columns 8mc..8mc+7; valid iff k < k_valid and the column chunk < mn_valid.
-__device__ __forceinline__ void load_mnmajor(u32x4 (&r)[4], const bf16_t* base, size_t ld,
-                                             int k_valid, int mn_valid) {
-  const int kq = threadIdx.x & 15, mc = threadIdx.x >> 4;
-  const bool col_ok = mc * 8 < mn_valid;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int k = kq * 4 + q;
-    r[q] = (col_ok && k < k_valid) ? *(const u32x4*)(base + (size_t)k * ld + mc * 8) : zero4();
-  }
+// Swizzles (see the file comment).  swz_k: 16 consecutive rows reading the
+// same k-chunk land in 16 distinct 16-byte bank groups.  swz_mn: the four
+// 16-lane groups of a transposing read (k-rows 8g..8g+3) split into two pairs
+// that each cover all 64 banks, for either pairing of the groups.
+__device__ __forceinline__ int swz_k(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int swz_mn(int k) {
+  return ((k & 3) << 1) | ((((k >> 3) ^ (k >> 4)) & 1) << 3);
 }
-// Transpose the 4 (k) x 8 (mn) block in registers and write 8 rows of 4 k.
-__device__ __forceinline__ void store_mnmajor(bf16_t* lds, const u32x4 (&r)[4]) {
-  const int kq = threadIdx.x & 15, mc = threadIdx.x >> 4;
+
+// k-contiguous tile of ROWS rows x 32 k (64-byte rows): this wave's
+// instructions j = wave + 4 i each fill rows 16j..16j+15.  off(row) = byte
+// offset of the row's k = 0 element.
+template <int ROWS, typename RowOff>
+__device__ __forceinline__ void issue_kmajor(char* tile, int wave, int lane, uint32_t k0_bytes,
+                                             RowOff off, __amdgpu_buffer_rsrc_t r) {
+  constexpr int N_INSTR = ROWS / 16 / NW;  // 1 KB instructions (16 rows of 64 B) per wave
+  static_assert(N_INSTR * NW * 16 == ROWS, "the waves' instructions must cover all rows");
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int d = j >> 1;
-    u32x2 v;
-    if (j & 1) {
-      v[0] = (r[0][d] >> 16) | (r[1][d] & 0xFFFF0000u);
-      v[1] = (r[2][d] >> 16) | (r[3][d] & 0xFFFF0000u);
-    } else {
-      v[0] = (r[0][d] & 0xFFFFu) | (r[1][d] << 16);
-      v[1] = (r[2][d] & 0xFFFFu) | (r[3][d] << 16);
-    }
-    *(u32x2*)(lds + (mc * 8 + j) * LDSR + kq * 4) = v;
+  for (int i = 0; i < N_INSTR; ++i) {
+    const int j = wave + NW * i;
+    const int row = 16 * j + (lane >> 2);
+    const int c = (lane & 3) ^ swz_k(row);
+    dma16(r, tile + j * 1024, off(row) + k0_bytes + c * 16);
   }
 }
 
-// LDS row of the B fragment j of wave column wn.  Gate/up tiles hold 64 gate
-// rows then the 64 matching up rows; each wave takes 2 gate + the 2 matching
-// up fragments so that g and u of one output land in the same lane.
+// Row-contiguous tile of 32 k-rows x C columns (C = 128 or 256): instruction j
+// fills k-rows j*KPI .. j*KPI + KPI - 1 (KPI = 512 / C).  Element (k, col) of
+// the tile comes from byte koff(k) + (col0 + col) * 2 of the operand.
+template <int C, typename KOff>
+__device__ __forceinline__ void issue_mnmajor(char* tile, int wave, int lane, int col0, KOff koff,
+                                              __amdgpu_buffer_rsrc_t r) {
+  constexpr int KPI = 512 / C, LPR = C / 8;  // k-rows per instruction, lanes per k-row
+  constexpr int N_INSTR = BK / KPI / NW;       // 1 KB instructions per wave
+  static_assert(N_INSTR * NW * KPI == BK, "the waves' instructions must cover all BK k-rows");
+#pragma unroll
+  for (int i = 0; i < N_INSTR; ++i) {
+    const int j = wave + NW * i;
+    const int k = j * KPI + lane / LPR;
+    const int c = (lane % LPR) ^ swz_mn(k);
+    dma16(r, tile + j * 1024, koff(k) + (uint32_t)(col0 + c * 8) * 2u);
+  }
+}
+
+template <typename F>
+__device__ __forceinline__ F read_kmajor(const char* tile, int r0, int lane) {
+  const int row = r0 + (lane & 15);
+  const int c = lane >> 4;
+  return *(const F*)(tile + row * 64 + ((c ^ swz_k(row)) << 4));
+}
+
+// Fragment of 16 "rows" (columns of the [k][col] tile) x 32 k: lane l gets
+// column c0 + l % 16 and k = 8 (l / 16) .. + 7, via two transposing reads.
+template <int C, typename F>
+__device__ __forceinline__ F read_mnmajor(const char* tile, int c0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int col = c0 + 4 * (j & 3);
+  const int k_lo = 8 * g + (j >> 2);
+  const int k_hi = k_lo + 4;
+  const char* p_lo = tile + k_lo * (2 * C) + ((((col >> 3) ^ swz_mn(k_lo))) << 4) + ((col >> 2) & 1) * 8;
+  const char* p_hi = tile + k_hi * (2 * C) + ((((col >> 3) ^ swz_mn(k_hi))) << 4) + ((col >> 2) & 1) * 8;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p_lo));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p_hi));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(F, v);
+}
+
+// bf16 fragment bits -> fp16 fragment (operands of the fp16 gradient GEMMs).
+__device__ __forceinline__ f16x8 frag_to_f16(f16x8 v) {
+  u32x4 u = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) u[d] = bf16x2_to_f16x2(u[d]);
+  return __builtin_bit_cast(f16x8, u);
+}
+
 template <int MODE>
-__device__ __forceinline__ int b_row(int wn, int j) {
-  if constexpr (MODE == kGateUpH || MODE == kGateUpGU)
-    return j < 2 ? wn * 32 + j * 16 : 64 + wn * 32 + (j - 2) * 16;
-  else
-    return wn * 64 + j * 16;
-}
-
-template <int MODE>
-__global__ __launch_bounds__(NTH) void grouped_gemm_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2][2][TILE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void grouped_gemm_kernel(
+    GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) char lds[NS][STAGE_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   constexpr bool kRowGrouped = MODE != kDW;
   constexpr bool kGateUp = MODE == kGateUpH || MODE == kGateUpGU;
-  // Gradient GEMMs (dXs, dW) multiply fp16 operands: dG/dU/Hw arrive in fp16,
-  // bf16 operands (weights, x, dY) are converted while staging into LDS.
   constexpr bool kF16 = MODE == kDXs || MODE == kDW;
+  constexpr bool kBmn = MODE == kDA || MODE == kDXs || MODE == kDW;  // B row-contiguous
   using frag_t = typename std::conditional<kF16, f16x8, bf16x8>::type;
 
   // ---------------------------------------------------------------- tile decode
-  int e, m0, n0, nk, rows_valid, mat = 0, k_count = 0;
+  int e, m0, n0, nk, rows_valid, mat = 0, k_count = 0, nk_pass = 0, nt_idx = 0;
   size_t kbase = 0;
-  int nt_idx = 0;
   {
     int total;
     if constexpr (kRowGrouped) {
@@ -169,7 +198,7 @@ __global__ __launch_bounds__(NTH) void grouped_gemm_kernel(GemmArgs p) {
       nt_idx = local / mcnt;
       const int mt = local - nt_idx * mcnt;
       m0 = p.offsets[e] + mt * BM;
-      rows_valid = p.offsets[e + 1] - m0;
+      rows_valid = min(BM, p.offsets[e + 1] - m0);
       n0 = nt_idx * (kGateUp ? BN / 2 : BN);
       nk = p.K / BK;
     } else {
@@ -185,120 +214,138 @@ __global__ __launch_bounds__(NTH) void grouped_gemm_kernel(GemmArgs p) {
       n0 = nt_idx * BN;
       kbase = (size_t)p.offsets[e];
       k_count = p.offsets[e + 1] - p.offsets[e];
-      nk = ceil_div(k_count, BK);
+      nk_pass = ceil_div(k_count, BK);
+      // split operand: a second pass over the rows with its low part
+      nk = (p.A_lo || p.B_lo) ? 2 * nk_pass : nk_pass;
       rows_valid = p.M - m0;
     }
   }
 
   // ---------------------------------------------------------------- operand sources
-  const size_t lda = p.lda, ldb = p.ldb;
-  const bf16_t* a_rows = nullptr;  // row-grouped: first A row of the tile
-  const bf16_t* bw0 = nullptr;     // row-grouped: expert weights
-  const bf16_t* bw1 = nullptr;
-  const bf16_t* a_tok = nullptr;   // kDW: A at the expert's first row, column m0
-  const bf16_t* b_tok = nullptr;   // kDW: B at the expert's first row, column n0
+  const uint32_t lda2 = (uint32_t)p.lda * 2u, ldb2 = (uint32_t)p.ldb * 2u;
+  __amdgpu_buffer_rsrc_t rA, rA2, rB, rB2;
   if constexpr (kRowGrouped) {
-    a_rows = p.A + (size_t)m0 * lda;
-    if constexpr (kGateUp) {
-      bw0 = p.B0 + ((size_t)e * p.N + n0) * ldb;  // Wg[e] rows n0.. ([I, D])
-      bw1 = p.B1 + ((size_t)e * p.N + n0) * ldb;
-    } else if constexpr (MODE == kDown) {
-      bw0 = p.B0 + ((size_t)e * p.N + n0) * ldb;  // Wd[e] rows n0.. ([D, I])
-    } else if constexpr (MODE == kDA) {
-      bw0 = p.B0 + (size_t)e * p.K * ldb + n0;    // Wd[e] as (k = d) x (n = i), ld I
-    } else {                                      // kDXs: (k = i) x (n = d), ld D
-      bw0 = p.B0 + (size_t)e * (p.K / 2) * ldb + n0;
-      bw1 = p.B1 + (size_t)e * (p.K / 2) * ldb + n0;
+    rA = make_rsrc(p.A + (size_t)m0 * p.lda, (size_t)rows_valid * lda2);
+    rA2 = rA;
+    if constexpr (kGateUp) {  // rows n0.. of Wg[e], Wu[e] ([I, D])
+      const size_t rows = (size_t)min(BN / 2, p.N - n0);
+      rB = make_rsrc(p.B0 + ((size_t)e * p.N + n0) * p.ldb, rows * ldb2);
+      rB2 = make_rsrc(p.B1 + ((size_t)e * p.N + n0) * p.ldb, rows * ldb2);
+    } else if constexpr (MODE == kDown) {  // rows n0.. of Wd[e] ([D, I])
+      const size_t rows = (size_t)min(BN, p.N - n0);
+      rB = make_rsrc(p.B0 + ((size_t)e * p.N + n0) * p.ldb, rows * ldb2);
+      rB2 = rB;
+    } else if constexpr (MODE == kDA) {  // Wd[e] as (k = d) x (n = i), ld I
+      rB = make_rsrc(p.B0 + (size_t)e * p.K * p.ldb, (size_t)p.K * ldb2);
+      rB2 = rB;
+    } else {  // kDXs: Wg[e] / Wu[e] as (k = i) x (n = d), ld D
+      rB = make_rsrc(p.B0 + (size_t)e * (p.K / 2) * p.ldb, (size_t)(p.K / 2) * ldb2);
+      rB2 = make_rsrc(p.B1 + (size_t)e * (p.K / 2) * p.ldb, (size_t)(p.K / 2) * ldb2);
     }
   } else {
-    a_tok = (mat == 0 ? p.A : p.A2) + kbase * lda + m0;
-    b_tok = p.B0 + kbase * ldb + n0;
+    const bf16_t* a = mat == 0 ? p.A : p.A2;
+    const bf16_t* alo = mat == 0 ? p.A_lo : p.A2_lo;
+    const size_t abytes = (size_t)k_count * lda2, bbytes = (size_t)k_count * ldb2;
+    rA = make_rsrc(a + kbase * p.lda, abytes);
+    rA2 = make_rsrc((alo ? alo : a) + kbase * p.lda, abytes);
+    rB = make_rsrc(p.B0 + kbase * p.ldb, bbytes);
+    rB2 = make_rsrc((p.B_lo ? p.B_lo : p.B0) + kbase * p.ldb, bbytes);
   }
-  const int b_rows_valid = kRowGrouped ? (kGateUp ? BN : p.N - n0) : 0;
 
-  u32x4 ra[4], rb[4];
-  auto load_stage = [&](int kt) {
-    const int k0 = kt * BK;
+  auto issue = [&](int kt) {
+    char* sa = lds[kt % NS];
+    char* sb = sa + A_BYTES;
     if constexpr (kRowGrouped) {
-      load_kmajor(ra, [&](int r) { return a_rows + (size_t)r * lda; }, rows_valid, k0);
+      const uint32_t k0b = (uint32_t)kt * BK * 2u;
+      issue_kmajor<128>(sa, wave, lane, k0b, [&](int row) { return (uint32_t)row * lda2; }, rA);
       if constexpr (kGateUp) {
-        load_kmajor(
-            rb, [&](int r) { return r < 64 ? bw0 + (size_t)r * ldb : bw1 + (size_t)(r - 64) * ldb; },
-            b_rows_valid, k0);
+        // B rows 0..127: gate rows, 128..255: the matching up rows
+        issue_kmajor<128>(sb, wave, lane, k0b, [&](int row) { return (uint32_t)row * ldb2; }, rB);
+        issue_kmajor<128>(sb + 128 * BK * 2, wave, lane, k0b,
+                        [&](int row) { return (uint32_t)row * ldb2; }, rB2);
       } else if constexpr (MODE == kDown) {
-        load_kmajor(rb, [&](int r) { return bw0 + (size_t)r * ldb; }, b_rows_valid, k0);
+        issue_kmajor<256>(sb, wave, lane, k0b, [&](int row) { return (uint32_t)row * ldb2; }, rB);
       } else if constexpr (MODE == kDA) {
-        load_mnmajor(rb, bw0 + (size_t)k0 * ldb, ldb, BK, b_rows_valid);
-      } else {
-        const int half = p.K / 2;
-        const bf16_t* src = k0 < half ? bw0 + (size_t)k0 * ldb : bw1 + (size_t)(k0 - half) * ldb;
-        load_mnmajor(rb, src, ldb, BK, b_rows_valid);
+        const int k0 = kt * BK;
+        issue_mnmajor<BN>(sb, wave, lane, n0, [&](int k) { return (uint32_t)(k0 + k) * ldb2; }, rB);
+      } else {  // kDXs: k < I from Wg, k >= I from Wu
+        const int half = p.K / 2, k0 = kt * BK;
+        const bool up = k0 >= half;
+        const int kr = up ? k0 - half : k0;
+        issue_mnmajor<BN>(sb, wave, lane, n0, [&](int k) { return (uint32_t)(kr + k) * ldb2; },
+                          up ? rB2 : rB);
       }
     } else {
-      const int kv = k_count - k0;
-      load_mnmajor(ra, a_tok + (size_t)k0 * lda, lda, kv, p.M - m0);
-      load_mnmajor(rb, b_tok + (size_t)k0 * ldb, ldb, kv, p.N - n0);
-    }
-  };
-  auto store_stage = [&](int buf) {
-    if constexpr (kF16) {
-      if (p.cvt_a) to_f16(ra);
-      if (p.cvt_b) to_f16(rb);
-    }
-    if constexpr (kRowGrouped) {
-      store_kmajor(lds[buf][0], ra);
-      if constexpr (MODE == kDA || MODE == kDXs) store_mnmajor(lds[buf][1], rb);
-      else store_kmajor(lds[buf][1], rb);
-    } else {
-      store_mnmajor(lds[buf][0], ra);
-      store_mnmajor(lds[buf][1], rb);
+      // stages [0, nk_pass): hi (or unsplit) operands; [nk_pass, 2 nk_pass): the
+      // split operand's low part against the same exact operand
+      const bool lo_pass = kt >= nk_pass;
+      const int k0 = (lo_pass ? kt - nk_pass : kt) * BK;
+      issue_mnmajor<BM>(sa, wave, lane, m0, [&](int k) { return (uint32_t)(k0 + k) * lda2; },
+                        lo_pass ? rA2 : rA);
+      issue_mnmajor<BN>(sb, wave, lane, n0, [&](int k) { return (uint32_t)(k0 + k) * ldb2; },
+                        lo_pass ? rB2 : rB);
     }
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][FN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---------------------------------------------------------------- main loop
-  if (nk > 0) {
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-  }
-  const int frow = lane & 15, fk = (lane >> 4) * 8;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_stage(kt + 1);
-    const bf16_t* la = lds[cur][0];
-    const bf16_t* lb = lds[cur][1];
+    // stage kt has landed once at most the next stage's 6 loads are in flight
+    if (kt + 1 < nk) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // every wave's part of stage kt is in LDS, and
+    asm volatile("" ::: "memory");  // every wave is done reading stage kt - 1
+    if (kt + NS - 1 < nk) issue(kt + NS - 1);
+    const char* sa = lds[kt % NS];
+    const char* sb = sa + A_BYTES;
+    frag_t af[4], bfr[FN];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      frag_t af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *(const frag_t*)(la + (wm * 64 + i * 16 + frow) * LDSR + kk + fk);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *(const frag_t*)(lb + (b_row<MODE>(wn, j) + frow) * LDSR + kk + fk);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if constexpr (kF16)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-        }
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (kRowGrouped) af[i] = read_kmajor<frag_t>(sa, wm * 64 + i * 16, lane);
+      else af[i] = read_mnmajor<BM, frag_t>(sa, wm * 64 + i * 16, lane);
     }
-    if (kt + 1 < nk) store_stage(cur ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (kGateUp) {
+        const int r = j < FN / 2 ? wn * 64 + j * 16 : 128 + wn * 64 + (j - FN / 2) * 16;
+        bfr[j] = read_kmajor<frag_t>(sb, r, lane);
+      } else if constexpr (kBmn) {
+        bfr[j] = read_mnmajor<BN, frag_t>(sb, wn * WTN + j * 16, lane);
+      } else {
+        bfr[j] = read_kmajor<frag_t>(sb, wn * WTN + j * 16, lane);
+      }
+    }
+    if constexpr (kF16) {
+      if (p.cvt_a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = frag_to_f16(af[i]);
+      if (p.cvt_b)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bfr[j] = frag_to_f16(bfr[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (kF16)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+      }
   }
 
   // ---------------------------------------------------------------- epilogue
   // Lane holds, for fragment (i, j), row wm*64 + i*16 + (lane % 16) and the 4
-  // consecutive columns b_row(wn, j) + 4*(lane / 16) + q of the tile.
+  // consecutive columns of B fragment j starting at 4 * (lane / 16).
+  const int frow = lane & 15;
   const int cq = 4 * (lane >> 4);
   if constexpr (MODE == kGateUpH || MODE == kGateUpGU) {
 #pragma unroll
@@ -307,9 +354,10 @@ __global__ __launch_bounds__(NTH) void grouped_gemm_kernel(GemmArgs p) {
       if (r >= rows_valid) continue;
       const size_t m = (size_t)(m0 + r);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = n0 + wn * 32 + j * 16 + cq;
-        const f32x4 g = acc[i][j], u = acc[i][j + 2];
+      for (int j = 0; j < FN / 2; ++j) {
+        const int col = n0 + wn * 64 + j * 16 + cq;
+        if (col >= p.N) continue;
+        const f32x4 g = acc[i][j], u = acc[i][j + FN / 2];
         if constexpr (MODE == kGateUpH) {
           float h[4];
 #pragma unroll
@@ -329,8 +377,8 @@ __global__ __launch_bounds__(NTH) void grouped_gemm_kernel(GemmArgs p) {
       if (r >= rows_valid) continue;
       const size_t m = (size_t)(m0 + r);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 64 + j * 16 + cq;
+      for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn * WTN + j * 16 + cq;
         if (col >= p.N) continue;
         const f32x4 v = acc[i][j];
         if constexpr (MODE == kDXs)  // fp32 rows: the K copies of a token are summed later
@@ -342,7 +390,7 @@ __global__ __launch_bounds__(NTH) void grouped_gemm_kernel(GemmArgs p) {
   } else if constexpr (MODE == kDA) {
     // dA = dY_routed Wd (fp32).  With g, u recomputed (fp32) and w the router
     // weight of the row:  h = silu(g) u;  partial dRW = sum dA h over the
-    // wave's 64 columns;  dH = w dA;  dG = dH u silu'(g);  dU = dH silu(g);
+    // wave's 128 columns;  dH = w dA;  dG = dH u silu'(g);  dU = dH silu(g);
     // Hw = w h (the weighted activations that dW_down needs).
     const int I = p.N;
 #pragma unroll
@@ -353,12 +401,13 @@ __global__ __launch_bounds__(NTH) void grouped_gemm_kernel(GemmArgs p) {
       const float wr = row_ok ? p.topk_w[p.s2f[m]] : 0.0f;
       float dot = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 64 + j * 16 + cq;
+      for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn * WTN + j * 16 + cq;
         if (!row_ok || col >= I) continue;
         const f32x4 gv = *(const f32x4*)(p.GU + m * (2 * (size_t)I) + col);
         const f32x4 uv = *(const f32x4*)(p.GU + m * (2 * (size_t)I) + I + col);
         float dg[4], du[4], hw[4];
+        uint32_t lo_dg[2], lo_du[2], lo_hw[2];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float g = gv[q];
@@ -372,10 +421,23 @@ __global__ __launch_bounds__(NTH) void grouped_gemm_kernel(GemmArgs p) {
           du[q] = dh * g * sg;
           hw[q] = wr * h;
         }
-        // fp16 (round to nearest): operands of the fp16 gradient GEMMs
-        *(u32x2*)(p.C0 + m * p.ldc + col) = u32x2{pack_f16x2(dg[0], dg[1]), pack_f16x2(dg[2], dg[3])};
-        *(u32x2*)(p.C1 + m * p.ldc + col) = u32x2{pack_f16x2(du[0], du[1]), pack_f16x2(du[2], du[3])};
-        *(u32x2*)(p.C2 + m * (size_t)I + col) = u32x2{pack_f16x2(hw[0], hw[1]), pack_f16x2(hw[2], hw[3])};
+        // fp16 hi = round(v) and lo = round(v - hi): the dX GEMM reads hi, the
+        // dW GEMMs read hi and lo
+        const u32x2 hi_dg = {pack_f16x2(dg[0], dg[1]), pack_f16x2(dg[2], dg[3])};
+        const u32x2 hi_du = {pack_f16x2(du[0], du[1]), pack_f16x2(du[2], du[3])};
+        const u32x2 hi_hw = {pack_f16x2(hw[0], hw[1]), pack_f16x2(hw[2], hw[3])};
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          lo_dg[h2] = f16x2_residual(dg[2 * h2], dg[2 * h2 + 1], hi_dg[h2]);
+          lo_du[h2] = f16x2_residual(du[2 * h2], du[2 * h2 + 1], hi_du[h2]);
+          lo_hw[h2] = f16x2_residual(hw[2 * h2], hw[2 * h2 + 1], hi_hw[h2]);
+        }
+        *(u32x2*)(p.C0 + m * p.ldc + col) = hi_dg;
+        *(u32x2*)(p.C1 + m * p.ldc + col) = hi_du;
+        *(u32x2*)(p.C2 + m * (size_t)I + col) = hi_hw;
+        *(u32x2*)(p.L0 + m * p.ldc + col) = u32x2{lo_dg[0], lo_dg[1]};
+        *(u32x2*)(p.L1 + m * p.ldc + col) = u32x2{lo_du[0], lo_du[1]};
+        *(u32x2*)(p.L2 + m * (size_t)I + col) = u32x2{lo_hw[0], lo_hw[1]};
       }
       dot += __shfl_xor(dot, 16);
       dot += __shfl_xor(dot, 32);
@@ -386,10 +448,10 @@ __global__ __launch_bounds__(NTH) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm * 64 + i * 16 + frow;
-      if (m0 + r >= p.M) continue;
+      if (r >= rows_valid) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 64 + j * 16 + cq;
+      for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn * WTN + j * 16 + cq;
         if (col >= p.N) continue;
         f32x4* dst = (f32x4*)(out + (size_t)(m0 + r) * p.N + col);
         f32x4 v = acc[i][j];

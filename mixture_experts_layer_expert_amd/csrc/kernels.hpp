@@ -48,8 +48,8 @@ hipError_t launch_reduce_partials(const float* part, const int32_t* f2s, float* 
 
 // ---- grouped GEMMs (gemm.hip)
 constexpr int kGemmBM = 128;  // rows of a workgroup tile (routed rows or dW rows)
-constexpr int kGemmBN = 128;  // columns of a workgroup tile (gate/up: 64 gate + 64 up)
-constexpr int kGemmBK = 64;   // reduction depth of one LDS stage
+constexpr int kGemmBN = 256;  // columns of a workgroup tile (gate/up: 128 gate + 128 up)
+constexpr int kGemmBK = 32;   // reduction depth of one LDS stage
 
 enum GemmMode : int {
   kGateUpH = 0,   // H  = silu(Xs Wg^T) * (Xs Wu^T)                       bf16 [R, I]
@@ -71,13 +71,19 @@ struct GemmArgs {
   int E;
   int M, N, K;  // kDW: output M x N per expert.  Row-grouped: N output cols, K reduction
   int lda, ldb;
-  int n_tiles;  // row-grouped: column tiles per m-tile
+  int n_tiles;  // row-grouped: column tiles per m-tile (gate/up: ceil(I/128), else ceil(N/256))
   int nmat;     // kDW: matrices in this launch (1 or 2)
   int cvt_a, cvt_b;  // kDXs / kDW: operand stored as bf16, convert to fp16 when staging
+  const f16_t* A_lo;   // kDW: low fp16 parts of a split A (mat 0) / A2 (mat 1), or null
+  const f16_t* A2_lo;
+  const f16_t* B_lo;   // kDW: low fp16 part of a split B, or null
   // epilogue operands
   bf16_t* C0;
   bf16_t* C1;
   bf16_t* C2;
+  f16_t* L0;  // kDA: low fp16 parts of dG, dU, Hw
+  f16_t* L1;
+  f16_t* L2;
   int ldc;
   float* Cf;
   float* Cf2;
