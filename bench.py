@@ -55,12 +55,36 @@ def kernel_work(wl: synth.Workload) -> dict:
         "gather": ("hbm", 4.0 * R * D + 4 * R), "gather2": ("hbm", 8.0 * R * D + 4 * R),
         # combine: read O (R*D*2), weights and indices (8R), write y (T*D*2)
         "combine": ("hbm", 2.0 * R * D + 8 * R + 2.0 * T * D),
-        "reduce_rows": ("hbm", 2.0 * R * D + 4 * R + 2.0 * T * D),
-        "reduce_partials": ("hbm", 4.0 * R * (2 * math.ceil(I / 128)) + 8 * R),
+        # dX reduce: read the fp32 per-row partials (R*D*4) and indices, write dX (T*D*2)
+        "reduce_rows": ("hbm", 4.0 * R * D + 4 * R + 2.0 * T * D),
+        "reduce_partials": ("hbm", 4.0 * R * (2 * math.ceil(I / 256)) + 8 * R),
         "route_topk": ("hbm", 4.0 * T * E + 8 * R),
         "route_hist": ("hbm", 4.0 * R), "route_scan": ("hbm", 8.0 * E),
         "route_scatter": ("hbm", 12.0 * R), "tilemap": ("hbm", 8.0 * E),
     }
+
+
+GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_expert_amd", "csrc", "gemm.hip")
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary profiles/<kernel>_<workload>_traffic.txt (FETCH_SIZE + WRITE_SIZE,
+    copy-calibrated), or None when there is none or when the GEMM source has
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if kv.get("gemm_source_sha256") != sha or "bytes_per_launch" not in kv:
+        return None
+    return float(kv["bytes_per_launch"])
 
 
 def cpu_baseline(wl: synth.Workload, data: dict, n_tokens: int) -> dict:
@@ -95,10 +119,13 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_30b_a3b", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-tokens", type=int, default=32,
+    ap.add_argument("--cpu-tokens", type=int, default=384,
                     help="tokens in the CPU-oracle baseline sample (0: skip)")
     ap.add_argument("--fwd-bwd-only", action="store_true",
                     help="time only the full steps (skip the separate fwd/bwd timing)")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="before the steps, run a plain device copy of this many MiB (twice), "
+                         "as the reference dispatch that scales HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not supported "
@@ -110,6 +137,14 @@ def main() -> int:
     from tests import gpu_common as G
 
     moe.load_library()
+    if args.copy_calib_mb > 0:
+        n = args.copy_calib_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wl = WORKLOADS[args.workload]
     data = synth.generate(wl)
     dev = G.DeviceInputs(data)
@@ -197,7 +232,8 @@ def main() -> int:
                    "seed": wl.seed},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": stored_traffic(dom, wl.name)},
         **extra,
         "gemm_tflops_all": round(gemm_flops / (gemm_total_ms * 1e-3) / 1e12, 2),
         "gemm_frac_all": round(gemm_flops / (gemm_total_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),

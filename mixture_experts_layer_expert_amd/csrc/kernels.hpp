@@ -1,7 +1,7 @@
 // Internal declarations of the MoE library's kernels and launchers.
 #pragma once
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "common.hpp"
 
 namespace moe {
