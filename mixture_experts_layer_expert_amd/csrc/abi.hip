@@ -71,7 +71,7 @@ struct BwdWs {
 };
 
 // router-weight-gradient partials per routed row: one per (column tile, wave column)
-int partials_per_row(const moe_dims& d) { return 2 * ((d.I + kGemmBN - 1) / kGemmBN); }
+int partials_per_row(const moe_dims& d) { return kGemmWN * ((d.I + kGemmBN - 1) / kGemmBN); }
 
 size_t route_ws(const moe_dims& d, int32_t** hist, void* base) {
   Carve c{(char*)base};

@@ -9,17 +9,21 @@
 // (TMA, warp-specialised WGMMA/UMMA, TMA reduce stores) is prior art only;
 // here every GEMM is one CDNA4 kernel:
 //
-//   - a 256-thread workgroup (4 waves) owns a 128 x 256 output tile; waves in
-//     2 (rows) x 2 (columns), each 64 x 128 = 4 x 8 fragments of
-//     v_mfma_f32_16x16x32_{bf16,f16} with fp32 accumulators;
+//   - a 512-thread workgroup (8 waves) owns a 256 x 256 output tile; waves in
+//     2 (rows) x 4 (columns), each 128 x 64 = 8 x 4 fragments of
+//     v_mfma_f32_16x16x32_{bf16,f16} with fp32 accumulators (the geometry is
+//     a compile-time choice in kernels.hpp; 128 x 256 tiles, 4 waves and
+//     32-deep stages are the other supported settings);
 //   - operands go HBM -> LDS directly (buffer_load ... lds: no VGPR staging),
-//     three 32-deep K stages in flight, one barrier per stage; a buffer
-//     resource per operand bounds the loads, so rows past a ragged edge read as
-//     zeros in hardware.  72 KB of LDS per workgroup lets two workgroups share
-//     a CU, so one's memory-bound epilogue overlaps the other's MFMA loop;
+//     64-deep K stages, double-buffered (128 KB of LDS, one workgroup per CU),
+//     one barrier per stage: the next stage's loads are issued right after the
+//     barrier and land while the MFMAs consume the current one.  A buffer
+//     resource per operand bounds the loads, so rows past a ragged edge read
+//     as zeros in hardware;
 //   - LDS keeps each operand in its HBM orientation, XOR-swizzled instead of
-//     padded.  k-contiguous operands ([row][k], 64-byte rows, 16-byte chunk c
-//     of row r stored at c ^ (r/4 % 4)) are read with ds_read_b128;
+//     padded.  k-contiguous operands ([row][k], 128-byte rows of eight 16-byte
+//     chunks; chunk c of row r stored at c ^ (r/2 % 8), or for 32-deep stages
+//     64-byte rows with c ^ (r/4 % 4)) are read with ds_read_b128;
 //     row-contiguous operands ([k][row], the token-major activations of the
 //     weight gradients and the weights read transposed; chunk c of k-row k
 //     stored at c ^ s(k), s(k) = 2 (k % 4) + 8 ((k/8 + k/16) % 2)) are read
@@ -56,17 +60,25 @@
 namespace moe {
 
 constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
-constexpr int NW = 4, NTH = NW * kWave;  // 4 waves: 2 (rows) x 2 (columns)
-constexpr int WTN = BN / 2;              // columns per wave (128)
-constexpr int FN = WTN / 16;             // B fragments per wave (8)
-constexpr int NS = 3;                    // K stages resident in LDS
-constexpr int A_BYTES = BM * BK * 2;     // 8 KB: 128 rows x 32 k, or 32 k x 128 rows
-constexpr int B_BYTES = BN * BK * 2;     // 16 KB
+constexpr int WM = kGemmWM, WN = kGemmWN;
+constexpr int NW = WM * WN, NTH = NW * kWave;
+constexpr int WTM = BM / WM, WTN = BN / WN;  // rows / columns per wave
+constexpr int FM = WTM / 16, FN = WTN / 16;  // A / B fragments per wave
+constexpr int NS = kGemmNS;                  // K stages resident in LDS
+constexpr int A_BYTES = BM * BK * 2;         // BM rows x BK k, or BK k x BM rows
+constexpr int B_BYTES = BN * BK * 2;
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-constexpr int LOADS_PER_STAGE = (A_BYTES + B_BYTES) / 1024 / NW;  // per wave: 6
+constexpr int LOADS_PER_STAGE = (A_BYTES + B_BYTES) / 1024 / NW;  // 1 KB loads per wave
 
-static_assert(BM == 128 && BN == 256 && BK == 32, "tile geometry is fixed by the loaders");
-static_assert(LOADS_PER_STAGE == 6, "s_waitcnt immediates below assume 6 loads per stage");
+static_assert(BK == 32 || BK == 64, "the loaders and swizzles handle 32- or 64-deep stages");
+constexpr int KROW = BK * 2;       // bytes of one k-contiguous row in LDS (64 or 128)
+constexpr int KCH = BK / 8;        // 16-byte chunks per k-contiguous row (4 or 8)
+constexpr int KRPI = 1024 / KROW;  // k-contiguous rows per 1 KB load instruction (16 or 8)
+static_assert(BM % (16 * WM) == 0 && BN % (32 * WN) == 0 && (BM == 128 || BM == 256) &&
+                  (BN == 128 || BN == 256),
+              "unsupported tile geometry");
+static_assert(NS * STAGE_BYTES <= 160 * 1024, "LDS budget");
+static_assert(NS >= 2, "at least double buffering");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
@@ -86,29 +98,31 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_wave_b
 // same k-chunk land in 16 distinct 16-byte bank groups.  swz_mn: the four
 // 16-lane groups of a transposing read (k-rows 8g..8g+3) split into two pairs
 // that each cover all 64 banks, for either pairing of the groups.
-__device__ __forceinline__ int swz_k(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int swz_k(int row) {
+  return BK == 32 ? (row >> 2) & 3 : (row >> 1) & 7;
+}
 __device__ __forceinline__ int swz_mn(int k) {
   return ((k & 3) << 1) | ((((k >> 3) ^ (k >> 4)) & 1) << 3);
 }
 
-// k-contiguous tile of ROWS rows x 32 k (64-byte rows): this wave's
-// instructions j = wave + 4 i each fill rows 16j..16j+15.  off(row) = byte
-// offset of the row's k = 0 element.
+// k-contiguous tile of ROWS rows x BK k (KROW-byte rows): this wave's
+// instructions j = wave + NW i each fill rows KRPI j .. KRPI j + KRPI - 1.
+// off(row) = byte offset of the row's k = 0 element.
 template <int ROWS, typename RowOff>
 __device__ __forceinline__ void issue_kmajor(char* tile, int wave, int lane, uint32_t k0_bytes,
                                              RowOff off, __amdgpu_buffer_rsrc_t r) {
-  constexpr int N_INSTR = ROWS / 16 / NW;  // 1 KB instructions (16 rows of 64 B) per wave
-  static_assert(N_INSTR * NW * 16 == ROWS, "the waves' instructions must cover all rows");
+  constexpr int N_INSTR = ROWS / KRPI / NW;  // 1 KB instructions (KRPI rows) per wave
+  static_assert(N_INSTR * NW * KRPI == ROWS, "the waves' instructions must cover all rows");
 #pragma unroll
   for (int i = 0; i < N_INSTR; ++i) {
     const int j = wave + NW * i;
-    const int row = 16 * j + (lane >> 2);
-    const int c = (lane & 3) ^ swz_k(row);
+    const int row = KRPI * j + lane / KCH;
+    const int c = (lane % KCH) ^ swz_k(row);
     dma16(r, tile + j * 1024, off(row) + k0_bytes + c * 16);
   }
 }
 
-// Row-contiguous tile of 32 k-rows x C columns (C = 128 or 256): instruction j
+// Row-contiguous tile of BK k-rows x C columns (C = 128 or 256): instruction j
 // fills k-rows j*KPI .. j*KPI + KPI - 1 (KPI = 512 / C).  Element (k, col) of
 // the tile comes from byte koff(k) + (col0 + col) * 2 of the operand.
 template <int C, typename KOff>
@@ -126,20 +140,22 @@ __device__ __forceinline__ void issue_mnmajor(char* tile, int wave, int lane, in
   }
 }
 
+// Fragment of 16 rows x 32 k starting at k = kk (a multiple of 32): lane l
+// gets row r0 + l % 16, k = kk + 8 (l / 16) .. + 7.
 template <typename F>
-__device__ __forceinline__ F read_kmajor(const char* tile, int r0, int lane) {
+__device__ __forceinline__ F read_kmajor(const char* tile, int r0, int kk, int lane) {
   const int row = r0 + (lane & 15);
-  const int c = lane >> 4;
-  return *(const F*)(tile + row * 64 + ((c ^ swz_k(row)) << 4));
+  const int c = (kk >> 3) + (lane >> 4);
+  return *(const F*)(tile + row * KROW + ((c ^ swz_k(row)) << 4));
 }
 
 // Fragment of 16 "rows" (columns of the [k][col] tile) x 32 k: lane l gets
-// column c0 + l % 16 and k = 8 (l / 16) .. + 7, via two transposing reads.
+// column c0 + l % 16 and k = kk + 8 (l / 16) .. + 7, via two transposing reads.
 template <int C, typename F>
-__device__ __forceinline__ F read_mnmajor(const char* tile, int c0, int lane) {
+__device__ __forceinline__ F read_mnmajor(const char* tile, int c0, int kk, int lane) {
   const int g = lane >> 4, j = lane & 15;
   const int col = c0 + 4 * (j & 3);
-  const int k_lo = 8 * g + (j >> 2);
+  const int k_lo = kk + 8 * g + (j >> 2);
   const int k_hi = k_lo + 4;
   const char* p_lo = tile + k_lo * (2 * C) + ((((col >> 3) ^ swz_mn(k_lo))) << 4) + ((col >> 2) & 1) * 8;
   const char* p_hi = tile + k_hi * (2 * C) + ((((col >> 3) ^ swz_mn(k_hi))) << 4) + ((col >> 2) & 1) * 8;
@@ -148,6 +164,19 @@ __device__ __forceinline__ F read_mnmajor(const char* tile, int c0, int lane) {
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(F, v);
+}
+
+// Waits until at most min(N, later) stages of LOADS_PER_STAGE loads per wave
+// are outstanding, where `later` stages were issued after the one needed now.
+template <int N>
+__device__ __forceinline__ void wait_stage(int later) {
+  static_assert(N * LOADS_PER_STAGE <= 63, "vmcnt holds at most 63");
+  if constexpr (N == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (later >= N) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N * LOADS_PER_STAGE) : "memory");
+    else wait_stage<N - 1>(later);
+  }
 }
 
 // bf16 fragment bits -> fp16 fragment (operands of the fp16 gradient GEMMs).
@@ -164,7 +193,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   __shared__ __attribute__((aligned(1024))) char lds[NS][STAGE_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   constexpr bool kRowGrouped = MODE != kDW;
   constexpr bool kGateUp = MODE == kGateUpH || MODE == kGateUpGU;
   constexpr bool kF16 = MODE == kDXs || MODE == kDW;
@@ -199,7 +228,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       const int mt = local - nt_idx * mcnt;
       m0 = p.offsets[e] + mt * BM;
       rows_valid = min(BM, p.offsets[e + 1] - m0);
-      n0 = nt_idx * (kGateUp ? BN / 2 : BN);
+      n0 = nt_idx * (kGateUp ? BN / 2 : BN);  // gate/up tiles: BN/2 gate + BN/2 up rows
       nk = p.K / BK;
     } else {
       const int tm = ceil_div(p.M, BM), tn = ceil_div(p.N, BN);
@@ -257,14 +286,14 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     char* sb = sa + A_BYTES;
     if constexpr (kRowGrouped) {
       const uint32_t k0b = (uint32_t)kt * BK * 2u;
-      issue_kmajor<128>(sa, wave, lane, k0b, [&](int row) { return (uint32_t)row * lda2; }, rA);
+      issue_kmajor<BM>(sa, wave, lane, k0b, [&](int row) { return (uint32_t)row * lda2; }, rA);
       if constexpr (kGateUp) {
         // B rows 0..127: gate rows, 128..255: the matching up rows
-        issue_kmajor<128>(sb, wave, lane, k0b, [&](int row) { return (uint32_t)row * ldb2; }, rB);
-        issue_kmajor<128>(sb + 128 * BK * 2, wave, lane, k0b,
-                        [&](int row) { return (uint32_t)row * ldb2; }, rB2);
+        issue_kmajor<BN / 2>(sb, wave, lane, k0b, [&](int row) { return (uint32_t)row * ldb2; }, rB);
+        issue_kmajor<BN / 2>(sb + (BN / 2) * BK * 2, wave, lane, k0b,
+                             [&](int row) { return (uint32_t)row * ldb2; }, rB2);
       } else if constexpr (MODE == kDown) {
-        issue_kmajor<256>(sb, wave, lane, k0b, [&](int row) { return (uint32_t)row * ldb2; }, rB);
+        issue_kmajor<BN>(sb, wave, lane, k0b, [&](int row) { return (uint32_t)row * ldb2; }, rB);
       } else if constexpr (MODE == kDA) {
         const int k0 = kt * BK;
         issue_mnmajor<BN>(sb, wave, lane, n0, [&](int k) { return (uint32_t)(k0 + k) * ldb2; }, rB);
@@ -287,9 +316,9 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     }
   };
 
-  f32x4 acc[4][FN];
+  f32x4 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -298,41 +327,43 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk) issue(s);
   for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once at most the next stage's 6 loads are in flight
-    if (kt + 1 < nk) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // stage kt has landed once only the stages issued after it (at most NS - 2)
+    // are still in flight
+    wait_stage<NS - 2>(nk - 1 - kt);
     __builtin_amdgcn_s_barrier();  // every wave's part of stage kt is in LDS, and
     asm volatile("" ::: "memory");  // every wave is done reading stage kt - 1
     if (kt + NS - 1 < nk) issue(kt + NS - 1);
     const char* sa = lds[kt % NS];
     const char* sb = sa + A_BYTES;
-    frag_t af[4], bfr[FN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (kRowGrouped) af[i] = read_kmajor<frag_t>(sa, wm * 64 + i * 16, lane);
-      else af[i] = read_mnmajor<BM, frag_t>(sa, wm * 64 + i * 16, lane);
+    for (int kk = 0; kk < BK; kk += 32) {
+    frag_t af[FM], bfr[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if constexpr (kRowGrouped) af[i] = read_kmajor<frag_t>(sa, wm * WTM + i * 16, kk, lane);
+      else af[i] = read_mnmajor<BM, frag_t>(sa, wm * WTM + i * 16, kk, lane);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       if constexpr (kGateUp) {
-        const int r = j < FN / 2 ? wn * 64 + j * 16 : 128 + wn * 64 + (j - FN / 2) * 16;
-        bfr[j] = read_kmajor<frag_t>(sb, r, lane);
+        const int r = j < FN / 2 ? wn * (WTN / 2) + j * 16 : BN / 2 + wn * (WTN / 2) + (j - FN / 2) * 16;
+        bfr[j] = read_kmajor<frag_t>(sb, r, kk, lane);
       } else if constexpr (kBmn) {
-        bfr[j] = read_mnmajor<BN, frag_t>(sb, wn * WTN + j * 16, lane);
+        bfr[j] = read_mnmajor<BN, frag_t>(sb, wn * WTN + j * 16, kk, lane);
       } else {
-        bfr[j] = read_kmajor<frag_t>(sb, wn * WTN + j * 16, lane);
+        bfr[j] = read_kmajor<frag_t>(sb, wn * WTN + j * 16, kk, lane);
       }
     }
     if constexpr (kF16) {
       if (p.cvt_a)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = frag_to_f16(af[i]);
+        for (int i = 0; i < FM; ++i) af[i] = frag_to_f16(af[i]);
       if (p.cvt_b)
 #pragma unroll
         for (int j = 0; j < FN; ++j) bfr[j] = frag_to_f16(bfr[j]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         if constexpr (kF16)
@@ -340,6 +371,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
         else
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
       }
+    }
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -349,13 +381,13 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int cq = 4 * (lane >> 4);
   if constexpr (MODE == kGateUpH || MODE == kGateUpGU) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 64 + i * 16 + frow;
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WTM + i * 16 + frow;
       if (r >= rows_valid) continue;
       const size_t m = (size_t)(m0 + r);
 #pragma unroll
       for (int j = 0; j < FN / 2; ++j) {
-        const int col = n0 + wn * 64 + j * 16 + cq;
+        const int col = n0 + wn * (WTN / 2) + j * 16 + cq;
         if (col >= p.N) continue;
         const f32x4 g = acc[i][j], u = acc[i][j + FN / 2];
         if constexpr (MODE == kGateUpH) {
@@ -372,8 +404,8 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     }
   } else if constexpr (MODE == kDown || MODE == kDXs) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 64 + i * 16 + frow;
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WTM + i * 16 + frow;
       if (r >= rows_valid) continue;
       const size_t m = (size_t)(m0 + r);
 #pragma unroll
@@ -390,12 +422,12 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   } else if constexpr (MODE == kDA) {
     // dA = dY_routed Wd (fp32).  With g, u recomputed (fp32) and w the router
     // weight of the row:  h = silu(g) u;  partial dRW = sum dA h over the
-    // wave's 128 columns;  dH = w dA;  dG = dH u silu'(g);  dU = dH silu(g);
+    // wave's WTN columns;  dH = w dA;  dG = dH u silu'(g);  dU = dH silu(g);
     // Hw = w h (the weighted activations that dW_down needs).
     const int I = p.N;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 64 + i * 16 + frow;
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WTM + i * 16 + frow;
       const bool row_ok = r < rows_valid;
       const size_t m = (size_t)(m0 + (row_ok ? r : 0));
       const float wr = row_ok ? p.topk_w[p.s2f[m]] : 0.0f;
@@ -441,13 +473,13 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       }
       dot += __shfl_xor(dot, 16);
       dot += __shfl_xor(dot, 32);
-      if (row_ok && lane < 16) p.part[m * p.np + nt_idx * 2 + wn] = dot;
+      if (row_ok && lane < 16) p.part[m * p.np + nt_idx * WN + wn] = dot;
     }
   } else {  // kDW
     float* out = (mat == 0 ? p.Cf : p.Cf2) + (size_t)e * p.M * p.N;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 64 + i * 16 + frow;
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WTM + i * 16 + frow;
       if (r >= rows_valid) continue;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {

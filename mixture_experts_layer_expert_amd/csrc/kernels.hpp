@@ -47,9 +47,32 @@ hipError_t launch_reduce_partials(const float* part, const int32_t* f2s, float* 
                                   int np, hipStream_t st);
 
 // ---- grouped GEMMs (gemm.hip)
-constexpr int kGemmBM = 128;  // rows of a workgroup tile (routed rows or dW rows)
-constexpr int kGemmBN = 256;  // columns of a workgroup tile (gate/up: 128 gate + 128 up)
-constexpr int kGemmBK = 32;   // reduction depth of one LDS stage
+// Workgroup tile geometry (shared by the kernels and the host-side tile
+// accounting).  The waves of a workgroup form a WM x WN grid.
+#ifndef MOE_GEMM_BM
+#define MOE_GEMM_BM 256
+#endif
+#ifndef MOE_GEMM_BN
+#define MOE_GEMM_BN 256
+#endif
+#ifndef MOE_GEMM_WM
+#define MOE_GEMM_WM 2
+#endif
+#ifndef MOE_GEMM_WN
+#define MOE_GEMM_WN 4
+#endif
+#ifndef MOE_GEMM_NS
+#define MOE_GEMM_NS 2
+#endif
+constexpr int kGemmBM = MOE_GEMM_BM;  // rows of a workgroup tile (routed rows or dW rows)
+constexpr int kGemmBN = MOE_GEMM_BN;  // columns of a tile (gate/up: BN/2 gate + BN/2 up)
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
+constexpr int kGemmBK = MOE_GEMM_BK;  // reduction depth of one LDS stage (32 or 64)
+constexpr int kGemmWM = MOE_GEMM_WM;  // waves along the rows
+constexpr int kGemmWN = MOE_GEMM_WN;  // waves along the columns
+constexpr int kGemmNS = MOE_GEMM_NS;  // K stages resident in LDS
 
 enum GemmMode : int {
   kGateUpH = 0,   // H  = silu(Xs Wg^T) * (Xs Wu^T)                       bf16 [R, I]
