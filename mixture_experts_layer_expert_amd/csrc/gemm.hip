@@ -79,6 +79,10 @@ static_assert(BM % (16 * WM) == 0 && BN % (32 * WN) == 0 && (BM == 128 || BM == 
               "unsupported tile geometry");
 static_assert(NS * STAGE_BYTES <= 160 * 1024, "LDS budget");
 static_assert(NS >= 2, "at least double buffering");
+constexpr int PREFETCH = kGemmPrefetch;  // L2 prefetch distance in stages (0: off)
+static_assert(PREFETCH == 0 || (NS == 2 && BK == 64 && BM == 256 && BN == 256 && NW == 8),
+              "the L2 prefetch covers a 256 x 256 x 64 stage with 8 waves, double-buffered");
+static_assert(NS * STAGE_BYTES + (PREFETCH ? NW * 256 : 0) <= 160 * 1024, "LDS budget");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
@@ -108,13 +112,21 @@ __device__ __forceinline__ int swz_mn(int k) {
 // k-contiguous tile of ROWS rows x BK k (KROW-byte rows): this wave's
 // instructions j = wave + NW i each fill rows KRPI j .. KRPI j + KRPI - 1.
 // off(row) = byte offset of the row's k = 0 element.
+template <int ROWS>
+constexpr int kmajor_instrs() { return ROWS / KRPI / NW; }
+
+// Issues this wave's instructions i of the tile whose piece number qbase + i
+// lies in [q0, q1) (pieces let the caller spread a stage's loads over the
+// MFMA sequence; with constant bounds the tests fold away).
 template <int ROWS, typename RowOff>
 __device__ __forceinline__ void issue_kmajor(char* tile, int wave, int lane, uint32_t k0_bytes,
-                                             RowOff off, __amdgpu_buffer_rsrc_t r) {
-  constexpr int N_INSTR = ROWS / KRPI / NW;  // 1 KB instructions (KRPI rows) per wave
+                                             RowOff off, __amdgpu_buffer_rsrc_t r, int qbase,
+                                             int q0, int q1) {
+  constexpr int N_INSTR = kmajor_instrs<ROWS>();  // 1 KB instructions (KRPI rows) per wave
   static_assert(N_INSTR * NW * KRPI == ROWS, "the waves' instructions must cover all rows");
 #pragma unroll
   for (int i = 0; i < N_INSTR; ++i) {
+    if (qbase + i < q0 || qbase + i >= q1) continue;
     const int j = wave + NW * i;
     const int row = KRPI * j + lane / KCH;
     const int c = (lane % KCH) ^ swz_k(row);
@@ -125,14 +137,18 @@ __device__ __forceinline__ void issue_kmajor(char* tile, int wave, int lane, uin
 // Row-contiguous tile of BK k-rows x C columns (C = 128 or 256): instruction j
 // fills k-rows j*KPI .. j*KPI + KPI - 1 (KPI = 512 / C).  Element (k, col) of
 // the tile comes from byte koff(k) + (col0 + col) * 2 of the operand.
+template <int C>
+constexpr int mnmajor_instrs() { return BK / (512 / C) / NW; }
+
 template <int C, typename KOff>
 __device__ __forceinline__ void issue_mnmajor(char* tile, int wave, int lane, int col0, KOff koff,
-                                              __amdgpu_buffer_rsrc_t r) {
+                                              __amdgpu_buffer_rsrc_t r, int qbase, int q0, int q1) {
   constexpr int KPI = 512 / C, LPR = C / 8;  // k-rows per instruction, lanes per k-row
-  constexpr int N_INSTR = BK / KPI / NW;       // 1 KB instructions per wave
+  constexpr int N_INSTR = mnmajor_instrs<C>();  // 1 KB instructions per wave
   static_assert(N_INSTR * NW * KPI == BK, "the waves' instructions must cover all BK k-rows");
 #pragma unroll
   for (int i = 0; i < N_INSTR; ++i) {
+    if (qbase + i < q0 || qbase + i >= q1) continue;
     const int j = wave + NW * i;
     const int k = j * KPI + lane / LPR;
     const int c = (lane % LPR) ^ swz_mn(k);
@@ -190,7 +206,9 @@ __device__ __forceinline__ f16x8 frag_to_f16(f16x8 v) {
 template <int MODE>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void grouped_gemm_kernel(
     GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) char lds[NS][STAGE_BYTES];
+  // NS stages, then (with L2 prefetch) 256 bytes per wave that the prefetch
+  // DMA writes and nothing reads
+  __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE_BYTES + (PREFETCH ? NW * 256 : 0)];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
@@ -281,28 +299,35 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     rB2 = make_rsrc((p.B_lo ? p.B_lo : p.B0) + kbase * p.ldb, bbytes);
   }
 
-  auto issue = [&](int kt) {
-    char* sa = lds[kt % NS];
+  // Loads of stage kt, pieces [q0, q1) of LOADS_PER_STAGE (A first, then B).
+  constexpr int QA = kRowGrouped ? kmajor_instrs<BM>() : mnmajor_instrs<BM>();
+  auto issue = [&](int kt, int q0, int q1) __attribute__((always_inline)) {
+    char* sa = lds + (kt % NS) * STAGE_BYTES;
     char* sb = sa + A_BYTES;
     if constexpr (kRowGrouped) {
       const uint32_t k0b = (uint32_t)kt * BK * 2u;
-      issue_kmajor<BM>(sa, wave, lane, k0b, [&](int row) { return (uint32_t)row * lda2; }, rA);
+      issue_kmajor<BM>(sa, wave, lane, k0b, [&](int row) { return (uint32_t)row * lda2; }, rA, 0, q0,
+                       q1);
       if constexpr (kGateUp) {
-        // B rows 0..127: gate rows, 128..255: the matching up rows
-        issue_kmajor<BN / 2>(sb, wave, lane, k0b, [&](int row) { return (uint32_t)row * ldb2; }, rB);
+        // B rows 0..BN/2-1: gate rows, BN/2..BN-1: the matching up rows
+        constexpr int QG = kmajor_instrs<BN / 2>();
+        issue_kmajor<BN / 2>(sb, wave, lane, k0b, [&](int row) { return (uint32_t)row * ldb2; }, rB,
+                             QA, q0, q1);
         issue_kmajor<BN / 2>(sb + (BN / 2) * BK * 2, wave, lane, k0b,
-                             [&](int row) { return (uint32_t)row * ldb2; }, rB2);
+                             [&](int row) { return (uint32_t)row * ldb2; }, rB2, QA + QG, q0, q1);
       } else if constexpr (MODE == kDown) {
-        issue_kmajor<BN>(sb, wave, lane, k0b, [&](int row) { return (uint32_t)row * ldb2; }, rB);
+        issue_kmajor<BN>(sb, wave, lane, k0b, [&](int row) { return (uint32_t)row * ldb2; }, rB, QA,
+                         q0, q1);
       } else if constexpr (MODE == kDA) {
         const int k0 = kt * BK;
-        issue_mnmajor<BN>(sb, wave, lane, n0, [&](int k) { return (uint32_t)(k0 + k) * ldb2; }, rB);
+        issue_mnmajor<BN>(sb, wave, lane, n0, [&](int k) { return (uint32_t)(k0 + k) * ldb2; }, rB,
+                          QA, q0, q1);
       } else {  // kDXs: k < I from Wg, k >= I from Wu
         const int half = p.K / 2, k0 = kt * BK;
         const bool up = k0 >= half;
         const int kr = up ? k0 - half : k0;
         issue_mnmajor<BN>(sb, wave, lane, n0, [&](int k) { return (uint32_t)(kr + k) * ldb2; },
-                          up ? rB2 : rB);
+                          up ? rB2 : rB, QA, q0, q1);
       }
     } else {
       // stages [0, nk_pass): hi (or unsplit) operands; [nk_pass, 2 nk_pass): the
@@ -310,10 +335,70 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       const bool lo_pass = kt >= nk_pass;
       const int k0 = (lo_pass ? kt - nk_pass : kt) * BK;
       issue_mnmajor<BM>(sa, wave, lane, m0, [&](int k) { return (uint32_t)(k0 + k) * lda2; },
-                        lo_pass ? rA2 : rA);
+                        lo_pass ? rA2 : rA, 0, q0, q1);
       issue_mnmajor<BN>(sb, wave, lane, n0, [&](int k) { return (uint32_t)(k0 + k) * ldb2; },
-                        lo_pass ? rB2 : rB);
+                        lo_pass ? rB2 : rB, QA, q0, q1);
     }
+  };
+
+  // L2 prefetch of stage kt: wave w touches 4 bytes of each of 64 distinct
+  // 128-byte lines of the stage (waves 0 .. NW/2-1 the A lines, the rest the
+  // B lines), so the stage's direct-to-LDS loads, issued PREFETCH stages
+  // later, find their lines in L2.  Stages past the end re-touch stage nk - 1.
+  // (Capture-free, every operand by value: selecting among captured resources
+  // would make the optimiser load them through the closure at a computed
+  // offset, forcing the resources out of scalar registers.)
+  auto touch_stage = [](int kt, int nk_, int nk_pass_, char* dst, int wave_, int lane_,
+                        __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t ra2,
+                        __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rb2, uint32_t lda2_,
+                        uint32_t ldb2_, int m0_, int n0_, int K_) __attribute__((always_inline)) {
+    kt = min(kt, nk_ - 1);
+    const int h = NW / 2;  // waves per operand
+    const bool opa = wave_ < h;
+    const int L = (opa ? wave_ : wave_ - h) * 64 + lane_;  // line within the operand
+    __amdgpu_buffer_rsrc_t r;
+    uint32_t off;
+    if constexpr (kRowGrouped) {
+      const uint32_t k0b = (uint32_t)kt * BK * 2u;
+      if (opa) {
+        r = ra;
+        off = (uint32_t)L * lda2_ + k0b;
+      } else if constexpr (kGateUp) {
+        const bool up = (wave_ - h) * 64 >= BN / 2;  // wave-uniform
+        r = up ? rb2 : rb;
+        off = (uint32_t)(up ? L - BN / 2 : L) * ldb2_ + k0b;
+      } else if constexpr (MODE == kDown) {
+        r = rb;
+        off = (uint32_t)L * ldb2_ + k0b;
+      } else {  // kDA / kDXs: B is [k][n], BN/64 lines per k-row
+        constexpr int LPK = BN / 64;
+        int k0 = kt * BK;
+        r = rb;
+        if constexpr (MODE == kDXs) {
+          if (k0 >= K_ / 2) {
+            k0 -= K_ / 2;
+            r = rb2;
+          }
+        }
+        off = (uint32_t)(k0 + L / LPK) * ldb2_ + (uint32_t)(n0_ + (L % LPK) * 64) * 2u;
+      }
+    } else {
+      const bool lo_pass = kt >= nk_pass_;
+      const int k0 = (lo_pass ? kt - nk_pass_ : kt) * BK;
+      constexpr int LPA = BM / 64, LPB = BN / 64;
+      if (opa) {
+        r = lo_pass ? ra2 : ra;
+        off = (uint32_t)(k0 + L / LPA) * lda2_ + (uint32_t)(m0_ + (L % LPA) * 64) * 2u;
+      } else {
+        r = lo_pass ? rb2 : rb;
+        off = (uint32_t)(k0 + L / LPB) * ldb2_ + (uint32_t)(n0_ + (L % LPB) * 64) * 2u;
+      }
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, dst), 4, off, 0, 0, 0);
+  };
+  char* const touch_dst = lds + NS * STAGE_BYTES + wave * 256;
+  auto touch = [&](int kt) __attribute__((always_inline)) {
+    touch_stage(kt, nk, nk_pass, touch_dst, wave, lane, rA, rA2, rB, rB2, lda2, ldb2, m0, n0, p.K);
   };
 
   f32x4 acc[FM][FN];
@@ -323,56 +408,99 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---------------------------------------------------------------- main loop
+  // The next stage's loads are spread over this stage's MFMAs: the FM * BK/32
+  // rows of MFMAs are slots, and every LOAD_STRIDE-th slot (the first
+  // LOAD_SLOTS of them) issues LOADS_PER_SLOT loads before its MFMAs, so no
+  // wave holds its MFMAs back behind a burst of memory instructions.
+  constexpr int SLOTS = FM * (BK / 32);
+  constexpr int LOAD_SLOTS = MOE_GEMM_LOAD_SLOTS, LOAD_STRIDE = MOE_GEMM_LOAD_STRIDE;
+  constexpr int LOADS_PER_SLOT = LOADS_PER_STAGE / LOAD_SLOTS;
+  static_assert(LOADS_PER_SLOT * LOAD_SLOTS == LOADS_PER_STAGE &&
+                    (LOAD_SLOTS - 1) * LOAD_STRIDE + (PREFETCH > 0 ? 1 : 0) < SLOTS,
+                "load slots must split the stage's loads evenly and fit the MFMA rows");
+  if constexpr (PREFETCH > 0) {
+    if (nk > 0) {
+#pragma unroll
+      for (int s = 1; s <= PREFETCH; ++s) touch(s);
+    }
+  }
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
+    if (s < nk) issue(s, 0, LOADS_PER_STAGE);
+  // One stage: wait for it, then MFMAs over it with the loads of stage
+  // kt + NS - 1 interleaved (kMore: that stage exists).
+  auto stage = [&](int kt, auto more_tag) __attribute__((always_inline)) {
+    constexpr bool kMore = decltype(more_tag)::value;
     // stage kt has landed once only the stages issued after it (at most NS - 2)
     // are still in flight
-    wait_stage<NS - 2>(nk - 1 - kt);
+    if constexpr (PREFETCH > 0) {
+      // only the prefetch issued last (after stage kt's loads) may be in flight
+      if (kt == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    } else {
+      wait_stage<NS - 2>(nk - 1 - kt);
+    }
     __builtin_amdgcn_s_barrier();  // every wave's part of stage kt is in LDS, and
     asm volatile("" ::: "memory");  // every wave is done reading stage kt - 1
-    if (kt + NS - 1 < nk) issue(kt + NS - 1);
-    const char* sa = lds[kt % NS];
+    const char* sa = lds + (kt % NS) * STAGE_BYTES;
     const char* sb = sa + A_BYTES;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 32) {
-    frag_t af[FM], bfr[FN];
+      frag_t af[FM], bfr[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if constexpr (kRowGrouped) af[i] = read_kmajor<frag_t>(sa, wm * WTM + i * 16, kk, lane);
-      else af[i] = read_mnmajor<BM, frag_t>(sa, wm * WTM + i * 16, kk, lane);
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      if constexpr (kGateUp) {
-        const int r = j < FN / 2 ? wn * (WTN / 2) + j * 16 : BN / 2 + wn * (WTN / 2) + (j - FN / 2) * 16;
-        bfr[j] = read_kmajor<frag_t>(sb, r, kk, lane);
-      } else if constexpr (kBmn) {
-        bfr[j] = read_mnmajor<BN, frag_t>(sb, wn * WTN + j * 16, kk, lane);
-      } else {
-        bfr[j] = read_kmajor<frag_t>(sb, wn * WTN + j * 16, kk, lane);
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (kRowGrouped) af[i] = read_kmajor<frag_t>(sa, wm * WTM + i * 16, kk, lane);
+        else af[i] = read_mnmajor<BM, frag_t>(sa, wm * WTM + i * 16, kk, lane);
       }
-    }
-    if constexpr (kF16) {
-      if (p.cvt_a)
-#pragma unroll
-        for (int i = 0; i < FM; ++i) af[i] = frag_to_f16(af[i]);
-      if (p.cvt_b)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) bfr[j] = frag_to_f16(bfr[j]);
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        if constexpr (kF16)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+        if constexpr (kGateUp) {
+          const int r = j < FN / 2 ? wn * (WTN / 2) + j * 16 : BN / 2 + wn * (WTN / 2) + (j - FN / 2) * 16;
+          bfr[j] = read_kmajor<frag_t>(sb, r, kk, lane);
+        } else if constexpr (kBmn) {
+          bfr[j] = read_mnmajor<BN, frag_t>(sb, wn * WTN + j * 16, kk, lane);
+        } else {
+          bfr[j] = read_kmajor<frag_t>(sb, wn * WTN + j * 16, kk, lane);
+        }
+      }
+      if constexpr (kF16) {
+        if (p.cvt_a)
+#pragma unroll
+          for (int i = 0; i < FM; ++i) af[i] = frag_to_f16(af[i]);
+        if (p.cvt_b)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) bfr[j] = frag_to_f16(bfr[j]);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int slot = (kk / 32) * FM + i;
+        const int t = slot / LOAD_STRIDE;
+        const bool loads_here = kMore && slot % LOAD_STRIDE == 0 && t < LOAD_SLOTS;
+        if (loads_here) issue(kt + NS - 1, t * LOADS_PER_SLOT, (t + 1) * LOADS_PER_SLOT);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if constexpr (kF16)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+        }
+        // keep the order: this slot's loads, then its row of MFMAs
+        if (loads_here) __builtin_amdgcn_sched_group_barrier(0x020, LOADS_PER_SLOT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);
+        if constexpr (PREFETCH > 0) {
+          if (kMore && slot == (LOAD_SLOTS - 1) * LOAD_STRIDE + 1) {
+            touch(kt + NS - 1 + PREFETCH);  // the stage's last memory instruction
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
+        }
       }
     }
-  }
+  };
+  int kt = 0;
+  for (; kt + NS - 1 < nk; ++kt) stage(kt, std::true_type{});
+  for (; kt < nk; ++kt) stage(kt, std::false_type{});
+  // no prefetch DMA may still be writing this workgroup's LDS when it ends
+  if constexpr (PREFETCH > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---------------------------------------------------------------- epilogue
   // Lane holds, for fragment (i, j), row wm*64 + i*16 + (lane % 16) and the 4

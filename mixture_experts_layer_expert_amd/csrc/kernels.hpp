@@ -69,6 +69,16 @@ constexpr int kGemmBN = MOE_GEMM_BN;  // columns of a tile (gate/up: BN/2 gate +
 #ifndef MOE_GEMM_BK
 #define MOE_GEMM_BK 64
 #endif
+#ifndef MOE_GEMM_LOAD_SLOTS
+#define MOE_GEMM_LOAD_SLOTS 8
+#endif
+#ifndef MOE_GEMM_LOAD_STRIDE
+#define MOE_GEMM_LOAD_STRIDE 1
+#endif
+#ifndef MOE_GEMM_PREFETCH
+#define MOE_GEMM_PREFETCH 1
+#endif
+constexpr int kGemmPrefetch = MOE_GEMM_PREFETCH;  // L2 prefetch distance in stages
 constexpr int kGemmBK = MOE_GEMM_BK;  // reduction depth of one LDS stage (32 or 64)
 constexpr int kGemmWM = MOE_GEMM_WM;  // waves along the rows
 constexpr int kGemmWN = MOE_GEMM_WN;  // waves along the columns
