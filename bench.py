@@ -119,7 +119,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_30b_a3b", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-tokens", type=int, default=384,
+    ap.add_argument("--cpu-tokens", type=int, default=640,
                     help="tokens in the CPU-oracle baseline sample (0: skip)")
     ap.add_argument("--fwd-bwd-only", action="store_true",
                     help="time only the full steps (skip the separate fwd/bwd timing)")
