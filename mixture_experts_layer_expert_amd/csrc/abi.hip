@@ -328,8 +328,9 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
     g.N = d.D;
     g.K = 2 * d.I;
     g.n_tiles = (d.D + kGemmBN - 1) / kGemmBN;
-    g.Cf = w.dxs;
+    g.Cf = w.dxs;  // rows in flat slot order (t*K + k)
     g.ldc = d.D;
+    g.s2f = sorted_to_flat;
     g.cvt_a = 0;  // dG | dU already fp16
     g.cvt_b = 1;  // weights bf16 -> fp16
     MOE_TRY(launch_gemm(kDXs, g, rowgrouped_grid(d, g.n_tiles), st));
@@ -370,7 +371,7 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   MOE_TRY(launch_gemm(kDW, g, dw_grid(2, d.E, d.I, d.D), st));
 
   if (R > 0) {
-    MOE_TRY(launch_reduce_rows(w.dxs, flat_to_sorted, dx, d.T, d.K, d.D, st));
+    MOE_TRY(launch_reduce_rows(w.dxs, dx, d.T, d.K, d.D, st));
     MOE_TRY(launch_reduce_partials(w.part, flat_to_sorted, d_topk_w, (int)R,
                                    partials_per_row(d), st));
   }

@@ -203,6 +203,45 @@ __device__ __forceinline__ f16x8 frag_to_f16(f16x8 v) {
   return __builtin_bit_cast(f16x8, u);
 }
 
+// Epilogue staging.  A lane's accumulators hold 4 consecutive columns of 16
+// different rows per fragment, so storing them directly writes 8- or 16-byte
+// pieces of 16 rows per instruction.  Instead each wave stages a strip of 16
+// rows x C columns (ES-byte elements) in its own LDS area (the stage buffers
+// are free once the main loop is done) and writes it back as whole row
+// segments, 16 bytes per lane.  Rows are padded by 16 bytes (16-byte aligned,
+// spread over the banks).
+template <int C, int ES>
+struct Strip {
+  static constexpr int ELEM = ES;
+  static constexpr int ROWB = C * ES;   // bytes of one staged row
+  static constexpr int SP = ROWB + 16;  // row pitch
+  static constexpr int BYTES = 16 * SP;
+  static constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;   // rows per wave-wide copy instruction
+  static_assert(ROWB % 16 == 0 && 64 % CPR == 0 && 16 % RPI == 0, "strip layout");
+};
+
+// The lane's 4 values of strip row `row` from strip column `col` on.
+template <class S, class V>
+__device__ __forceinline__ void strip_put(char* stg, int row, int col, V v) {
+  static_assert(sizeof(V) == 4 * S::ELEM, "4 elements per lane");
+  *(V*)(stg + row * S::SP + col * S::ELEM) = v;
+}
+
+// Copies the staged strip out: strip row r (< nrows) goes to the byte address
+// row_ptr(r) of its column 0; chunks past ncols columns are skipped.  op(dst,
+// v) stores (or accumulates) one 16-byte chunk.
+template <class S, class RowPtr, class Op>
+__device__ __forceinline__ void strip_out(const char* stg, int lane, int nrows, int ncols,
+                                          RowPtr row_ptr, Op op) {
+#pragma unroll
+  for (int h = 0; h < 16 / S::RPI; ++h) {
+    const int r = h * S::RPI + lane / S::CPR, ch = lane % S::CPR;
+    const u32x4 v = *(const u32x4*)(stg + r * S::SP + ch * 16);
+    if (r < nrows && ch * (16 / S::ELEM) < ncols) op(row_ptr(r) + ch * 16, v);
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void grouped_gemm_kernel(
     GemmArgs p) {
@@ -503,48 +542,75 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   if constexpr (PREFETCH > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---------------------------------------------------------------- epilogue
-  // Lane holds, for fragment (i, j), row wm*64 + i*16 + (lane % 16) and the 4
-  // consecutive columns of B fragment j starting at 4 * (lane / 16).
+  // Lane holds, for fragment (i, j), row wm*WTM + i*16 + (lane % 16) and the 4
+  // consecutive columns of B fragment j starting at 4 * (lane / 16).  Results
+  // leave through per-wave LDS strips (see Strip).
   const int frow = lane & 15;
   const int cq = 4 * (lane >> 4);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();  // every wave is done reading the stage buffers
+  asm volatile("" ::: "memory");
+  auto store16 = [](char* dst, u32x4 v) { *(u32x4*)dst = v; };
   if constexpr (MODE == kGateUpH || MODE == kGateUpGU) {
+    // the wave's WTN/2 gate columns and the matching up columns
+    constexpr int CW = WTN / 2;
+    using S = Strip<CW, MODE == kGateUpH ? 2 : 4>;
+    static_assert(NW * 2 * S::BYTES <= NS * STAGE_BYTES, "staging fits the stage buffers");
+    char* const stg = lds + wave * 2 * S::BYTES;
+    const int col0 = n0 + wn * CW;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int r = wm * WTM + i * 16 + frow;
-      if (r >= rows_valid) continue;
-      const size_t m = (size_t)(m0 + r);
+      const int rb = wm * WTM + i * 16;  // strip's first row within the tile
 #pragma unroll
       for (int j = 0; j < FN / 2; ++j) {
-        const int col = n0 + wn * (WTN / 2) + j * 16 + cq;
-        if (col >= p.N) continue;
+        const int cl = j * 16 + cq;
         const f32x4 g = acc[i][j], u = acc[i][j + FN / 2];
         if constexpr (MODE == kGateUpH) {
           float h[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) h[q] = g[q] * sigmoidf_(g[q]) * u[q];
-          *(u32x2*)(p.C0 + m * p.ldc + col) = u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+          strip_put<S>(stg, frow, cl, u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])});
         } else {
           // recomputed gate/up pre-activations stay fp32 for the SwiGLU backward
-          *(f32x4*)(p.Cf + m * p.ldc + col) = g;
-          *(f32x4*)(p.Cf2 + m * p.ldc + col) = u;
+          strip_put<S>(stg, frow, cl, g);
+          strip_put<S>(stg + S::BYTES, frow, cl, u);
         }
+      }
+      const int nrows = rows_valid - rb, ncols = p.N - col0;
+      if constexpr (MODE == kGateUpH) {
+        strip_out<S>(stg, lane, nrows, ncols, [&](int r) {
+          return (char*)(p.C0 + (size_t)(m0 + rb + r) * p.ldc + col0); }, store16);
+      } else {
+        strip_out<S>(stg, lane, nrows, ncols, [&](int r) {
+          return (char*)(p.Cf + (size_t)(m0 + rb + r) * p.ldc + col0); }, store16);
+        strip_out<S>(stg + S::BYTES, lane, nrows, ncols, [&](int r) {
+          return (char*)(p.Cf2 + (size_t)(m0 + rb + r) * p.ldc + col0); }, store16);
       }
     }
   } else if constexpr (MODE == kDown || MODE == kDXs) {
+    using S = Strip<WTN, MODE == kDown ? 2 : 4>;
+    static_assert(NW * S::BYTES <= NS * STAGE_BYTES, "staging fits the stage buffers");
+    char* const stg = lds + wave * S::BYTES;
+    const int col0 = n0 + wn * WTN;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int r = wm * WTM + i * 16 + frow;
-      if (r >= rows_valid) continue;
-      const size_t m = (size_t)(m0 + r);
+      const int rb = wm * WTM + i * 16;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * WTN + j * 16 + cq;
-        if (col >= p.N) continue;
+        const int cl = j * 16 + cq;
         const f32x4 v = acc[i][j];
-        if constexpr (MODE == kDXs)  // fp32 rows: the K copies of a token are summed later
-          *(f32x4*)(p.Cf + m * p.ldc + col) = v;
-        else
-          *(u32x2*)(p.C0 + m * p.ldc + col) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        if constexpr (MODE == kDXs) strip_put<S>(stg, frow, cl, v);
+        else strip_put<S>(stg, frow, cl, u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+      }
+      const int nrows = rows_valid - rb, ncols = p.N - col0;
+      if constexpr (MODE == kDXs) {
+        // fp32 rows at their flat slot t*K + k: the K copies of a token sit
+        // together for the reduction
+        strip_out<S>(stg, lane, nrows, ncols, [&](int r) {
+          return (char*)(p.Cf + (size_t)p.s2f[m0 + rb + r] * p.ldc + col0); }, store16);
+      } else {
+        strip_out<S>(stg, lane, nrows, ncols, [&](int r) {
+          return (char*)(p.C0 + (size_t)(m0 + rb + r) * p.ldc + col0); }, store16);
       }
     }
   } else if constexpr (MODE == kDA) {
@@ -552,7 +618,21 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     // weight of the row:  h = silu(g) u;  partial dRW = sum dA h over the
     // wave's WTN columns;  dH = w dA;  dG = dH u silu'(g);  dU = dH silu(g);
     // Hw = w h (the weighted activations that dW_down needs).
+    //
+    // The six fp16 outputs (dG, dU, Hw, each as hi = round(v) and lo =
+    // round(v - hi)) leave through LDS: each wave stages one 16-row strip of
+    // all six in its own area (the stage buffers are free now) and writes
+    // them back as whole 128-byte row segments, 16 bytes per lane, instead of
+    // 8-byte pieces of 16 rows per store.
     const int I = p.N;
+    constexpr int SP = WTN * 2 + 16;   // staged row pitch (bytes; padded, 16-byte aligned)
+    constexpr int OB = 16 * SP;        // one output's staged strip
+    constexpr int CPR = WTN * 2 / 16;  // 16-byte chunks per staged row
+    static_assert(NW * 6 * OB <= NS * STAGE_BYTES && 64 % CPR == 0, "epilogue staging layout");
+    char* const stg = lds + wave * 6 * OB;
+    bf16_t* const outs[6] = {p.C0, p.C1, p.C2, p.L0, p.L1, p.L2};
+    const size_t ldo[6] = {(size_t)p.ldc, (size_t)p.ldc, (size_t)I,
+                            (size_t)p.ldc, (size_t)p.ldc, (size_t)I};
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = wm * WTM + i * 16 + frow;
@@ -562,12 +642,15 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       float dot = 0.0f;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * WTN + j * 16 + cq;
-        if (!row_ok || col >= I) continue;
-        const f32x4 gv = *(const f32x4*)(p.GU + m * (2 * (size_t)I) + col);
-        const f32x4 uv = *(const f32x4*)(p.GU + m * (2 * (size_t)I) + I + col);
+        const int cl = j * 16 + cq;  // column within the wave's WTN
+        const int col = n0 + wn * WTN + cl;
+        const bool ok = row_ok && col < I;
+        f32x4 gv = {0.f, 0.f, 0.f, 0.f}, uv = {0.f, 0.f, 0.f, 0.f};
+        if (ok) {
+          gv = *(const f32x4*)(p.GU + m * (2 * (size_t)I) + col);
+          uv = *(const f32x4*)(p.GU + m * (2 * (size_t)I) + I + col);
+        }
         float dg[4], du[4], hw[4];
-        uint32_t lo_dg[2], lo_du[2], lo_hw[2];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float g = gv[q];
@@ -575,7 +658,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
           const float da = acc[i][j][q];
           const float sg = sigmoidf_(g);
           const float h = g * sg * u;
-          dot += da * h;
+          if (ok) dot += da * h;
           const float dh = wr * da;
           dg[q] = dh * u * sg * (1.0f + g * (1.0f - sg));
           du[q] = dh * g * sg;
@@ -586,38 +669,57 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
         const u32x2 hi_dg = {pack_f16x2(dg[0], dg[1]), pack_f16x2(dg[2], dg[3])};
         const u32x2 hi_du = {pack_f16x2(du[0], du[1]), pack_f16x2(du[2], du[3])};
         const u32x2 hi_hw = {pack_f16x2(hw[0], hw[1]), pack_f16x2(hw[2], hw[3])};
+        u32x2 lo_dg, lo_du, lo_hw;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           lo_dg[h2] = f16x2_residual(dg[2 * h2], dg[2 * h2 + 1], hi_dg[h2]);
           lo_du[h2] = f16x2_residual(du[2 * h2], du[2 * h2 + 1], hi_du[h2]);
           lo_hw[h2] = f16x2_residual(hw[2 * h2], hw[2 * h2 + 1], hi_hw[h2]);
         }
-        *(u32x2*)(p.C0 + m * p.ldc + col) = hi_dg;
-        *(u32x2*)(p.C1 + m * p.ldc + col) = hi_du;
-        *(u32x2*)(p.C2 + m * (size_t)I + col) = hi_hw;
-        *(u32x2*)(p.L0 + m * p.ldc + col) = u32x2{lo_dg[0], lo_dg[1]};
-        *(u32x2*)(p.L1 + m * p.ldc + col) = u32x2{lo_du[0], lo_du[1]};
-        *(u32x2*)(p.L2 + m * (size_t)I + col) = u32x2{lo_hw[0], lo_hw[1]};
+        char* const sp = stg + frow * SP + cl * 2;
+        *(u32x2*)(sp + 0 * OB) = hi_dg;
+        *(u32x2*)(sp + 1 * OB) = hi_du;
+        *(u32x2*)(sp + 2 * OB) = hi_hw;
+        *(u32x2*)(sp + 3 * OB) = lo_dg;
+        *(u32x2*)(sp + 4 * OB) = lo_du;
+        *(u32x2*)(sp + 5 * OB) = lo_hw;
+      }
+      // this wave's strip is staged (a wave's LDS accesses complete in order):
+      // write it back as row segments, CPR lanes per row
+#pragma unroll
+      for (int o = 0; o < 6; ++o) {
+#pragma unroll
+        for (int h = 0; h < 16 * CPR / 64; ++h) {
+          const int srow = h * (64 / CPR) + lane / CPR, ch = lane % CPR;
+          const u32x4 v = *(const u32x4*)(stg + o * OB + srow * SP + ch * 16);
+          const int rr = wm * WTM + i * 16 + srow;
+          const int cg = n0 + wn * WTN + ch * 8;
+          if (rr < rows_valid && cg < I) *(u32x4*)(outs[o] + (size_t)(m0 + rr) * ldo[o] + cg) = v;
+        }
       }
       dot += __shfl_xor(dot, 16);
       dot += __shfl_xor(dot, 32);
       if (row_ok && lane < 16) p.part[m * p.np + nt_idx * WN + wn] = dot;
     }
   } else {  // kDW
-    float* out = (mat == 0 ? p.Cf : p.Cf2) + (size_t)e * p.M * p.N;
+    using S = Strip<WTN, 4>;
+    static_assert(NW * S::BYTES <= NS * STAGE_BYTES, "staging fits the stage buffers");
+    char* const stg = lds + wave * S::BYTES;
+    float* const out = (mat == 0 ? p.Cf : p.Cf2) + (size_t)e * p.M * p.N;
+    const int col0 = n0 + wn * WTN;
+    const bool accum = p.accumulate != 0;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int r = wm * WTM + i * 16 + frow;
-      if (r >= rows_valid) continue;
+      const int rb = wm * WTM + i * 16;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * WTN + j * 16 + cq;
-        if (col >= p.N) continue;
-        f32x4* dst = (f32x4*)(out + (size_t)(m0 + r) * p.N + col);
-        f32x4 v = acc[i][j];
-        if (p.accumulate) v += *dst;
-        *dst = v;
-      }
+      for (int j = 0; j < FN; ++j) strip_put<S>(stg, frow, j * 16 + cq, acc[i][j]);
+      strip_out<S>(stg, lane, rows_valid - rb, p.N - col0, [&](int r) {
+        return (char*)(out + (size_t)(m0 + rb + r) * p.N + col0); },
+        [&](char* dst, u32x4 v) {
+          f32x4 x = __builtin_bit_cast(f32x4, v);
+          if (accum) x += *(const f32x4*)dst;
+          *(f32x4*)dst = x;
+        });
     }
   }
 }

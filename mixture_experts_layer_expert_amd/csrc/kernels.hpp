@@ -41,8 +41,7 @@ hipError_t launch_gather(const void* src0, const void* src1, void* dst0, void* d
                          const int32_t* s2f, int R, int K, int D, hipStream_t st);
 hipError_t launch_combine(const void* O, const float* w, const int32_t* f2s, void* y, int T,
                           int K, int D, hipStream_t st);
-hipError_t launch_reduce_rows(const void* dXs, const int32_t* f2s, void* dx, int T, int K, int D,
-                              hipStream_t st);
+hipError_t launch_reduce_rows(const void* dXs, void* dx, int T, int K, int D, hipStream_t st);
 hipError_t launch_reduce_partials(const float* part, const int32_t* f2s, float* out, int R,
                                   int np, hipStream_t st);
 
@@ -90,7 +89,7 @@ enum GemmMode : int {
   kDown = 2,      // O  = H Wd^T                                         bf16 [R, D]
   kDA = 3,        // dA = dOu Wd; SwiGLU backward (dG, dU, Hw in fp16) and router-weight
                   // partials in the epilogue
-  kDXs = 4,       // dXs = dG Wg + dU Wu                                  fp32 [R, D]
+  kDXs = 4,       // dXs = dG Wg + dU Wu            fp32 [R, D], row f = flat slot of the routed row
   kDW = 5,        // dW[e] = A_e^T B_e over the expert's rows              fp32
 };
 

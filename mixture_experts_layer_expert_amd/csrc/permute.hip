@@ -15,9 +15,12 @@ namespace moe {
 
 constexpr int kPermuteThreads = 256;
 
+#ifndef MOE_PERMUTE_GRID_CAP
+#define MOE_PERMUTE_GRID_CAP (256 * 64)
+#endif
 static inline int grid_for(size_t work) {
   size_t b = (work + kPermuteThreads - 1) / kPermuteThreads;
-  const size_t cap = 256 * 64;  // enough resident waves to saturate HBM; rest loop
+  const size_t cap = MOE_PERMUTE_GRID_CAP;  // enough resident waves to saturate HBM; rest loop
   return (int)(b < 1 ? 1 : (b > cap ? cap : b));
 }
 
@@ -37,23 +40,41 @@ __global__ __launch_bounds__(kPermuteThreads) void gather_rows_kernel(
 }
 
 // y[t, :] = sum_{k<K} w[t,k] * O[flat_to_sorted[t*K+k], :]   (fp32, k ascending)
+// KT = K known at compile time (0: runtime K): all K row indices are read
+// first and all K row loads are then in flight together.
+template <int KT>
 __global__ __launch_bounds__(kPermuteThreads) void combine_kernel(
     const u32x4* __restrict__ O, const float* __restrict__ w, const int32_t* __restrict__ f2s,
-    u32x4* __restrict__ y, int T, int K, int cpr) {
+    u32x4* __restrict__ y, int T, int K_, int cpr) {
+  const int K = KT > 0 ? KT : K_;
   const size_t total = (size_t)T * cpr;
   for (size_t c = (size_t)blockIdx.x * kPermuteThreads + threadIdx.x; c < total;
        c += (size_t)gridDim.x * kPermuteThreads) {
     const size_t t = c / cpr;
     const int j = (int)(c - t * cpr);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int k = 0; k < K; ++k) {
-      const float wk = w[t * K + k];
-      const u32x4 v = O[(size_t)f2s[t * K + k] * cpr + j];
+    auto add = [&](float wk, u32x4 v) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         acc[2 * q] += wk * bf16_lo(v[q]);
         acc[2 * q + 1] += wk * bf16_hi(v[q]);
       }
+    };
+    if constexpr (KT > 0) {
+      int rows[KT];
+      float wk[KT];
+      u32x4 v[KT];
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
+        rows[k] = f2s[t * KT + k];
+        wk[k] = w[t * KT + k];
+      }
+#pragma unroll
+      for (int k = 0; k < KT; ++k) v[k] = O[(size_t)rows[k] * cpr + j];
+#pragma unroll
+      for (int k = 0; k < KT; ++k) add(wk[k], v[k]);
+    } else {
+      for (int k = 0; k < K; ++k) add(w[t * K + k], O[(size_t)f2s[t * K + k] * cpr + j]);
     }
     u32x4 out;
 #pragma unroll
@@ -62,24 +83,31 @@ __global__ __launch_bounds__(kPermuteThreads) void combine_kernel(
   }
 }
 
-// dX[t, :] = sum_{k<K} dXs[flat_to_sorted[t*K+k], :]  (fp32 rows, fp32 sum, k ascending)
-// Each thread produces 8 outputs (two 16-byte fp32 reads per routed copy).
+// dX[t, :] = sum_{k<K} dXs[t*K + k, :]  (fp32 rows in flat slot order, fp32 sum,
+// k ascending).  The K rows of a token are contiguous, so the reads stream.
+// Each thread produces 4 outputs from one 16-byte read per routed copy; with
+// KT > 0 all K reads are in flight together.  cpr4 = D / 4.
+template <int KT>
 __global__ __launch_bounds__(kPermuteThreads) void reduce_rows_kernel(
-    const f32x4* __restrict__ dXs, const int32_t* __restrict__ f2s, u32x4* __restrict__ dx, int T,
-    int K, int cpr) {
-  const size_t total = (size_t)T * cpr;
+    const f32x4* __restrict__ dXs, u32x2* __restrict__ dx, int T, int K_, int cpr4) {
+  const int K = KT > 0 ? KT : K_;
+  const size_t total = (size_t)T * cpr4;
   for (size_t c = (size_t)blockIdx.x * kPermuteThreads + threadIdx.x; c < total;
        c += (size_t)gridDim.x * kPermuteThreads) {
-    const size_t t = c / cpr;
-    const int j = (int)(c - t * cpr);
-    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < K; ++k) {
-      const f32x4* row = dXs + (size_t)f2s[t * K + k] * (2 * cpr) + 2 * j;
-      a0 += row[0];
-      a1 += row[1];
+    const size_t t = c / cpr4;
+    const int j = (int)(c - t * cpr4);
+    const f32x4* rows = dXs + t * K * cpr4 + j;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (KT > 0) {
+      f32x4 v[KT];
+#pragma unroll
+      for (int k = 0; k < KT; ++k) v[k] = rows[(size_t)k * cpr4];
+#pragma unroll
+      for (int k = 0; k < KT; ++k) a += v[k];
+    } else {
+      for (int k = 0; k < K; ++k) a += rows[(size_t)k * cpr4];
     }
-    dx[c] = u32x4{pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]),
-                  pack_bf16x2(a1[0], a1[1]), pack_bf16x2(a1[2], a1[3])};
+    dx[c] = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
   }
 }
 
@@ -110,17 +138,36 @@ hipError_t launch_combine(const void* O, const float* w, const int32_t* f2s, voi
                           int K, int D, hipStream_t st) {
   const int cpr = D / 8;
   if (T == 0) return hipSuccess;
-  MOE_LAUNCH(kKCombine, combine_kernel, dim3(grid_for((size_t)T * cpr)), dim3(kPermuteThreads), 0,
-                     st, (const u32x4*)O, w, f2s, (u32x4*)y, T, K, cpr);
+  const dim3 grid(grid_for((size_t)T * cpr)), block(kPermuteThreads);
+#define MOE_COMBINE(KT)                                                                          \
+  MOE_LAUNCH(kKCombine, combine_kernel<KT>, grid, block, 0, st, (const u32x4*)O, w, f2s, (u32x4*)y, \
+             T, K, cpr)
+  switch (K) {
+    case 1: MOE_COMBINE(1); break;
+    case 2: MOE_COMBINE(2); break;
+    case 4: MOE_COMBINE(4); break;
+    case 8: MOE_COMBINE(8); break;
+    default: MOE_COMBINE(0); break;
+  }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_rows(const void* dXs, const int32_t* f2s, void* dx, int T, int K, int D,
-                              hipStream_t st) {
-  const int cpr = D / 8;
+hipError_t launch_reduce_rows(const void* dXs, void* dx, int T, int K, int D, hipStream_t st) {
+  const int cpr4 = D / 4;
   if (T == 0) return hipSuccess;
-  MOE_LAUNCH(kKReduceRows, reduce_rows_kernel, dim3(grid_for((size_t)T * cpr)), dim3(kPermuteThreads),
-                     0, st, (const f32x4*)dXs, f2s, (u32x4*)dx, T, K, cpr);
+  const dim3 grid(grid_for((size_t)T * cpr4)), block(kPermuteThreads);
+#define MOE_REDUCE(KT)                                                                     \
+  MOE_LAUNCH(kKReduceRows, reduce_rows_kernel<KT>, grid, block, 0, st, (const f32x4*)dXs, \
+             (u32x2*)dx, T, K, cpr4)
+  switch (K) {
+    case 1: MOE_REDUCE(1); break;
+    case 2: MOE_REDUCE(2); break;
+    case 4: MOE_REDUCE(4); break;
+    case 8: MOE_REDUCE(8); break;
+    default: MOE_REDUCE(0); break;
+  }
+#undef MOE_REDUCE
   return hipGetLastError();
 }
 
