@@ -466,6 +466,9 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk) issue(s, 0, LOADS_PER_STAGE);
+  // Waves whose rows all lie past a ragged expert's end (row-grouped tiles)
+  // skip the fragment reads and MFMAs; wave-uniform.
+  const bool wave_rows = !kRowGrouped || wm * WTM < rows_valid;
   // One stage: wait for it, then MFMAs over it with the loads of stage
   // kt + NS - 1 interleaved (kMore: that stage exists).
   auto stage = [&](int kt, auto more_tag) __attribute__((always_inline)) {
@@ -481,6 +484,15 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     }
     __builtin_amdgcn_s_barrier();  // every wave's part of stage kt is in LDS, and
     asm volatile("" ::: "memory");  // every wave is done reading stage kt - 1
+    if (!wave_rows) {
+      // all of this wave's rows are padding: it only moves its share of the
+      // next stage (and the prefetch)
+      if constexpr (kMore) {
+        issue(kt + NS - 1, 0, LOADS_PER_STAGE);
+        if constexpr (PREFETCH > 0) touch(kt + NS - 1 + PREFETCH);
+      }
+      return;
+    }
     const char* sa = lds + (kt % NS) * STAGE_BYTES;
     const char* sb = sa + A_BYTES;
 #pragma unroll
