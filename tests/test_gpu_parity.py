@@ -65,10 +65,15 @@ def _full_compare(wl, data, backward=True):
 SMALL = {
     # the tiny workload itself
     "tiny": lambda: (synth.TINY, synth.generate(synth.TINY)),
-    # several 128-row tiles per expert with a ragged tail, I not a multiple of 128
-    "ragged_tiles": lambda: _custom(T=600, D=256, I=192, E=8, K=2, score=0, seed=101),
-    # D not a multiple of 128 (masked column tail in the down/dXs tiles), many experts
-    "ragged_cols": lambda: _custom(T=300, D=320, I=64, E=16, K=4, score=0, seed=102),
+    # several 256-row tiles per expert with a ragged last tile of 129..255 rows (the
+    # skewed case below has last tiles of <= 128 rows, whose second wave row is all
+    # padding), I not a multiple of 128 (partial gate/up column tile)
+    "ragged_tiles": lambda: _custom(T=1500, D=256, I=192, E=4, K=2, score=0, seed=101),
+    # D not a multiple of 256 (masked column tail in the down/dXs tiles), many experts,
+    # K = 3 (the combine and dX reduction without a compile-time K)
+    "ragged_cols": lambda: _custom(T=300, D=320, I=64, E=16, K=3, score=0, seed=102),
+    # many routed copies per token (K = 16 of 64 experts)
+    "k16": lambda: _custom(T=96, D=128, I=64, E=64, K=16, score=0, seed=108),
     # skewed routing: one hot expert, three experts never chosen
     "skew_empty": lambda: _custom(T=500, D=128, I=128, E=8, K=2, score=0, seed=103, hot=1,
                                   dead=(2, 5, 7)),
