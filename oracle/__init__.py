@@ -179,3 +179,32 @@ def dw_entries(L: Layer, idx, w, which, e, r, c):
                                      ctypes.c_int64(n), _p(which), _p(e), _p(r), _p(c),
                                      _p(out)), "dw_entries")
     return out
+
+
+def router_logits(x: np.ndarray, w_r: np.ndarray) -> np.ndarray:
+    """Router projection logits = x w_r  (x [T, D], w_r [D, E]) in float64."""
+    lib = _load()
+    x, w_r = _f64(x), _f64(w_r)
+    T, D = x.shape
+    D2, E = w_r.shape
+    assert D2 == D
+    out = np.empty((T, E), dtype=np.float64)
+    d = _Dims(T, D, 1, E, 1, 0)
+    _check(lib.moe_oracle_router_logits(ctypes.byref(d), _p(x), _p(w_r), _p(out)), "router_logits")
+    return out
+
+
+def router_backward(x: np.ndarray, w_r: np.ndarray, idx, w, drw, score: int):
+    """Router backward with the selection fixed -> (dl [T,E], dW_r [D,E], dX_router [T,D])."""
+    lib = _load()
+    x, w_r, idx, w, drw = _f64(x), _f64(w_r), _i32(idx), _f64(w), _f64(drw)
+    T, D = x.shape
+    E = w_r.shape[1]
+    K = idx.shape[1]
+    dl = np.empty((T, E), dtype=np.float64)
+    dw_r = np.empty((D, E), dtype=np.float64)
+    dx_r = np.empty((T, D), dtype=np.float64)
+    d = _Dims(T, D, 1, E, K, score)
+    _check(lib.moe_oracle_router_backward(ctypes.byref(d), _p(x), _p(w_r), _p(idx), _p(w),
+                                          _p(drw), _p(dl), _p(dw_r), _p(dx_r)), "router_backward")
+    return dl, dw_r, dx_r

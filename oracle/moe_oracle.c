@@ -36,6 +36,12 @@
  *   w_down           [E, D, I]  expert e maps I -> D
  *   idx              [T, K]   int32   selected experts, slot order = rank
  *   w                [T, K]   float64 router weights of the selected experts
+ *   w_r              [D, E]   router projection (logits = x w_r)
+ *
+ * The router projection and its backward (moe_oracle_router_*) extend the
+ * page's layer by its input side: the logits the routing selects on, and
+ * the gradient that flows back through the router weights into the logits,
+ * the projection weights and the layer input.
  */
 #include <math.h>
 #include <stddef.h>
@@ -461,4 +467,77 @@ int moe_oracle_dw_entries(const moe_oracle_dims *d, const double *x,
         free(rows);
     }
     return status;
+}
+
+/* ---------------------------------------------------------------------------
+ * Router projection:  logits[t, e] = sum_d x[t, d] * w_r[d, e]   (d ascending)
+ * x [T, D], w_r [D, E] -> logits [T, E].
+ * ------------------------------------------------------------------------- */
+int moe_oracle_router_logits(const moe_oracle_dims *d, const double *x,
+                             const double *w_r, double *logits) {
+    if (!dims_ok(d) || !x || !w_r || !logits) return ORACLE_BAD_ARG;
+    const int D = d->D, E = d->E;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < d->T; ++t) {
+        for (int e = 0; e < E; ++e) {
+            double s = 0.0;
+            for (int j = 0; j < D; ++j) s += x[t * D + j] * w_r[(size_t)j * E + e];
+            logits[t * E + e] = s;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Router backward, with the selection held fixed (the top-K choice is
+ * piecewise constant in the logits).  drw[t, k] = dL/dw[t, k] is the
+ * router-weight gradient of the layer.
+ *   score 0, w_k = exp(l_k) / sum_{j in selected} exp(l_j):
+ *     dw_k/dl_m = w_k (delta_km - w_m) for selected m, so
+ *     dl[t, idx_m] = w_m (drw_m - sum_k w_k drw_k);  0 for unselected experts
+ *   score 1, w_k = sigmoid(l_k):
+ *     dl[t, idx_k] = drw_k w_k (1 - w_k)
+ *   dw_r[d, e] = sum_t x[t, d] dl[t, e]        (t ascending)
+ *   dx_r[t, d] = sum_e dl[t, e] w_r[d, e]      (e ascending)
+ * dl [T, E], dw_r [D, E], dx_r [T, D]  (dx_r is the router's contribution to
+ * the layer's input gradient; the expert path adds its own).
+ * ------------------------------------------------------------------------- */
+int moe_oracle_router_backward(const moe_oracle_dims *d, const double *x,
+                               const double *w_r, const int32_t *idx,
+                               const double *w, const double *drw, double *dl,
+                               double *dw_r, double *dx_r) {
+    if (!dims_ok(d) || !x || !w_r || !idx || !w || !drw || !dl || !dw_r || !dx_r)
+        return ORACLE_BAD_ARG;
+    const int D = d->D, E = d->E, K = d->K;
+    const int64_t T = d->T;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        double *dlt = dl + t * E;
+        for (int e = 0; e < E; ++e) dlt[e] = 0.0;
+        const double *wt = w + t * K, *gt = drw + t * K;
+        if (d->score == 0) {
+            double s = 0.0;
+            for (int k = 0; k < K; ++k) s += wt[k] * gt[k];
+            for (int m = 0; m < K; ++m) dlt[idx[t * K + m]] = wt[m] * (gt[m] - s);
+        } else {
+            for (int k = 0; k < K; ++k) dlt[idx[t * K + k]] = gt[k] * wt[k] * (1.0 - wt[k]);
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int j = 0; j < D; ++j) {
+        for (int e = 0; e < E; ++e) {
+            double s = 0.0;
+            for (int64_t t = 0; t < T; ++t) s += x[t * D + j] * dl[t * E + e];
+            dw_r[(size_t)j * E + e] = s;
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int j = 0; j < D; ++j) {
+            double s = 0.0;
+            for (int e = 0; e < E; ++e) s += dl[t * E + e] * w_r[(size_t)j * E + e];
+            dx_r[t * D + j] = s;
+        }
+    }
+    return ORACLE_OK;
 }

@@ -319,6 +319,120 @@ def pin_backward_dw_token_subset():
         np.testing.assert_allclose(u, v, rtol=1e-13, atol=1e-15)
 
 
+# --------------------------------------------------------------------------- router side
+
+def pin_router_logits_library():
+    """The router projection equals a numpy matmul x @ W_r."""
+    r = _rng(41)
+    x = r.standard_normal((37, 24))
+    w_r = r.standard_normal((24, 9)) / math.sqrt(24)
+    np.testing.assert_allclose(oracle.router_logits(x, w_r), x @ w_r, rtol=1e-13, atol=1e-13)
+
+
+def _router_weights(l, idx, score):
+    """Router weights of the selected experts as a function of the logits (numpy)."""
+    ls = np.take_along_axis(l, idx.astype(np.int64), axis=1)
+    if score == synth.SOFTMAX_TOPK:
+        z = np.exp(ls - ls.max(axis=1, keepdims=True))
+        return z / z.sum(axis=1, keepdims=True)
+    return 1.0 / (1.0 + np.exp(-ls))
+
+
+def pin_router_backward_finite_differences():
+    """With the selection fixed, L(x, W_r) = sum drw * w(x W_r); central
+    differences of L against every entry of dl = dL/dlogits, dW_r and the
+    router's dX, for both scores."""
+    h = 1e-6
+    for score, K in ((synth.SOFTMAX_TOPK, 3), (synth.SIGMOID, 1), (synth.SOFTMAX_TOPK, 5)):
+        r = _rng(42 + K)
+        T, D, E = 7, 6, 5
+        x = r.standard_normal((T, D))
+        w_r = r.standard_normal((D, E))
+        drw = r.standard_normal((T, K))
+        l0 = x @ w_r
+        idx, w = oracle.route(l0.astype(np.float32), K, score)
+        dl, dw_r, dx_r = oracle.router_backward(x, w_r, idx, _router_weights(l0, idx, score), drw,
+                                                score)
+
+        def loss_l(l):
+            return float(np.sum(drw * _router_weights(l, idx, score)))
+
+        def fd(arr, f):
+            out = np.empty(arr.size)
+            flat = arr.reshape(-1)
+            for j in range(flat.size):
+                keep = flat[j]
+                flat[j] = keep + h
+                lp = f()
+                flat[j] = keep - h
+                lm = f()
+                flat[j] = keep
+                out[j] = (lp - lm) / (2 * h)
+            return out.reshape(arr.shape)
+
+        l = l0.copy()
+        np.testing.assert_allclose(dl, fd(l, lambda: loss_l(l)), rtol=1e-6, atol=1e-8, err_msg="dl")
+        np.testing.assert_allclose(dw_r, fd(w_r, lambda: loss_l(x @ w_r)), rtol=1e-6, atol=1e-8,
+                                   err_msg="dW_r")
+        np.testing.assert_allclose(dx_r, fd(x, lambda: loss_l(x @ w_r)), rtol=1e-6, atol=1e-8,
+                                   err_msg="dx_r")
+
+
+def pin_router_backward_invariants():
+    """Renormalised weights are invariant to a common shift of the selected
+    logits, so each token's dl sums to 0 over its experts; K = 1 renormalised
+    (w = 1 always) gives dl = 0 exactly; unselected experts get dl = 0."""
+    r = _rng(45)
+    T, D, E, K = 40, 8, 6, 3
+    x = r.standard_normal((T, D))
+    w_r = r.standard_normal((D, E))
+    l = (x @ w_r).astype(np.float32)
+    idx, w = oracle.route(l, K, synth.SOFTMAX_TOPK)
+    dl, _, _ = oracle.router_backward(x, w_r, idx, w, r.standard_normal((T, K)), synth.SOFTMAX_TOPK)
+    np.testing.assert_allclose(dl.sum(axis=1), 0.0, atol=1e-13)
+    sel = np.zeros((T, E), bool)
+    np.put_along_axis(sel, idx.astype(np.int64), True, axis=1)
+    assert not dl[~sel].any()
+    idx1, w1 = oracle.route(l, 1, synth.SOFTMAX_TOPK)
+    assert np.all(w1 == 1.0)
+    dl1, dw1, dx1 = oracle.router_backward(x, w_r, idx1, w1, r.standard_normal((T, 1)),
+                                           synth.SOFTMAX_TOPK)
+    assert not dl1.any() and not dw1.any() and not dx1.any()
+
+
+def pin_router_full_layer_input_gradient():
+    """Through the whole layer with the selection fixed, L = <dY, y> depends on
+    x along two paths (the experts' inputs and the router logits x W_r); the
+    expert-path dX plus the router's dX (fed with the layer's dRouterWeights)
+    matches central differences of L in x, and dW_r matches them in W_r."""
+    L, _ = _random_layer(T=6, D=5, I=4, E=4, K=2, score=synth.SOFTMAX_TOPK, seed=46)
+    r = _rng(47)
+    w_r = r.standard_normal((L.D, L.E))
+    l0 = L.x @ w_r
+    idx, _ = oracle.route(l0.astype(np.float32), 2, synth.SOFTMAX_TOPK)
+
+    def loss():
+        w = _router_weights(L.x @ w_r, idx, synth.SOFTMAX_TOPK)
+        return float(np.sum(L.dy * oracle.forward(L, idx, w)))
+
+    w = _router_weights(l0, idx, synth.SOFTMAX_TOPK)
+    dx_e, drw = oracle.backward_tokens(L, idx, w)
+    _, dw_r, dx_r = oracle.router_backward(L.x, w_r, idx, w, drw, synth.SOFTMAX_TOPK)
+    h = 1e-6
+    for arr, grad, name in ((L.x, dx_e + dx_r, "dx"), (w_r, dw_r, "dW_r")):
+        flat = arr.reshape(-1)
+        num = np.empty(flat.size)
+        for j in range(flat.size):
+            keep = flat[j]
+            flat[j] = keep + h
+            lp = loss()
+            flat[j] = keep - h
+            lm = loss()
+            flat[j] = keep
+            num[j] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(grad.reshape(-1), num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
 PINS = [
     pin_route_bruteforce,
     pin_route_hand_example,
@@ -333,6 +447,10 @@ PINS = [
     pin_backward_euler_identities,
     pin_backward_empty_expert_and_entries,
     pin_backward_dw_token_subset,
+    pin_router_logits_library,
+    pin_router_backward_finite_differences,
+    pin_router_backward_invariants,
+    pin_router_full_layer_input_gradient,
 ]
 
 

@@ -38,6 +38,20 @@ MUTANTS = [
      "acc += (which[q] == 0 ? du : dg) * xt[c];"),
     ("dW_gate uses the up gradient", "dwg[(size_t)i * D + c] += dg[i] * xt[c];",
      "dwg[(size_t)i * D + c] += du[i] * xt[c];"),
+    ("router: renormalisation correction with the wrong sign",
+     "dlt[idx[t * K + m]] = wt[m] * (gt[m] - s);", "dlt[idx[t * K + m]] = wt[m] * (gt[m] + s);"),
+    ("router: sigmoid derivative factor dropped",
+     "dlt[idx[t * K + k]] = gt[k] * wt[k] * (1.0 - wt[k]);", "dlt[idx[t * K + k]] = gt[k] * wt[k];"),
+    ("router: projection reads W_r transposed",
+     "s += x[t * D + j] * w_r[(size_t)j * E + e];",
+     "s += x[t * D + j] * w_r[((size_t)e * D + j) % ((size_t)D * E)];"),
+    ("router: dW_r pairs x with the wrong expert",
+     "s += x[t * D + j] * dl[t * E + e];", "s += x[t * D + j] * dl[t * E + (E - 1 - e)];"),
+    ("router: dX reads W_r transposed",
+     "s += dl[t * E + e] * w_r[(size_t)j * E + e];",
+     "s += dl[t * E + e] * w_r[((size_t)e * D + j) % ((size_t)D * E)];"),
+    ("router: dW_r without the input",
+     "s += x[t * D + j] * dl[t * E + e];", "s += dl[t * E + e];"),
     ("unstable placement inside an expert",
      "int32_t p = cursor[idx[f]]++;", "int32_t p = offsets[idx[f] + 1] - 1 - (cursor[idx[f]]++ - offsets[idx[f]]);"),
 ]
