@@ -1,6 +1,7 @@
 /*
  * moe.h -- C ABI of the routed SwiGLU mixture-of-experts layer on one AMD
- * Instinct MI355X (gfx950): routing + sort by expert, forward, backward.
+ * Instinct MI355X (gfx950): router projection, routing + sort by expert,
+ * forward, backward, router backward.
  *
  * Method: the LigerCute package README (liger-cute-kernels 0.8.3), section
  * "LigerMoE design" (sub-sections "Forward pass" and "Backward pass"): sort
@@ -27,7 +28,8 @@
  *     status tells why.  Device *contents* are not validated (expert ids out
  *     of range, offsets that do not match the ids): that is undefined
  *     behaviour, because checking it would need a device-to-host read.
- *   - Outputs are overwritten (see `accumulate_dw` for the one exception).
+ *   - Outputs are overwritten, except where an `accumulate_*` flag asks for
+ *     addition and for the in/out `dx` of moe_router_bwd.
  *     Results are bitwise deterministic run to run (no floating-point atomics).
  *   - Symbols: the library exports only `moe_*`.
  *
@@ -46,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* Router score functions. */
 #define MOE_SCORE_SOFTMAX_TOPK 0 /* softmax over E, keep top K, renormalise over the K */
@@ -64,6 +66,7 @@ extern "C" {
 #define MOE_PHASE_ROUTE 0
 #define MOE_PHASE_FWD 1
 #define MOE_PHASE_BWD 2
+#define MOE_PHASE_ROUTER_BWD 3
 
 typedef int32_t moe_status;
 
@@ -136,6 +139,47 @@ moe_status moe_bwd(const moe_dims *dims, const void *x, const void *w_gate, cons
                    const void *dy, void *dx, float *dw_gate, float *dw_up, float *dw_down,
                    float *d_topk_w, int32_t accumulate_dw, void *ws, size_t ws_bytes,
                    void *stream);
+
+/* Router projection, the input side of the layer: the logits that
+ * moe_route_sort selects on ("LigerMoE design / Forward pass": the router
+ * weights that the final combine applies come from these logits).
+ *     logits[t, e] = sum_d x[t, d] w_r[d, e]
+ *   x        device bf16 [T, D]
+ *   w_r      device fp32 [D, E]   router projection (note: [in, out], so that
+ *                                 logits = x w_r)
+ *   logits   device fp32 [T, E]   out
+ * Computed on the fp32 matrix cores (bf16 x converted exactly to fp32), fp32
+ * accumulation.  Only dims->T, D, E are used; the other dims must still be
+ * valid (the router is part of the layer the dims describe). */
+moe_status moe_router_fwd(const moe_dims *dims, const void *x, const float *w_r, float *logits,
+                          void *stream);
+
+/* Router backward, the step before the input side of "LigerMoE design /
+ * Backward pass": with the top-K selection held fixed (it is piecewise
+ * constant in the logits), the router-weight gradient d_topk_w that moe_bwd
+ * returns flows back through the score function into the selected logits,
+ *   softmax-renormalised:  dl[t, idx_k] = w_k (d_k - sum_j w_j d_j)
+ *   sigmoid:               dl[t, idx_k] = d_k w_k (1 - w_k)
+ * (dl = 0 for unselected experts), and from there into the projection and
+ * the layer input:
+ *   dw_r = x^T dl          [D, E]
+ *   dx  += dl w_r^T        [T, D]
+ *   x, w_r              as for moe_router_fwd
+ *   topk_idx, topk_w    as produced by moe_route_sort (the selection and its weights)
+ *   d_topk_w            device fp32 [T, K]  dL/dtopk_w, as produced by moe_bwd
+ *   dx                  device bf16 [T, D]  in/out: the expert-path input gradient
+ *                       from moe_bwd on entry; on return dx + the router path's
+ *                       contribution (fp32 sum over k ascending, one rounding)
+ *   dw_r                device fp32 [D, E]  out: dL/dw_r
+ *   accumulate_dwr      0: overwrite dw_r;  1: add into dw_r (fp32)
+ *   ws, ws_bytes        device workspace of at least
+ *                       moe_workspace_bytes(dims, MOE_PHASE_ROUTER_BWD)
+ * dw_r is reduced over fixed token ranges whose partials are summed in range
+ * order (no atomics: bitwise deterministic). */
+moe_status moe_router_bwd(const moe_dims *dims, const void *x, const float *w_r,
+                          const int32_t *topk_idx, const float *topk_w, const float *d_topk_w,
+                          void *dx, float *dw_r, int32_t accumulate_dwr, void *ws,
+                          size_t ws_bytes, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *moe_status_string(moe_status status);

@@ -17,7 +17,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
 
 MOE_SCORE_SOFTMAX_TOPK = 0
 MOE_SCORE_SIGMOID = 1
-MOE_PHASE_ROUTE, MOE_PHASE_FWD, MOE_PHASE_BWD = 0, 1, 2
+MOE_PHASE_ROUTE, MOE_PHASE_FWD, MOE_PHASE_BWD, MOE_PHASE_ROUTER_BWD = 0, 1, 2, 3
 MOE_OK = 0
 
 
@@ -62,6 +62,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.moe_bwd.restype = ctypes.c_int32
         lib.moe_bwd.argtypes = ([ctypes.POINTER(moe_dims)] + [_vp] * 14 + [ctypes.c_int32] +
                                 [_vp, ctypes.c_size_t, _vp])
+        lib.moe_router_fwd.restype = ctypes.c_int32
+        lib.moe_router_fwd.argtypes = [ctypes.POINTER(moe_dims)] + [_vp] * 3 + [_vp]
+        lib.moe_router_bwd.restype = ctypes.c_int32
+        lib.moe_router_bwd.argtypes = ([ctypes.POINTER(moe_dims)] + [_vp] * 7 + [ctypes.c_int32] +
+                                       [_vp, ctypes.c_size_t, _vp])
         lib.moe_status_string.restype = ctypes.c_char_p
         lib.moe_status_string.argtypes = [ctypes.c_int32]
         lib.moe_abi_version.restype = ctypes.c_int32
@@ -232,6 +237,49 @@ def moe_bwd(x, w_gate, w_up, w_down, route: dict, dy, K: int, score: int = MOE_S
         _vp(ws.data_ptr()), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream))
     _check(rc, "moe_bwd")
     return out
+
+
+def _router_dims(x, w_r, K, score):
+    T, D = x.shape
+    E = w_r.shape[1]
+    return dims(T, D, 64, E, K, score)
+
+
+def moe_router_fwd(x, w_r, *, logits=None, stream=None):
+    """Router projection.  x bf16 [T, D]; w_r fp32 [D, E].  Returns logits fp32 [T, E]."""
+    torch = _torch()
+    d = _router_dims(x, w_r, 1, MOE_SCORE_SOFTMAX_TOPK)
+    T, D, E = d.T, d.D, d.E
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    rc = load_library().moe_router_fwd(
+        ctypes.byref(d), _ptr(x, torch.bfloat16, (T, D), "x"),
+        _ptr(w_r, torch.float32, (D, E), "w_r"), _ptr(logits, torch.float32, (T, E), "logits"),
+        _stream(stream))
+    _check(rc, "moe_router_fwd")
+    return logits
+
+
+def moe_router_bwd(x, w_r, route: dict, d_topk_w, dx, K: int,
+                   score: int = MOE_SCORE_SOFTMAX_TOPK, *, dw_r=None,
+                   accumulate_dwr: bool = False, ws=None, stream=None):
+    """Router backward, selection fixed.  Adds the router path's input gradient
+    into dx (bf16 [T, D], in place) and returns dw_r fp32 [D, E]."""
+    torch = _torch()
+    d = _router_dims(x, w_r, K, score)
+    T, D, E = d.T, d.D, d.E
+    if dw_r is None:
+        dw_r = torch.empty((D, E), dtype=torch.float32, device=x.device)
+    ws, need = _workspace(d, MOE_PHASE_ROUTER_BWD, ws, x.device)
+    b, i32, f32 = torch.bfloat16, torch.int32, torch.float32
+    rc = load_library().moe_router_bwd(
+        ctypes.byref(d), _ptr(x, b, (T, D), "x"), _ptr(w_r, f32, (D, E), "w_r"),
+        _ptr(route["topk_idx"], i32, (T, K), "topk_idx"), _ptr(route["topk_w"], f32, (T, K), "topk_w"),
+        _ptr(d_topk_w, f32, (T, K), "d_topk_w"), _ptr(dx, b, (T, D), "dx"),
+        _ptr(dw_r, f32, (D, E), "dw_r"), ctypes.c_int32(1 if accumulate_dwr else 0),
+        _vp(ws.data_ptr()), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream))
+    _check(rc, "moe_router_bwd")
+    return dw_r
 
 
 # ----------------------------------------------------------------------------- per-kernel timing

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["abi.hip", "route.hip", "permute.hip", "gemm.hip", "prof.hip"]
+SOURCES = ["abi.hip", "route.hip", "permute.hip", "gemm.hip", "router.hip", "prof.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -108,6 +108,20 @@ size_t bwd_ws(const moe_dims& d, BwdWs* w, void* base) {
   return c.used;
 }
 
+struct RouterBwdWs {
+  float *w_rt, *dl, *part;
+};
+
+size_t router_bwd_ws(const moe_dims& d, RouterBwdWs* w, void* base) {
+  Carve c{(char*)base};
+  int splits, tc;
+  router_dwr_split(d.T, &splits, &tc);
+  w->w_rt = c.take<float>((size_t)d.E * d.D);
+  w->dl = c.take<float>(std::max<size_t>(1, (size_t)d.T * d.K));
+  w->part = c.take<float>((size_t)splits * d.D * d.E);
+  return c.used;
+}
+
 int rowgrouped_grid(const moe_dims& d, int n_tiles) {
   const int64_t R = (int64_t)d.T * d.K;
   const int64_t mt = (R + (int64_t)d.E * (kGemmBM - 1)) / kGemmBM;
@@ -161,6 +175,10 @@ MOE_EXPORT size_t moe_workspace_bytes(const moe_dims* dims, int32_t phase) {
     case MOE_PHASE_BWD: {
       BwdWs w;
       return bwd_ws(*dims, &w, nullptr);
+    }
+    case MOE_PHASE_ROUTER_BWD: {
+      RouterBwdWs w;
+      return router_bwd_ws(*dims, &w, nullptr);
     }
     default:
       return 0;
@@ -376,6 +394,44 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
                                    partials_per_row(d), st));
   }
   return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_router_fwd(const moe_dims* dims, const void* x, const float* w_r,
+                                     float* logits, void* stream) {
+  moe_status s = check_dims(dims);
+  if (s != MOE_OK) return s;
+  const size_t TD = (size_t)dims->T * dims->D;
+  if (!ptr_ok(x, TD, 16) || !ptr_ok(w_r, (size_t)dims->D * dims->E, 16) ||
+      !ptr_ok(logits, (size_t)dims->T * dims->E, 4))
+    return MOE_ERR_BAD_ARG;
+  clear_stale_error();
+  return hip_status(launch_router_logits(x, w_r, logits, dims->T, dims->D, dims->E,
+                                         (hipStream_t)stream),
+                    "router_fwd");
+}
+
+MOE_EXPORT moe_status moe_router_bwd(const moe_dims* dims, const void* x, const float* w_r,
+                                     const int32_t* topk_idx, const float* topk_w,
+                                     const float* d_topk_w, void* dx, float* dw_r,
+                                     int32_t accumulate_dwr, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  moe_status s = check_dims(dims);
+  if (s != MOE_OK) return s;
+  const size_t R = (size_t)dims->T * dims->K, TD = (size_t)dims->T * dims->D;
+  const size_t DE = (size_t)dims->D * dims->E;
+  if (!ptr_ok(x, TD, 16) || !ptr_ok(dx, TD, 16) || !ptr_ok(w_r, DE, 16) ||
+      !ptr_ok(dw_r, DE, 16) || !ptr_ok(topk_idx, R, 4) || !ptr_ok(topk_w, R, 4) ||
+      !ptr_ok(d_topk_w, R, 4) || !ptr_ok(ws, 1, 16))
+    return MOE_ERR_BAD_ARG;
+  if (accumulate_dwr != 0 && accumulate_dwr != 1) return MOE_ERR_BAD_ARG;
+  RouterBwdWs w;
+  if (ws_bytes < router_bwd_ws(*dims, &w, ws)) return MOE_ERR_WORKSPACE;
+  const moe_dims& d = *dims;
+  clear_stale_error();
+  return hip_status(launch_router_bwd(x, w_r, topk_idx, topk_w, d_topk_w, dx, dw_r,
+                                      accumulate_dwr, w.dl, w.w_rt, w.part, d.T, d.D, d.E, d.K,
+                                      d.score, (hipStream_t)stream),
+                    "router_bwd");
 }
 
 MOE_EXPORT const char* moe_status_string(moe_status status) {

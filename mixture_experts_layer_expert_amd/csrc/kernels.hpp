@@ -10,7 +10,8 @@ namespace moe {
 enum KernelId : int {
   kKRouteTopk, kKRouteHist, kKRouteScan, kKRouteScatter, kKTilemap, kKGather,
   kKGemmGateUpH, kKGemmGateUpGU, kKGemmDown, kKGemmDA, kKGemmDXs, kKGemmDWDown,
-  kKGemmDWGateUp, kKCombine, kKReduceRows, kKReducePartials, kKGather2, kNumKernels
+  kKGemmDWGateUp, kKCombine, kKReduceRows, kKReducePartials, kKGather2, kKRouterLogits,
+  kKRouterPrep, kKRouterDx, kKRouterDwr, kKRouterDwrSum, kNumKernels
 };
 namespace prof {
 void begin(int kid, hipStream_t st);  // no-ops unless timing is enabled
@@ -44,6 +45,16 @@ hipError_t launch_combine(const void* O, const float* w, const int32_t* f2s, voi
 hipError_t launch_reduce_rows(const void* dXs, void* dx, int T, int K, int D, hipStream_t st);
 hipError_t launch_reduce_partials(const float* part, const int32_t* f2s, float* out, int R,
                                   int np, hipStream_t st);
+
+// ---- router projection and router backward (router.hip)
+hipError_t launch_router_logits(const void* x, const float* w_r, float* logits, int T, int D,
+                                int E, hipStream_t st);
+// Token ranges of the dW_r partials: `splits` ranges of `tokens_per_split` tokens.
+void router_dwr_split(int T, int* splits, int* tokens_per_split);
+hipError_t launch_router_bwd(const void* x, const float* w_r, const int32_t* topk_idx,
+                             const float* topk_w, const float* d_topk_w, void* dx, float* dw_r,
+                             int accumulate, float* dl, float* w_rt, float* part, int T, int D,
+                             int E, int K, int score, hipStream_t st);
 
 // ---- grouped GEMMs (gemm.hip)
 // Workgroup tile geometry (shared by the kernels and the host-side tile

@@ -27,7 +27,8 @@ const char* const kNames[kNumKernels] = {
     "route_topk",   "route_hist",    "route_scan",    "route_scatter", "tilemap",
     "gather",       "gemm_gateup_h", "gemm_gateup_gu", "gemm_down",    "gemm_da",
     "gemm_dxs",     "gemm_dw_down",  "gemm_dw_gateup", "combine",      "reduce_rows",
-    "reduce_partials", "gather2"};
+    "reduce_partials", "gather2",   "router_logits", "router_prep",  "router_dx",
+    "router_dwr",   "router_dwr_sum"};
 
 hipEvent_t take() {
   if (!pool.empty()) {

@@ -36,14 +36,14 @@ def test_no_torch_dependency(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     for code in range(6):
         assert moe.status_string(code)
 
 
 def test_workspace_bytes_host_only(lib):
     q = moe.dims(8192, 2048, 768, 128, 8)
-    sizes = [moe.moe_workspace_bytes(q, ph) for ph in range(3)]
+    sizes = [moe.moe_workspace_bytes(q, ph) for ph in range(4)]
     assert all(s > 0 for s in sizes)
     # backward holds Xs, dOu, GU, dGU, Hw, dXs in bf16 + fp32 partials at least
     R = 8192 * 8
@@ -91,6 +91,24 @@ def test_bad_pointers_and_workspace(lib):
                        ctypes.c_size_t(1 << 40), None) == 1           # accumulate_dw not 0/1
     assert lib.moe_bwd(ctypes.byref(d), *bwd_args, ctypes.c_int32(0), FAKE,
                        ctypes.c_size_t(8), None) == 3
+
+
+def test_router_bad_args(lib):
+    d = moe.dims(16, 64, 64, 4, 2)
+    assert lib.moe_router_fwd(ctypes.byref(moe.dims(16, 100, 64, 4, 2)), FAKE, FAKE, FAKE,
+                              None) == 2                                # D % 64
+    assert lib.moe_router_fwd(ctypes.byref(d), ctypes.c_void_p(0), FAKE, FAKE, None) == 1
+    assert lib.moe_router_fwd(ctypes.byref(d), FAKE, ctypes.c_void_p((1 << 20) + 4), FAKE,
+                              None) == 1                                # w_r not 16-B aligned
+    args = [FAKE] * 7
+    assert lib.moe_router_bwd(ctypes.byref(d), *args, ctypes.c_int32(2), FAKE,
+                              ctypes.c_size_t(1 << 40), None) == 1      # accumulate_dwr not 0/1
+    assert lib.moe_router_bwd(ctypes.byref(d), *args, ctypes.c_int32(0), FAKE,
+                              ctypes.c_size_t(8), None) == 3            # workspace too small
+    assert lib.moe_router_bwd(ctypes.byref(d), *args[:6], ctypes.c_void_p(0), ctypes.c_int32(0),
+                              FAKE, ctypes.c_size_t(1 << 40), None) == 1  # null dw_r
+    need = moe.moe_workspace_bytes(d, moe.MOE_PHASE_ROUTER_BWD)
+    assert need >= 4 * (64 * 4 + 16 * 2 + 64 * 4)    # W_r^T, dl, one partial of dW_r
 
 
 def test_prof_names(lib):
