@@ -36,6 +36,7 @@ import synth  # noqa: E402
 
 METRIC = "MoE layer TFLOP/s fwd & bwd, Qwen3-30B-A3B shape, 8192 tokens, 1×MI355X"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak (no sparsity)
+PEAK_FP32_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
 PEAK_HBM_GBPS = 8000.0
 
 WORKLOADS = {"qwen3_30b_a3b": synth.QWEN3_30B_A3B, "llama4_scout": synth.LLAMA4_SCOUT,
@@ -61,7 +62,18 @@ def kernel_work(wl: synth.Workload) -> dict:
         "route_topk": ("hbm", 4.0 * T * E + 8 * R),
         "route_hist": ("hbm", 4.0 * R), "route_scan": ("hbm", 8.0 * E),
         "route_scatter": ("hbm", 12.0 * R), "tilemap": ("hbm", 8.0 * E),
+        # router projection and router backward (timed beside the step, not in it)
+        "router_logits": ("mfma32", 2.0 * T * D * E), "router_dwr": ("mfma32", 2.0 * T * D * E),
+        # dX += dl W_r^T: read and write dX (4*T*D), dl and indices (8R); W_r^T rows from L2
+        "router_dx": ("hbm", 4.0 * T * D + 8 * R),
+        "router_dwr_sum": ("hbm", 4.0 * D * E * (router_splits(T) + 1)),
     }
+
+
+def router_splits(T: int) -> int:
+    """Token ranges of the dW_r partials (as the library chooses them)."""
+    tc = max(512, (-(-T // 64) + 31) // 32 * 32)
+    return max(1, -(-T // tc))
 
 
 GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_expert_amd", "csrc", "gemm.hip")
@@ -201,16 +213,49 @@ def main() -> int:
             extra[f"{name}_ms"] = round(ms, 4)
             extra[f"{name}_tflops"] = round(fl / (ms * 1e-3) / 1e12, 2)
 
+    # router projection + router backward, timed on their own (not part of the step)
+    router = None
+    if not args.fwd_bwd_only:
+        w_r = G.to_dev(data["w_r"])
+        logits = torch.empty((wl.T, wl.E), dtype=torch.float32, device="cuda")
+        ws_r = torch.empty(moe.moe_workspace_bytes(d, moe.MOE_PHASE_ROUTER_BWD), dtype=torch.uint8,
+                           device="cuda")
+        dx_r = grads["dx"].clone()
+        dw_r = torch.empty((wl.D, wl.E), dtype=torch.float32, device="cuda")
+
+        def rstep(fwd=True, bwd=True):
+            if fwd:
+                moe.moe_router_fwd(dev.x, w_r, logits=logits)
+            if bwd:
+                moe.moe_router_bwd(dev.x, w_r, route, grads["d_topk_w"], dx_r, wl.K, wl.score,
+                                   dw_r=dw_r, ws=ws_r)
+
+        for _ in range(args.warmup):
+            rstep()
+        torch.cuda.synchronize()
+        moe.moe_prof_enable(True)
+        router = {}
+        for name, kw in (("fwd", dict(bwd=False)), ("bwd", dict(fwd=False))):
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(args.steps):
+                rstep(**kw)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            router[f"{name}_ms"] = round(ev0.elapsed_time(ev1) / args.steps, 4)
+        kern.update(moe.moe_prof_read())
+        moe.moe_prof_enable(False)
+
     work = kernel_work(wl)
     kernels = {}
     for name, (tot_ms, n) in kern.items():
         avg_ms = tot_ms / n
         bound, amount = work.get(name, ("hbm", 0.0))
         rate = amount / (avg_ms * 1e-3)
-        if bound == "mfma":
-            kernels[name] = {"avg_us": round(avg_ms * 1e3, 2), "launches": n, "bound": "mfma",
-                             "tflops": round(rate / 1e12, 2),
-                             "frac": round(rate / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        if bound in ("mfma", "mfma32"):
+            peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_FP32_TFLOPS
+            kernels[name] = {"avg_us": round(avg_ms * 1e3, 2), "launches": n, "bound": bound,
+                             "tflops": round(rate / 1e12, 2), "frac": round(rate / 1e12 / peak, 4)}
         else:
             kernels[name] = {"avg_us": round(avg_ms * 1e3, 2), "launches": n, "bound": "hbm",
                              "gbps": round(rate / 1e9, 1),
@@ -235,6 +280,7 @@ def main() -> int:
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": stored_traffic(dom, wl.name)},
         **extra,
+        "router": router,
         "gemm_tflops_all": round(gemm_flops / (gemm_total_ms * 1e-3) / 1e12, 2),
         "gemm_frac_all": round(gemm_flops / (gemm_total_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernels": kernels,

@@ -40,11 +40,13 @@
 //     GEMMs (dXs, dW) multiply fp16: dG/dU/Hw are rounded to fp16 (3 more
 //     mantissa bits than bf16, at the same matrix-core rate) and bf16 operand
 //     fragments are converted (exactly, for |v| in fp16's normal range) after
-//     the LDS read.  The dW GEMMs sum over all of an expert's rows, where
-//     rounding errors grow with the row count while the result can cancel to
-//     ~0, so there the rounded operand is split in fp16 hi + lo and
-//     multiplied in two passes into the same accumulators (error about
-//     2^-22 sum |terms|);
+//     the LDS read.  The dW GEMMs sum over all of an expert's rows, where the
+//     rounding error grows like the square root of the row count while the
+//     result can cancel to ~0, so for an expert with more than kDwSplitRows
+//     rows the rounded operand is split in fp16 hi + lo and multiplied in two
+//     passes into the same accumulators (error about 2^-22 sum |terms|);
+//     smaller experts take one pass over hi (error about 2^-12 times the
+//     root-sum-square of the terms);
 //   - ragged expert segments: the tile list is built on the device from the
 //     expert offsets (no host read-back, graph-capturable);
 //   - weight gradients: one workgroup owns one output tile and walks all of
@@ -301,8 +303,8 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       kbase = (size_t)p.offsets[e];
       k_count = p.offsets[e + 1] - p.offsets[e];
       nk_pass = ceil_div(k_count, BK);
-      // split operand: a second pass over the rows with its low part
-      nk = (p.A_lo || p.B_lo) ? 2 * nk_pass : nk_pass;
+      // split operand (experts with many rows): a second pass with its low part
+      nk = ((p.A_lo || p.B_lo) && k_count > kDwSplitRows) ? 2 * nk_pass : nk_pass;
       rows_valid = p.M - m0;
     }
   }
@@ -645,6 +647,8 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     bf16_t* const outs[6] = {p.C0, p.C1, p.C2, p.L0, p.L1, p.L2};
     const size_t ldo[6] = {(size_t)p.ldc, (size_t)p.ldc, (size_t)I,
                             (size_t)p.ldc, (size_t)p.ldc, (size_t)I};
+    // the low parts are read only by the dW GEMMs of experts with many rows
+    const bool need_lo = p.offsets[e + 1] - p.offsets[e] > kDwSplitRows;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = wm * WTM + i * 16 + frow;
@@ -700,6 +704,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       // write it back as row segments, CPR lanes per row
 #pragma unroll
       for (int o = 0; o < 6; ++o) {
+        if (o >= 3 && !need_lo) break;
 #pragma unroll
         for (int h = 0; h < 16 * CPR / 64; ++h) {
           const int srow = h * (64 / CPR) + lane / CPR, ch = lane % CPR;

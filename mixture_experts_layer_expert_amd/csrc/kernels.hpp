@@ -88,6 +88,12 @@ constexpr int kGemmBN = MOE_GEMM_BN;  // columns of a tile (gate/up: BN/2 gate +
 #ifndef MOE_GEMM_PREFETCH
 #define MOE_GEMM_PREFETCH 1
 #endif
+#ifndef MOE_DW_SPLIT_ROWS
+#define MOE_DW_SPLIT_ROWS 2048
+#endif
+// Experts with more routed rows than this get the fp16 hi + lo split of the
+// rounded dW operand (two MFMA passes); smaller ones one pass over fp16 hi.
+constexpr int kDwSplitRows = MOE_DW_SPLIT_ROWS;
 constexpr int kGemmPrefetch = MOE_GEMM_PREFETCH;  // L2 prefetch distance in stages
 constexpr int kGemmBK = MOE_GEMM_BK;  // reduction depth of one LDS stage (32 or 64)
 constexpr int kGemmWM = MOE_GEMM_WM;  // waves along the rows
