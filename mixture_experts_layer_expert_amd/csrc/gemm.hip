@@ -564,7 +564,9 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();  // every wave is done reading the stage buffers
   asm volatile("" ::: "memory");
-  auto store16 = [](char* dst, u32x4 v) { *(u32x4*)dst = v; };
+  // Results are written once and not re-read by this kernel: non-temporal
+  // stores keep them from evicting lines that later kernels still read.
+  auto store16 = [](char* dst, u32x4 v) { __builtin_nontemporal_store(v, (u32x4*)dst); };
   if constexpr (MODE == kGateUpH || MODE == kGateUpGU) {
     // the wave's WTN/2 gate columns and the matching up columns
     constexpr int CW = WTN / 2;
@@ -735,7 +737,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
         [&](char* dst, u32x4 v) {
           f32x4 x = __builtin_bit_cast(f32x4, v);
           if (accum) x += *(const f32x4*)dst;
-          *(f32x4*)dst = x;
+          __builtin_nontemporal_store(x, (f32x4*)dst);
         });
     }
   }

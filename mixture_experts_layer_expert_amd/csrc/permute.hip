@@ -84,7 +84,8 @@ __global__ __launch_bounds__(kPermuteThreads) void combine_kernel(
 }
 
 // dX[t, :] = sum_{k<K} dXs[t*K + k, :]  (fp32 rows in flat slot order, fp32 sum,
-// k ascending).  The K rows of a token are contiguous, so the reads stream.
+// k ascending).  The K rows of a token are contiguous, so the reads stream;
+// they are read once (non-temporal loads).
 // Each thread produces 4 outputs from one 16-byte read per routed copy; with
 // KT > 0 all K reads are in flight together.  cpr4 = D / 4.
 template <int KT>
@@ -101,11 +102,11 @@ __global__ __launch_bounds__(kPermuteThreads) void reduce_rows_kernel(
     if constexpr (KT > 0) {
       f32x4 v[KT];
 #pragma unroll
-      for (int k = 0; k < KT; ++k) v[k] = rows[(size_t)k * cpr4];
+      for (int k = 0; k < KT; ++k) v[k] = __builtin_nontemporal_load(rows + (size_t)k * cpr4);
 #pragma unroll
       for (int k = 0; k < KT; ++k) a += v[k];
     } else {
-      for (int k = 0; k < K; ++k) a += rows[(size_t)k * cpr4];
+      for (int k = 0; k < K; ++k) a += __builtin_nontemporal_load(rows + (size_t)k * cpr4);
     }
     dx[c] = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
   }

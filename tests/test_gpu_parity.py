@@ -74,6 +74,9 @@ SMALL = {
     "ragged_cols": lambda: _custom(T=300, D=320, I=64, E=16, K=3, score=0, seed=102),
     # many routed copies per token (K = 16 of 64 experts)
     "k16": lambda: _custom(T=96, D=128, I=64, E=64, K=16, score=0, seed=108),
+    # one expert above the 2048-row threshold of the dW operand split (two MFMA
+    # passes) beside three below it (one pass), every element compared
+    "split_hot": lambda: _custom(T=3000, D=128, I=64, E=4, K=2, score=0, seed=109, hot=0),
     # skewed routing: one hot expert, three experts never chosen
     "skew_empty": lambda: _custom(T=500, D=128, I=128, E=8, K=2, score=0, seed=103, hot=1,
                                   dead=(2, 5, 7)),
