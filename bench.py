@@ -2,9 +2,10 @@
 """Benchmark of the routed SwiGLU MoE layer on one MI355X.
 
 One step = the whole hot path over one batch: routing + sort by expert,
-forward (gather, gate/up GEMM + SwiGLU, down GEMM, weighted combine) and
-backward (re-gather, recompute, dA + SwiGLU backward, dX GEMM, dW GEMMs,
-dX/dRouterWeights reductions), all through the C ABI on device-resident
+forward (gate/up GEMM + SwiGLU over the routed rows gathered in its loads,
+down GEMM, weighted combine) and backward (recompute, dA + SwiGLU backward,
+dX GEMM, dW GEMMs, all gathering x / dy rows in their loads; dX and
+dRouterWeights reductions), all through the C ABI on device-resident
 inputs.  Workload: the Qwen3-30B-A3B layer shape (T=8192 tokens, D=2048,
 I=768, E=128 experts, top-8, softmax-renormalised routing), synthetic seeded
 inputs.
@@ -62,6 +63,7 @@ def kernel_work(wl: synth.Workload) -> dict:
         "route_topk": ("hbm", 4.0 * T * E + 8 * R),
         "route_hist": ("hbm", 4.0 * R), "route_scan": ("hbm", 8.0 * E),
         "route_scatter": ("hbm", 12.0 * R), "tilemap": ("hbm", 8.0 * E),
+        "row_offsets": ("hbm", 8.0 * R),
         # router projection and router backward (timed beside the step, not in it)
         "router_logits": ("mfma32", 2.0 * T * D * E), "router_dwr": ("mfma32", 2.0 * T * D * E),
         # dX += dl W_r^T: read and write dX (4*T*D), dl and indices (8R); W_r^T rows from L2

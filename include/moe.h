@@ -101,9 +101,10 @@ moe_status moe_route_sort(const moe_dims *dims, const float *logits, int32_t *to
                           int32_t *sorted_to_flat, int32_t *flat_to_sorted, void *ws,
                           size_t ws_bytes, void *stream);
 
-/* Forward ("LigerMoE design / Forward pass"): gather the routed rows into
- * expert order, grouped gate/up GEMM with the SwiGLU fused into its epilogue,
- * grouped down GEMM, then the router-weighted combine
+/* Forward ("LigerMoE design / Forward pass"): grouped gate/up GEMM over the
+ * routed rows in expert order (gathered from x inside the GEMM's operand
+ * loads) with the SwiGLU fused into its epilogue, grouped down GEMM, then the
+ * router-weighted combine
  *     y[t] = sum_{k<K} topk_w[t,k] * o[t,k]      (fp32 accumulation, k ascending)
  *
  *   x               device bf16 [T, D]
@@ -112,8 +113,8 @@ moe_status moe_route_sort(const moe_dims *dims, const float *logits, int32_t *to
  *   topk_w, offsets, sorted_to_flat, flat_to_sorted   as produced by moe_route_sort
  *   y               device bf16 [T, D]   out
  *   ws, ws_bytes    device workspace of at least moe_workspace_bytes(dims, MOE_PHASE_FWD)
- * Intermediates (gathered rows, SwiGLU activations, unweighted expert outputs)
- * are stored as bf16 in the workspace; all GEMMs accumulate in fp32. */
+ * Intermediates (SwiGLU activations, unweighted expert outputs) are stored as
+ * bf16 in the workspace; all GEMMs accumulate in fp32. */
 moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, const void *w_up,
                    const void *w_down, const float *topk_w, const int32_t *offsets,
                    const int32_t *sorted_to_flat, const int32_t *flat_to_sorted, void *y,
@@ -128,7 +129,8 @@ moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, cons
  *   dw_down   device fp32 [E, D, I] out: dL/dW_down
  *   d_topk_w  device fp32 [T, K]   out: dL/dtopk_w[t,k] = <dy[t], o[t,k]>
  *   accumulate_dw  0: overwrite dw_*;  1: add into dw_* (fp32)
- * The gate/up activations are recomputed (not read from the forward).  Each
+ * The gate/up activations are recomputed (not read from the forward); the
+ * routed rows of x and dy are gathered inside the GEMMs' operand loads.  Each
  * weight-gradient tile is produced by one workgroup that walks all of its
  * expert's rows (no atomics); experts with no rows get exact zeros (or are
  * left unchanged when accumulating).

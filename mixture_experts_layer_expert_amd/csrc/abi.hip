@@ -60,13 +60,14 @@ struct Carve {
 
 struct FwdWs {
   int32_t* tstart;
-  bf16_t *xs, *h, *o;
+  bf16_t *h, *o;
 };
 struct BwdWs {
   int32_t* tstart;
   bf16_t *xs, *dou;
   f16_t *dgu, *hw;        // fp16 operands of the gradient GEMMs (rounded values)
   f16_t *dgu_lo, *hw_lo;  // their low parts (value - rounded value), for the dW GEMMs
+  uint32_t* rowoff;       // byte offset of each routed row's token row in x / dy
   float *gu, *dxs, *part;
 };
 
@@ -86,7 +87,6 @@ size_t fwd_ws(const moe_dims& d, FwdWs* w, void* base) {
   Carve c{(char*)base};
   const size_t R = (size_t)d.T * d.K;
   w->tstart = c.take<int32_t>(d.E + 1);
-  w->xs = c.take<bf16_t>(R * d.D);
   w->h = c.take<bf16_t>(R * d.I);
   w->o = c.take<bf16_t>(R * d.D);
   return c.used;
@@ -96,8 +96,10 @@ size_t bwd_ws(const moe_dims& d, BwdWs* w, void* base) {
   Carve c{(char*)base};
   const size_t R = (size_t)d.T * d.K;
   w->tstart = c.take<int32_t>(d.E + 1);
-  w->xs = c.take<bf16_t>(R * d.D);
-  w->dou = c.take<bf16_t>(R * d.D);
+  // routed rows in expert order, only where the dW GEMMs cannot gather them
+  w->xs = kGemmGatherDw ? nullptr : c.take<bf16_t>(R * d.D);
+  w->dou = kGemmGatherDw ? nullptr : c.take<bf16_t>(R * d.D);
+  w->rowoff = kGemmGatherDw ? c.take<uint32_t>(std::max<size_t>(1, R)) : nullptr;
   w->gu = c.take<float>(R * 2 * d.I);
   w->dgu = c.take<f16_t>(R * 2 * d.I);
   w->hw = c.take<f16_t>(R * d.I);
@@ -226,15 +228,18 @@ MOE_EXPORT moe_status moe_fwd(const moe_dims* dims, const void* x, const void* w
   hipStream_t st = (hipStream_t)stream;
   clear_stale_error();
 
-  MOE_TRY(launch_gather(x, nullptr, w.xs, nullptr, sorted_to_flat, (int)R, d.K, d.D, st));
   MOE_TRY(launch_tilemap(offsets, d.E, kGemmBM, w.tstart, st));
 
   GemmArgs g{};
   g.offsets = offsets;
   g.tstart = w.tstart;
   g.E = d.E;
-  // gate/up + SwiGLU: H[R, I] = silu(Xs Wg^T) * (Xs Wu^T)
-  g.A = w.xs;
+  // gate/up + SwiGLU: H[R, I] = silu(Xs Wg^T) * (Xs Wu^T), the routed rows Xs
+  // gathered from x inside the GEMM's operand loads
+  g.A = (const bf16_t*)x;
+  g.a_gather = sorted_to_flat;
+  g.a_div = d.K;
+  g.a_rows = d.T;
   g.lda = d.D;
   g.B0 = (const bf16_t*)w_gate;
   g.B1 = (const bf16_t*)w_up;
@@ -249,6 +254,7 @@ MOE_EXPORT moe_status moe_fwd(const moe_dims* dims, const void* x, const void* w
   g.A = w.h;
   g.lda = d.I;
   g.B0 = (const bf16_t*)w_down;
+  g.a_gather = nullptr;
   g.B1 = nullptr;
   g.ldb = d.I;
   g.N = d.D;
@@ -286,8 +292,12 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   clear_stale_error();
 
   if (R > 0) {
-    // routed output gradients and the re-gathered inputs, in expert order
-    MOE_TRY(launch_gather(x, dy, w.xs, w.dou, sorted_to_flat, (int)R, d.K, d.D, st));
+    // routed output gradients and the re-gathered inputs, in expert order (only
+    // where the dW GEMMs cannot gather them; the row-grouped GEMMs always do)
+    if (kGemmGatherDw)
+      MOE_TRY(launch_row_offsets(sorted_to_flat, (int)R, d.K, (uint32_t)d.D * 2u, w.rowoff, st));
+    else
+      MOE_TRY(launch_gather(x, dy, w.xs, w.dou, sorted_to_flat, (int)R, d.K, d.D, st));
     MOE_TRY(launch_tilemap(offsets, d.E, kGemmBM, w.tstart, st));
   }
   GemmArgs g{};
@@ -295,8 +305,11 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   g.tstart = w.tstart;
   g.E = d.E;
   if (R > 0) {
-    // recompute G, U (fp32) into GU[R, 2I]
-    g.A = w.xs;
+    // recompute G, U (fp32) into GU[R, 2I], the routed rows gathered from x
+    g.A = (const bf16_t*)x;
+    g.a_gather = sorted_to_flat;
+    g.a_div = d.K;
+    g.a_rows = d.T;
     g.lda = d.D;
     g.B0 = (const bf16_t*)w_gate;
     g.B1 = (const bf16_t*)w_up;
@@ -313,7 +326,10 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
     g.offsets = offsets;
     g.tstart = w.tstart;
     g.E = d.E;
-    g.A = w.dou;
+    g.A = (const bf16_t*)dy;  // dOu: the routed rows gathered from dy
+    g.a_gather = sorted_to_flat;
+    g.a_div = d.K;
+    g.a_rows = d.T;
     g.lda = d.D;
     g.B0 = (const bf16_t*)w_down;
     g.ldb = d.I;
@@ -357,7 +373,13 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   g = GemmArgs{};
   g.offsets = offsets;
   g.E = d.E;
-  g.A = w.dou;
+  if (kGemmGatherDw) {
+    g.A = (const bf16_t*)dy;
+    g.a_rowoff = w.rowoff;
+    g.a_rows = d.T;
+  } else {
+    g.A = w.dou;
+  }
   g.lda = d.D;
   g.B0 = w.hw;
   g.ldb = d.I;
@@ -373,8 +395,15 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   // dW_gate[e] = dG_e^T Xs_e, dW_up[e] = dU_e^T Xs_e   ([I, D])
   g.A = w.dgu;
   g.A2 = w.dgu + d.I;
+  g.a_rowoff = nullptr;
   g.lda = 2 * d.I;
-  g.B0 = w.xs;
+  if (kGemmGatherDw) {
+    g.B0 = (const bf16_t*)x;
+    g.b_rowoff = w.rowoff;
+    g.b_rows = d.T;
+  } else {
+    g.B0 = w.xs;
+  }
   g.ldb = d.D;
   g.M = d.I;
   g.N = d.D;

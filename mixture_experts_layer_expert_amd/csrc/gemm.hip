@@ -86,6 +86,17 @@ static_assert(PREFETCH == 0 || (NS == 2 && BK == 64 && BM == 256 && BN == 256 &&
               "the L2 prefetch covers a 256 x 256 x 64 stage with 8 waves, double-buffered");
 static_assert(NS * STAGE_BYTES + (PREFETCH ? NW * 256 : 0) <= 160 * 1024, "LDS budget");
 
+// Weight-gradient GEMMs with a gathered operand read its k-rows (routed rows)
+// through their token index.  The indices of an expert's rows pass through a
+// ring of RING_SLOTS chunks of RING_ROWS indices in LDS: chunk q is loaded
+// (one 4-byte-per-lane DMA per wave) three stages before its first use, into
+// slot q % RING_SLOTS, which no stage in flight still reads.
+constexpr int RING_ROWS = NW * 64, RING_SLOTS = 3;
+constexpr int RING_BYTES = RING_SLOTS * RING_ROWS * 4;
+constexpr int RING_STAGES = RING_ROWS / BK;  // stages per chunk
+static_assert(NS * STAGE_BYTES + (PREFETCH ? NW * 256 : 0) + RING_BYTES <= 160 * 1024,
+              "LDS budget with the index ring");
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -113,7 +124,8 @@ __device__ __forceinline__ int swz_mn(int k) {
 
 // k-contiguous tile of ROWS rows x BK k (KROW-byte rows): this wave's
 // instructions j = wave + NW i each fill rows KRPI j .. KRPI j + KRPI - 1.
-// off(row) = byte offset of the row's k = 0 element.
+// off(i, row) = byte offset of the row's k = 0 element (row is the lane's row
+// of instruction i).
 template <int ROWS>
 constexpr int kmajor_instrs() { return ROWS / KRPI / NW; }
 
@@ -132,13 +144,14 @@ __device__ __forceinline__ void issue_kmajor(char* tile, int wave, int lane, uin
     const int j = wave + NW * i;
     const int row = KRPI * j + lane / KCH;
     const int c = (lane % KCH) ^ swz_k(row);
-    dma16(r, tile + j * 1024, off(row) + k0_bytes + c * 16);
+    dma16(r, tile + j * 1024, off(i, row) + k0_bytes + c * 16);
   }
 }
 
 // Row-contiguous tile of BK k-rows x C columns (C = 128 or 256): instruction j
 // fills k-rows j*KPI .. j*KPI + KPI - 1 (KPI = 512 / C).  Element (k, col) of
-// the tile comes from byte koff(k) + (col0 + col) * 2 of the operand.
+// the tile comes from byte koff(i, k) + (col0 + col) * 2 of the operand (k is
+// the lane's k-row of this wave's instruction i).
 template <int C>
 constexpr int mnmajor_instrs() { return BK / (512 / C) / NW; }
 
@@ -154,7 +167,7 @@ __device__ __forceinline__ void issue_mnmajor(char* tile, int wave, int lane, in
     const int j = wave + NW * i;
     const int k = j * KPI + lane / LPR;
     const int c = (lane % LPR) ^ swz_mn(k);
-    dma16(r, tile + j * 1024, koff(k) + (uint32_t)(col0 + c * 8) * 2u);
+    dma16(r, tile + j * 1024, koff(i, k) + (uint32_t)(col0 + c * 8) * 2u);
   }
 }
 
@@ -248,8 +261,9 @@ template <int MODE>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void grouped_gemm_kernel(
     GemmArgs p) {
   // NS stages, then (with L2 prefetch) 256 bytes per wave that the prefetch
-  // DMA writes and nothing reads
-  __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE_BYTES + (PREFETCH ? NW * 256 : 0)];
+  // DMA writes and nothing reads, then (kDW) the ring of gathered row indices
+  constexpr int kRingOff = NS * STAGE_BYTES + (PREFETCH ? NW * 256 : 0);
+  __shared__ __attribute__((aligned(1024))) char lds[kRingOff + (MODE == kDW ? RING_BYTES : 0)];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
@@ -330,6 +344,10 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       rB = make_rsrc(p.B0 + (size_t)e * (p.K / 2) * p.ldb, (size_t)(p.K / 2) * ldb2);
       rB2 = make_rsrc(p.B1 + (size_t)e * (p.K / 2) * p.ldb, (size_t)(p.K / 2) * ldb2);
     }
+    if (p.a_gather) {
+      rA = make_rsrc(p.A, (size_t)p.a_rows * lda2);
+      rA2 = rA;
+    }
   } else {
     const bf16_t* a = mat == 0 ? p.A : p.A2;
     const bf16_t* alo = mat == 0 ? p.A_lo : p.A2_lo;
@@ -338,36 +356,91 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     rA2 = make_rsrc((alo ? alo : a) + kbase * p.lda, abytes);
     rB = make_rsrc(p.B0 + kbase * p.ldb, bbytes);
     rB2 = make_rsrc((p.B_lo ? p.B_lo : p.B0) + kbase * p.ldb, bbytes);
+    // a gathered operand is addressed from the start of its token-major rows
+    if (kGemmGatherDw && p.a_rowoff) rA = rA2 = make_rsrc(a, (size_t)p.a_rows * lda2);
+    if (kGemmGatherDw && p.b_rowoff) rB = rB2 = make_rsrc(p.B0, (size_t)p.b_rows * ldb2);
+  }
+
+  // ---------------------------------------------------------------- kDW gathered operand
+  // ga / gb: A / B k-rows are gathered (wave-uniform).  gofs[i]: byte offset of
+  // the token row behind this lane's k-row of load instruction i of the next
+  // stage; gtouch: the same for the row this lane touches for the L2 prefetch.
+  const bool ga = kGemmGatherDw && !kRowGrouped && p.a_rowoff;
+  const bool gb = kGemmGatherDw && !kRowGrouped && p.b_rowoff;
+  constexpr int QG = mnmajor_instrs<BM>();
+  uint32_t gofs[QG] = {}, gtouch = 0;
+  char* const ring = lds + kRingOff;
+  const int nch = ceil_div(nk_pass, RING_STAGES);  // index chunks per pass over the rows
+  // chunk sequence number of stage kt (the second pass of a split restarts the rows)
+  auto chunk_q = [&](int kt) { return kt < nk_pass ? kt / RING_STAGES : nch + (kt - nk_pass) / RING_STAGES; };
+  const uint32_t* const gsrc = ga ? p.a_rowoff : gb ? p.b_rowoff : nullptr;
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(gsrc ? gsrc + kbase : nullptr,
+                                              gsrc ? (size_t)k_count * 4u : 0);
+  auto ring_load = [&](int q) __attribute__((always_inline)) {
+    const int rb = (q < nch ? q : q - nch) * RING_ROWS + wave * 64;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rS, LDS_PTR(void, ring + (q % RING_SLOTS) * (RING_ROWS * 4) + wave * 256), 4,
+        (uint32_t)(rb + lane) * 4u, 0, 0, 0);
+  };
+  // byte offset of the token row behind k-row k of stage kt (past the rows: a
+  // sentinel beyond every buffer, which reads zeros).  Branch-free, so that the
+  // index reads of a stage are issued together.
+  auto gtok = [&](int kt, int k) -> uint32_t {
+    const int kr = (kt < nk_pass ? kt : kt - nk_pass) * BK + k;
+    const uint32_t v = *(const uint32_t*)(ring + (chunk_q(kt) % RING_SLOTS) * (RING_ROWS * 4) +
+                                          (kr % RING_ROWS) * 4);
+    return kr < k_count ? v : 0x80000000u;
+  };
+  auto gather_offsets = [&](int kt_load, int kt_touch) __attribute__((always_inline)) {
+    constexpr int KPI = 512 / BM, LPR = BM / 8;
+#pragma unroll
+    for (int i = 0; i < QG; ++i) gofs[i] = gtok(kt_load, (wave + NW * i) * KPI + lane / LPR);
+    if (PREFETCH > 0) gtouch = gtok(min(kt_touch, nk - 1), ((wave % (NW / 2)) * 64 + lane) / (BM / 64));
+  };
+
+  // Row-grouped A: the byte offset of each A row this lane loads (one row per
+  // load instruction, fixed for the tile) and of the row it touches for the L2
+  // prefetch.  Gathered rows come straight from the token-major operand; rows
+  // past the expert's end get an offset beyond the buffer (they read zeros).
+  constexpr int QA = kRowGrouped ? kmajor_instrs<BM>() : mnmajor_instrs<BM>();
+  uint32_t aoff[QA], atouch = 0;
+  if constexpr (kRowGrouped) {
+    auto row_off = [&](int row) -> uint32_t {
+      if (!p.a_gather) return (uint32_t)row * lda2;
+      if (row >= rows_valid) return 0x80000000u;
+      return (uint32_t)(p.a_gather[m0 + row] / p.a_div) * lda2;
+    };
+#pragma unroll
+    for (int i = 0; i < QA; ++i) aoff[i] = row_off(KRPI * (wave + NW * i) + lane / KCH);
+    if (PREFETCH > 0 && wave < NW / 2) atouch = row_off(wave * 64 + lane);
   }
 
   // Loads of stage kt, pieces [q0, q1) of LOADS_PER_STAGE (A first, then B).
-  constexpr int QA = kRowGrouped ? kmajor_instrs<BM>() : mnmajor_instrs<BM>();
   auto issue = [&](int kt, int q0, int q1) __attribute__((always_inline)) {
     char* sa = lds + (kt % NS) * STAGE_BYTES;
     char* sb = sa + A_BYTES;
     if constexpr (kRowGrouped) {
       const uint32_t k0b = (uint32_t)kt * BK * 2u;
-      issue_kmajor<BM>(sa, wave, lane, k0b, [&](int row) { return (uint32_t)row * lda2; }, rA, 0, q0,
-                       q1);
+      issue_kmajor<BM>(sa, wave, lane, k0b, [&](int i, int) { return aoff[i]; }, rA, 0, q0, q1);
       if constexpr (kGateUp) {
         // B rows 0..BN/2-1: gate rows, BN/2..BN-1: the matching up rows
         constexpr int QG = kmajor_instrs<BN / 2>();
-        issue_kmajor<BN / 2>(sb, wave, lane, k0b, [&](int row) { return (uint32_t)row * ldb2; }, rB,
+        issue_kmajor<BN / 2>(sb, wave, lane, k0b, [&](int, int row) { return (uint32_t)row * ldb2; }, rB,
                              QA, q0, q1);
         issue_kmajor<BN / 2>(sb + (BN / 2) * BK * 2, wave, lane, k0b,
-                             [&](int row) { return (uint32_t)row * ldb2; }, rB2, QA + QG, q0, q1);
+                             [&](int, int row) { return (uint32_t)row * ldb2; }, rB2, QA + QG, q0, q1);
       } else if constexpr (MODE == kDown) {
-        issue_kmajor<BN>(sb, wave, lane, k0b, [&](int row) { return (uint32_t)row * ldb2; }, rB, QA,
+        issue_kmajor<BN>(sb, wave, lane, k0b, [&](int, int row) { return (uint32_t)row * ldb2; }, rB, QA,
                          q0, q1);
       } else if constexpr (MODE == kDA) {
         const int k0 = kt * BK;
-        issue_mnmajor<BN>(sb, wave, lane, n0, [&](int k) { return (uint32_t)(k0 + k) * ldb2; }, rB,
-                          QA, q0, q1);
+        issue_mnmajor<BN>(sb, wave, lane, n0, [&](int, int k) { return (uint32_t)(k0 + k) * ldb2; },
+                          rB, QA, q0, q1);
       } else {  // kDXs: k < I from Wg, k >= I from Wu
         const int half = p.K / 2, k0 = kt * BK;
         const bool up = k0 >= half;
         const int kr = up ? k0 - half : k0;
-        issue_mnmajor<BN>(sb, wave, lane, n0, [&](int k) { return (uint32_t)(kr + k) * ldb2; },
+        issue_mnmajor<BN>(sb, wave, lane, n0, [&](int, int k) { return (uint32_t)(kr + k) * ldb2; },
                           up ? rB2 : rB, QA, q0, q1);
       }
     } else {
@@ -375,10 +448,10 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       // split operand's low part against the same exact operand
       const bool lo_pass = kt >= nk_pass;
       const int k0 = (lo_pass ? kt - nk_pass : kt) * BK;
-      issue_mnmajor<BM>(sa, wave, lane, m0, [&](int k) { return (uint32_t)(k0 + k) * lda2; },
-                        lo_pass ? rA2 : rA, 0, q0, q1);
-      issue_mnmajor<BN>(sb, wave, lane, n0, [&](int k) { return (uint32_t)(k0 + k) * ldb2; },
-                        lo_pass ? rB2 : rB, QA, q0, q1);
+      issue_mnmajor<BM>(sa, wave, lane, m0, [&](int i, int k) {
+        return ga ? gofs[i] : (uint32_t)(k0 + k) * lda2; }, lo_pass ? rA2 : rA, 0, q0, q1);
+      issue_mnmajor<BN>(sb, wave, lane, n0, [&](int i, int k) {
+        return gb ? gofs[i] : (uint32_t)(k0 + k) * ldb2; }, lo_pass ? rB2 : rB, QA, q0, q1);
     }
   };
 
@@ -392,7 +465,8 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   auto touch_stage = [](int kt, int nk_, int nk_pass_, char* dst, int wave_, int lane_,
                         __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t ra2,
                         __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rb2, uint32_t lda2_,
-                        uint32_t ldb2_, int m0_, int n0_, int K_) __attribute__((always_inline)) {
+                        uint32_t ldb2_, int m0_, int n0_, int K_, uint32_t atouch_, bool ga_,
+                        bool gb_, uint32_t gtouch_) __attribute__((always_inline)) {
     kt = min(kt, nk_ - 1);
     const int h = NW / 2;  // waves per operand
     const bool opa = wave_ < h;
@@ -403,7 +477,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       const uint32_t k0b = (uint32_t)kt * BK * 2u;
       if (opa) {
         r = ra;
-        off = (uint32_t)L * lda2_ + k0b;
+        off = atouch_ + k0b;
       } else if constexpr (kGateUp) {
         const bool up = (wave_ - h) * 64 >= BN / 2;  // wave-uniform
         r = up ? rb2 : rb;
@@ -429,17 +503,18 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       constexpr int LPA = BM / 64, LPB = BN / 64;
       if (opa) {
         r = lo_pass ? ra2 : ra;
-        off = (uint32_t)(k0 + L / LPA) * lda2_ + (uint32_t)(m0_ + (L % LPA) * 64) * 2u;
+        off = (ga_ ? gtouch_ : (uint32_t)(k0 + L / LPA) * lda2_) + (uint32_t)(m0_ + (L % LPA) * 64) * 2u;
       } else {
         r = lo_pass ? rb2 : rb;
-        off = (uint32_t)(k0 + L / LPB) * ldb2_ + (uint32_t)(n0_ + (L % LPB) * 64) * 2u;
+        off = (gb_ ? gtouch_ : (uint32_t)(k0 + L / LPB) * ldb2_) + (uint32_t)(n0_ + (L % LPB) * 64) * 2u;
       }
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, dst), 4, off, 0, 0, 0);
   };
   char* const touch_dst = lds + NS * STAGE_BYTES + wave * 256;
   auto touch = [&](int kt) __attribute__((always_inline)) {
-    touch_stage(kt, nk, nk_pass, touch_dst, wave, lane, rA, rA2, rB, rB2, lda2, ldb2, m0, n0, p.K);
+    touch_stage(kt, nk, nk_pass, touch_dst, wave, lane, rA, rA2, rB, rB2, lda2, ldb2, m0, n0, p.K,
+                atouch, ga, gb, gtouch);
   };
 
   f32x4 acc[FM][FN];
@@ -459,6 +534,17 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   static_assert(LOADS_PER_SLOT * LOAD_SLOTS == LOADS_PER_STAGE &&
                     (LOAD_SLOTS - 1) * LOAD_STRIDE + (PREFETCH > 0 ? 1 : 0) < SLOTS,
                 "load slots must split the stage's loads evenly and fit the MFMA rows");
+  if constexpr (!kRowGrouped) {
+    if ((ga || gb) && nk > 0) {
+      // the index chunks of stages 0..2, then everyone's chunks are in LDS
+      for (int s = 0; s < 3 && s < nk; ++s)
+        if (s == 0 || chunk_q(s) != chunk_q(s - 1)) ring_load(chunk_q(s));
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      gather_offsets(0, PREFETCH);
+    }
+  }
   if constexpr (PREFETCH > 0) {
     if (nk > 0) {
 #pragma unroll
@@ -486,6 +572,14 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     }
     __builtin_amdgcn_s_barrier();  // every wave's part of stage kt is in LDS, and
     asm volatile("" ::: "memory");  // every wave is done reading stage kt - 1
+    if constexpr (!kRowGrouped && kMore) {
+      if (ga || gb) {
+        // load the index chunk that stage kt + 3 starts, if it starts one; read
+        // the indices of the next stage's loads and of the prefetch touch
+        if (kt + 3 < nk && chunk_q(kt + 3) != chunk_q(kt + 2)) ring_load(chunk_q(kt + 3));
+        gather_offsets(kt + 1, kt + 1 + PREFETCH);
+      }
+    }
     if (!wave_rows) {
       // all of this wave's rows are padding: it only moves its share of the
       // next stage (and the prefetch)

@@ -11,7 +11,7 @@ enum KernelId : int {
   kKRouteTopk, kKRouteHist, kKRouteScan, kKRouteScatter, kKTilemap, kKGather,
   kKGemmGateUpH, kKGemmGateUpGU, kKGemmDown, kKGemmDA, kKGemmDXs, kKGemmDWDown,
   kKGemmDWGateUp, kKCombine, kKReduceRows, kKReducePartials, kKGather2, kKRouterLogits,
-  kKRouterPrep, kKRouterDx, kKRouterDwr, kKRouterDwrSum, kNumKernels
+  kKRouterPrep, kKRouterDx, kKRouterDwr, kKRouterDwrSum, kKRowOffsets, kNumKernels
 };
 namespace prof {
 void begin(int kid, hipStream_t st);  // no-ops unless timing is enabled
@@ -45,6 +45,9 @@ hipError_t launch_combine(const void* O, const float* w, const int32_t* f2s, voi
 hipError_t launch_reduce_rows(const void* dXs, void* dx, int T, int K, int D, hipStream_t st);
 hipError_t launch_reduce_partials(const float* part, const int32_t* f2s, float* out, int R,
                                   int np, hipStream_t st);
+// rowoff[p] = (sorted_to_flat[p] / K) * row_bytes: byte offset of routed row p's token row
+hipError_t launch_row_offsets(const int32_t* s2f, int R, int K, uint32_t row_bytes,
+                              uint32_t* rowoff, hipStream_t st);
 
 // ---- router projection and router backward (router.hip)
 hipError_t launch_router_logits(const void* x, const float* w_r, float* logits, int T, int D,
@@ -99,6 +102,10 @@ constexpr int kGemmBK = MOE_GEMM_BK;  // reduction depth of one LDS stage (32 or
 constexpr int kGemmWM = MOE_GEMM_WM;  // waves along the rows
 constexpr int kGemmWN = MOE_GEMM_WN;  // waves along the columns
 constexpr int kGemmNS = MOE_GEMM_NS;  // K stages resident in LDS
+// The weight-gradient GEMMs can gather a token-major operand inside their
+// loads (square tiles, double-buffered stages); otherwise the backward first
+// copies the routed rows into expert order.
+constexpr bool kGemmGatherDw = kGemmBM == kGemmBN && kGemmNS == 2;
 
 enum GemmMode : int {
   kGateUpH = 0,   // H  = silu(Xs Wg^T) * (Xs Wu^T)                       bf16 [R, I]
@@ -112,6 +119,15 @@ enum GemmMode : int {
 
 struct GemmArgs {
   const bf16_t* A;   // row-grouped modes: [R, lda] K-major.  kDW: token-major [R, lda]
+  // Row-grouped modes: if non-null, routed row p of A is row a_gather[p] / a_div
+  // of the token-major A [a_rows, lda]: the gather is folded into the loads.
+  const int32_t* a_gather;
+  int a_div, a_rows;
+  // kDW: if non-null, k-row p of A (B) lies at byte a_rowoff[p] (b_rowoff[p]) of
+  // the token-major operand [a_rows (b_rows), ld]; at most one is gathered.
+  const uint32_t* a_rowoff;
+  const uint32_t* b_rowoff;
+  int b_rows;
   const bf16_t* A2;  // kDW second matrix's A (dW_up), else unused
   const bf16_t* B0;  // weights (row-grouped) or token-major activations (kDW)
   const bf16_t* B1;  // up weights (kGateUp*, kDXs)

@@ -125,6 +125,22 @@ __global__ __launch_bounds__(kPermuteThreads) void reduce_partials_kernel(
   }
 }
 
+// rowoff[p] = (s2f[p] / K) * row_bytes
+__global__ __launch_bounds__(kPermuteThreads) void row_offsets_kernel(
+    const int32_t* __restrict__ s2f, int R, int K, uint32_t row_bytes, uint32_t* __restrict__ out) {
+  for (int p = blockIdx.x * kPermuteThreads + threadIdx.x; p < R;
+       p += gridDim.x * kPermuteThreads)
+    out[p] = (uint32_t)(s2f[p] / K) * row_bytes;
+}
+
+hipError_t launch_row_offsets(const int32_t* s2f, int R, int K, uint32_t row_bytes,
+                              uint32_t* rowoff, hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  MOE_LAUNCH(kKRowOffsets, row_offsets_kernel, dim3(grid_for((size_t)R)), dim3(kPermuteThreads), 0,
+             st, s2f, R, K, row_bytes, rowoff);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather(const void* src0, const void* src1, void* dst0, void* dst1,
                          const int32_t* s2f, int R, int K, int D, hipStream_t st) {
   const int cpr = D / 8;
