@@ -634,6 +634,11 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
         // keep the order: this slot's loads, then its row of MFMAs
         if (loads_here) __builtin_amdgcn_sched_group_barrier(0x020, LOADS_PER_SLOT, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);
+        // raised issue priority between MFMA rows, normal after the stage's last
+        // row, so the other wave on the SIMD reads its fragments meanwhile
+        // (measured: -0.6% per step)
+        if (i == FM - 1) __builtin_amdgcn_s_setprio(0);
+        else __builtin_amdgcn_s_setprio(1);
         if constexpr (PREFETCH > 0) {
           if (kMore && slot == (LOAD_SLOTS - 1) * LOAD_STRIDE + 1) {
             touch(kt + NS - 1 + PREFETCH);  // the stage's last memory instruction
