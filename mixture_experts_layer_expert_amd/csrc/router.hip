@@ -12,8 +12,9 @@
 // E, top-K, renormalise), or the sigmoid of each selected logit.
 //
 // Kernels:
-//   router_logits  dense x [T,D] (bf16) x W_r [D,E] (fp32) on the fp32 matrix
-//                  cores (v_mfma_f32_16x16x4_f32), 64 x 64 tiles, LDS-staged;
+//   router_logits  dense x [T,D] (bf16) x W_r [D,E] (fp32) on the bf16 matrix
+//                  cores: W_r is split into three bf16 terms (exact), so the
+//                  three MFMA passes accumulate exact fp32 products in fp32;
 //   router_prep    dl per routed slot, and W_r transposed to [E, D];
 //   router_dx      dX[t] += sum_k dl[t,k] W_r[:, idx[t,k]]   (fp32, k ascending,
 //                  one rounding of the sum into the bf16 dX);
@@ -30,87 +31,130 @@ namespace {
 
 constexpr int kRTile = 64;  // tokens x experts per logits workgroup
 constexpr int kRBK = 32;    // d per stage
-constexpr int kAPitch = kRBK + 4;     // floats; conflict-free fragment reads
 constexpr int kBPitch = kRTile + 16;  // floats
 
-// logits[t, e] = sum_d x[t, d] w_r[d, e].  256 threads = 4 waves in 2 x 2,
-// each wave 32 x 32 = 2 x 2 fragments of 16 x 16.  Fragment lanes (verified on
-// gfx950): A lane l = A[l % 16][l / 16], B lane l = B[l / 16][l % 16], result
-// register j of lane l = C[4 (l / 16) + j][l % 16].
+// logits[t, e] = sum_d x[t, d] w_r[d, e] on the bf16 matrix cores.
+// Each fp32 weight is split into three bf16 terms, w = w0 + w1 + w2 with
+// w0 = bf16(w), w1 = bf16(w - w0), w2 = w - w0 - w1 (round to nearest even;
+// every difference is exact and w2 has at most 8 significant bits, so the
+// split is exact for normal values).  x is bf16, so each product x * wi is
+// exact in fp32, and the three MFMA passes accumulate the exact products of x
+// and w in fp32: the precision of an fp32 product, at the bf16 rate.
+// Workgroup: 64 tokens x 64 experts, 4 waves of 16 tokens x 64 experts (4
+// fragments of v_mfma_f32_16x16x32_bf16 per split).  Stages of 64 d: the
+// waves load the stage's W_r block (fp32, 64 d x 64 experts, coalesced along
+// the experts), split it and store it in LDS as k-contiguous bf16 rows per
+// expert (double-buffered); x fragments come straight from global memory.
+constexpr int kLT = 64, kLE = 64, kLK = 64;
+constexpr int kLPitch = kLK * 2 + 16;              // bytes per staged expert row
+constexpr int kLSplit = kLE * kLPitch;             // one split's block
+constexpr int kLStage = 3 * kLSplit;               // one stage (27648 bytes)
+constexpr int kLDPW = kLK / 4;                     // d per wave when staging (16)
+
 __global__ __launch_bounds__(256) void router_logits_kernel(const bf16_t* __restrict__ x,
                                                             const float* __restrict__ w_r,
                                                             float* __restrict__ logits, int T,
                                                             int D, int E) {
-  __shared__ float As[kRTile * kAPitch];
-  __shared__ float Bs[kRBK * kBPitch];
+  __shared__ __attribute__((aligned(16))) char Bs[2 * kLStage];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int t0 = blockIdx.x * kRTile, e0 = blockIdx.y * kRTile;
-  f32x4 acc[2][2];
+  const int t0 = blockIdx.x * kLT, e0 = blockIdx.y * kLE;
+  // staging: this thread owns expert e0 + lane and d = d0 + 16 wave .. + 15
+  const int se = e0 + lane;
+  float wv[kLDPW];
+  auto load_w = [&](int d0) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < kLDPW; ++j) {
+      const int d = d0 + wave * kLDPW + j;
+      wv[j] = se < E && d < D ? w_r[(size_t)d * E + se] : 0.0f;
+    }
+  };
+  auto store_w = [&](int buf) __attribute__((always_inline)) {
+    char* row = Bs + buf * kLStage + lane * kLPitch + wave * kLDPW * 2;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int d0 = 0; d0 < D; d0 += kRBK) {
-    {  // A: 64 rows x 32 d bf16 -> fp32; thread = one row's 8-element chunk
-      const int r = tid >> 2, c = (tid & 3) * 8;
-      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (t0 + r < T) {
-        const u32x4 q = *(const u32x4*)(x + (size_t)(t0 + r) * D + d0 + c);
+    for (int c = 0; c < kLDPW / 8; ++c) {
+      u32x4 h0, h1, h2;
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          v[2 * h] = bf16_lo(q[h]);
-          v[2 * h + 1] = bf16_hi(q[h]);
+      for (int q = 0; q < 4; ++q) {
+        uint32_t t0b[2], t1b[2], t2b[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float w = wv[c * 8 + 2 * q + h];
+          t0b[h] = f32_to_bf16(w);
+          const float r1 = w - bf16_to_f32(t0b[h]);
+          t1b[h] = f32_to_bf16(r1);
+          t2b[h] = f32_to_bf16(r1 - bf16_to_f32(t1b[h]));
+        }
+        h0[q] = t0b[0] | (t0b[1] << 16);
+        h1[q] = t1b[0] | (t1b[1] << 16);
+        h2[q] = t2b[0] | (t2b[1] << 16);
+      }
+      *(u32x4*)(row + c * 16) = h0;
+      *(u32x4*)(row + kLSplit + c * 16) = h1;
+      *(u32x4*)(row + 2 * kLSplit + c * 16) = h2;
+    }
+  };
+  // x fragment of k-step kk: lane l holds token row t0 + 16 wave + l % 16 and
+  // d = d0 + kk + 8 (l / 16) .. + 7
+  const int xt = t0 + wave * 16 + (lane & 15);
+  auto load_x = [&](int d) -> bf16x8 {
+    u32x4 q = {0u, 0u, 0u, 0u};  // D is a multiple of 64: a 16-byte chunk is all in or all out
+    if (xt < T && d < D) q = *(const u32x4*)(x + (size_t)xt * D + d + 8 * (lane >> 4));
+    return __builtin_bit_cast(bf16x8, q);
+  };
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nst = (D + kLK - 1) / kLK;  // a last partial stage reads zeros past D
+  load_w(0);
+  store_w(0);
+  bf16x8 xa[kLK / 32], xn[kLK / 32];
+#pragma unroll
+  for (int s = 0; s < kLK / 32; ++s) xa[s] = load_x(s * 32);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const bool more = st + 1 < nst;
+    if (more) {
+      load_w((st + 1) * kLK);
+#pragma unroll
+      for (int s = 0; s < kLK / 32; ++s) xn[s] = load_x((st + 1) * kLK + s * 32);
+    }
+    const char* b = Bs + (st & 1) * kLStage;
+#pragma unroll
+    for (int s = 0; s < kLK / 32; ++s) {
+#pragma unroll
+      for (int sp = 0; sp < 3; ++sp) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // B fragment: expert column 16 j + l % 16, k = 32 s + 8 (l / 16) .. + 7
+          const bf16x8 bw = *(const bf16x8*)(b + sp * kLSplit + (j * 16 + (lane & 15)) * kLPitch +
+                                             (s * 32 + 8 * (lane >> 4)) * 2);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw, xa[s], acc[j], 0, 0, 0);
         }
       }
-#pragma unroll
-      for (int h = 0; h < 8; ++h) As[r * kAPitch + c + h] = v[h];
     }
+    if (more) {
+      store_w((st + 1) & 1);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {  // B: 32 d-rows x 64 experts fp32, 4 per chunk
-      const int ch = tid + 256 * s;
-      const int k = ch >> 4, c = (ch & 15) * 4;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if ((E & 3) == 0 && e0 + c + 3 < E) {  // 16-byte aligned whole chunk
-        v = *(const f32x4*)(w_r + (size_t)(d0 + k) * E + e0 + c);
-      } else {
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-          if (e0 + c + h < E) v[h] = w_r[(size_t)(d0 + k) * E + e0 + c + h];
-      }
-#pragma unroll
-      for (int h = 0; h < 4; ++h) Bs[k * kBPitch + c + h] = v[h];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kRBK; kk += 4) {
-      float a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = As[(wm * 32 + i * 16 + (lane & 15)) * kAPitch + kk + (lane >> 4)];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = Bs[(kk + (lane >> 4)) * kBPitch + wn * 32 + j * 16 + (lane & 15)];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int s = 0; s < kLK / 32; ++s) xa[s] = xn[s];
     }
     __syncthreads();
   }
+  // lane l holds token row 16 wave + l % 16 and experts 16 j + 4 (l / 16) .. + 3
+  const int t = t0 + wave * 16 + (lane & 15);
+  if (t < T) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + j * 16 + 4 * (lane >> 4);
+      float* o = logits + (size_t)t * E + e;
+      if ((E & 3) == 0 && e + 3 < E) {
+        *(f32x4*)o = acc[j];
+      } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int e = e0 + wn * 32 + j * 16 + (lane & 15);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int t = t0 + wm * 32 + i * 16 + 4 * (lane >> 4) + q;
-        if (t < T && e < E) logits[(size_t)t * E + e] = acc[i][j][q];
+        for (int q = 0; q < 4; ++q)
+          if (e + q < E) o[q] = acc[j][q];
       }
     }
+  }
 }
 
 // dl per routed slot f = t*K + k (selection fixed):
@@ -265,7 +309,7 @@ int blocks_for(size_t n, int cap) {
 hipError_t launch_router_logits(const void* x, const float* w_r, float* logits, int T, int D,
                                 int E, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  const dim3 grid((T + kRTile - 1) / kRTile, (E + kRTile - 1) / kRTile);
+  const dim3 grid((T + kLT - 1) / kLT, (E + kLE - 1) / kLE);
   MOE_LAUNCH(kKRouterLogits, router_logits_kernel, grid, dim3(256), 0, st, (const bf16_t*)x, w_r,
              logits, T, D, E);
   return hipGetLastError();
