@@ -41,7 +41,8 @@ __global__ __launch_bounds__(kPermuteThreads) void gather_rows_kernel(
 
 // y[t, :] = sum_{k<K} w[t,k] * O[flat_to_sorted[t*K+k], :]   (fp32, k ascending)
 // KT = K known at compile time (0: runtime K): all K row indices are read
-// first and all K row loads are then in flight together.
+// first and all K row loads are then in flight together.  O is read once
+// (non-temporal loads).
 template <int KT>
 __global__ __launch_bounds__(kPermuteThreads) void combine_kernel(
     const u32x4* __restrict__ O, const float* __restrict__ w, const int32_t* __restrict__ f2s,
@@ -70,11 +71,12 @@ __global__ __launch_bounds__(kPermuteThreads) void combine_kernel(
         wk[k] = w[t * KT + k];
       }
 #pragma unroll
-      for (int k = 0; k < KT; ++k) v[k] = O[(size_t)rows[k] * cpr + j];
+      for (int k = 0; k < KT; ++k) v[k] = __builtin_nontemporal_load(O + (size_t)rows[k] * cpr + j);
 #pragma unroll
       for (int k = 0; k < KT; ++k) add(wk[k], v[k]);
     } else {
-      for (int k = 0; k < K; ++k) add(w[t * K + k], O[(size_t)f2s[t * K + k] * cpr + j]);
+      for (int k = 0; k < K; ++k)
+        add(w[t * K + k], __builtin_nontemporal_load(O + (size_t)f2s[t * K + k] * cpr + j));
     }
     u32x4 out;
 #pragma unroll
