@@ -61,8 +61,10 @@ def kernel_work(wl: synth.Workload) -> dict:
         "reduce_rows": ("hbm", 4.0 * R * D + 4 * R + 2.0 * T * D),
         "reduce_partials": ("hbm", 4.0 * R * (2 * math.ceil(I / 256)) + 8 * R),
         "route_topk": ("hbm", 4.0 * T * E + 8 * R),
-        "route_hist": ("hbm", 4.0 * R), "route_scan": ("hbm", 8.0 * E),
-        "route_scatter": ("hbm", 12.0 * R), "tilemap": ("hbm", 8.0 * E),
+        "route_hist": ("hbm", 4.0 * R),
+        # scatter: read the ids (4R) and the histogram table once, write both permutations (8R)
+        "route_scatter": ("hbm", 12.0 * R + 4.0 * E * math.ceil(R / route_chunk(R))),
+        "tilemap": ("hbm", 8.0 * E),
         "row_offsets": ("hbm", 8.0 * R),
         # router projection and router backward (timed beside the step, not in it)
         "router_logits": ("mfma32", 2.0 * T * D * E), "router_dwr": ("mfma32", 2.0 * T * D * E),
@@ -70,6 +72,13 @@ def kernel_work(wl: synth.Workload) -> dict:
         "router_dx": ("hbm", 4.0 * T * D + 8 * R),
         "router_dwr_sum": ("hbm", 4.0 * D * E * (router_splits(T) + 1)),
     }
+
+
+def route_chunk(R: int) -> int:
+    """Flat slots per routing block (as the library chooses them)."""
+    per = (R + 255) // 256
+    per = (per + 63) // 64 * 64
+    return max(1024, per)
 
 
 def router_splits(T: int) -> int:

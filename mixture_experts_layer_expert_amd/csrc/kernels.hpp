@@ -8,7 +8,7 @@ namespace moe {
 
 // ---- per-kernel timing (prof.hip)
 enum KernelId : int {
-  kKRouteTopk, kKRouteHist, kKRouteScan, kKRouteScatter, kKTilemap, kKGather,
+  kKRouteTopk, kKRouteHist, kKRouteScatter, kKTilemap, kKGather,
   kKGemmGateUpH, kKGemmGateUpGU, kKGemmDown, kKGemmDA, kKGemmDXs, kKGemmDWDown,
   kKGemmDWGateUp, kKCombine, kKReduceRows, kKReducePartials, kKGather2, kKRouterLogits,
   kKRouterPrep, kKRouterDx, kKRouterDwr, kKRouterDwrSum, kKRowOffsets, kNumKernels

@@ -24,7 +24,7 @@ int open_kid = -1;
 hipEvent_t open_start = nullptr;
 
 const char* const kNames[kNumKernels] = {
-    "route_topk",   "route_hist",    "route_scan",    "route_scatter", "tilemap",
+    "route_topk",   "route_hist",    "route_scatter", "tilemap",
     "gather",       "gemm_gateup_h", "gemm_gateup_gu", "gemm_down",    "gemm_da",
     "gemm_dxs",     "gemm_dw_down",  "gemm_dw_gateup", "combine",      "reduce_rows",
     "reduce_partials", "gather2",   "router_logits", "router_prep",  "router_dx",

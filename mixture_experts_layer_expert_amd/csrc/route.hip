@@ -120,44 +120,58 @@ __device__ int block_exclusive_scan_1024(int v, int* total) {
   return before + incl - v;
 }
 
-// Single block of 1024 threads: in-place exclusive scan of hist ([E][nblk],
-// E*nblk entries) -> per-(expert, block) base rows; offsets[e] = base[e][0],
-// offsets[E] = R, counts[e] = offsets[e+1] - offsets[e].
-__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ hist, int E, int nblk,
-                                                    int R, int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets) {
-  const long n = (long)E * nblk;
-  const long per = (n + 1023) / 1024;
-  const long b0 = min(n, per * threadIdx.x), b1 = min(n, b0 + per);
-  int s = 0;
-  for (long i = b0; i < b1; ++i) s += hist[i];
-  int total;
-  int run = block_exclusive_scan_1024(s, &total);
-  for (long i = b0; i < b1; ++i) {
-    const int c = hist[i];
-    hist[i] = run;
-    if (nblk > 0 && i % nblk == 0) offsets[i / nblk] = run;
-    run += c;
-  }
-  if (nblk == 0)
-    for (int e = threadIdx.x; e < E; e += 1024) offsets[e] = 0;
-  if (threadIdx.x == 0) offsets[E] = R;
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 1024) counts[e] = offsets[e + 1] - offsets[e];
-}
-
 // Stable scatter, one wave per block (block b owns flat slots of chunk b and
-// walks them in order, 64 at a time).  Lanes holding the same expert are
-// found with one ballot per expert-id bit; a lane's rank among them is the
-// count of lower lanes in that group.  Running positions live in LDS.
+// walks them in order, 64 at a time).  The block first derives its own first
+// output row per expert from the per-block histograms: base(e, b) = (rows of
+// experts < e) + (rows of expert e in blocks < b); block 0 also writes counts
+// and offsets.  Lanes holding the same expert are found with one ballot per
+// expert-id bit; a lane's rank among them is the count of lower lanes in that
+// group.  Running positions live in LDS (run[0..E)), expert totals in
+// run[E..2E).
 __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ idx, int R, int E,
                                                      int chunk, int nblk,
-                                                     const int32_t* __restrict__ base,
+                                                     const int32_t* __restrict__ hist,
                                                      int32_t* __restrict__ s2f,
-                                                     int32_t* __restrict__ f2s) {
+                                                     int32_t* __restrict__ f2s,
+                                                     int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets) {
   extern __shared__ int run[];
+  int* const tot = run + E;
   const int b = blockIdx.x, lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) run[e] = base[(size_t)e * nblk + b];
+  for (int e = lane; e < E; e += 64) {
+    const int32_t* h = hist + (size_t)e * nblk;
+    int before = 0, all = 0;
+    for (int j = 0; j < nblk; ++j) {
+      const int c = h[j];
+      before += j < b ? c : 0;
+      all += c;
+    }
+    run[e] = before;
+    tot[e] = all;
+  }
+  __syncthreads();
+  // exclusive scan of the expert totals (E <= 1024), 64 experts per round
+  int carry = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    const int v = e < E ? tot[e] : 0;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (e < E) {
+      const int ex = carry + incl - v;
+      run[e] += ex;
+      if (b == 0) {
+        offsets[e] = ex;
+        counts[e] = v;
+      }
+    }
+    carry += __shfl(incl, 63);
+  }
+  if (b == 0 && lane == 0) offsets[E] = R;
   __syncthreads();
   const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
   const int fbeg = b * chunk, fend = min(R, fbeg + chunk);
@@ -230,11 +244,9 @@ hipError_t launch_route_sort(const moe_dims& d, const float* logits, int32_t* id
   if (nblk > 0)
     MOE_LAUNCH(kKRouteHist, hist_kernel, dim3(nblk), dim3(256), d.E * sizeof(int), st, idx, R,
                d.E, chunk, nblk, hist);
-  MOE_LAUNCH(kKRouteScan, scan_kernel, dim3(1), dim3(1024), 0, st, hist, d.E, nblk, R, counts,
-             offsets);
-  if (nblk > 0)
-    MOE_LAUNCH(kKRouteScatter, scatter_kernel, dim3(nblk), dim3(64), d.E * sizeof(int), st, idx,
-               R, d.E, chunk, nblk, hist, s2f, f2s);
+  // with no routed rows one scatter block still writes counts = 0 and offsets = 0
+  MOE_LAUNCH(kKRouteScatter, scatter_kernel, dim3(nblk > 0 ? nblk : 1), dim3(64),
+             2 * d.E * sizeof(int), st, idx, R, d.E, chunk, nblk, hist, s2f, f2s, counts, offsets);
   return hipGetLastError();
 }
 
