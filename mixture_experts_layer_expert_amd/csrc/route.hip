@@ -141,10 +141,25 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
   for (int e = lane; e < E; e += 64) {
     const int32_t* h = hist + (size_t)e * nblk;
     int before = 0, all = 0;
-    for (int j = 0; j < nblk; ++j) {
-      const int c = h[j];
-      before += j < b ? c : 0;
-      all += c;
+    if ((nblk & 3) == 0) {  // 16-byte rows of 4 blocks (the table is 16-byte aligned)
+      typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+      const i32x4* h4 = (const i32x4*)h;
+#pragma unroll 16
+      for (int j4 = 0; j4 < nblk / 4; ++j4) {
+        const i32x4 c = h4[j4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          before += 4 * j4 + q < b ? c[q] : 0;
+          all += c[q];
+        }
+      }
+    } else {
+#pragma unroll 8
+      for (int j = 0; j < nblk; ++j) {
+        const int c = h[j];
+        before += j < b ? c : 0;
+        all += c;
+      }
     }
     run[e] = before;
     tot[e] = all;
