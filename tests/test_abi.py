@@ -111,6 +111,17 @@ def test_router_bad_args(lib):
     assert need >= 4 * (64 * 4 + 16 * 2 + 64 * 4)    # W_r^T, dl, one partial of dW_r
 
 
+def test_missing_library_fails_loudly(tmp_path):
+    """No CPU fallback: a missing library is an error, not a silent substitute."""
+    saved = binding._lib
+    try:
+        binding._lib = None
+        with pytest.raises(binding.MoeError):
+            binding.load_library(str(tmp_path / "libmoe.so"))
+    finally:
+        binding._lib = saved
+
+
 def test_prof_names(lib):
     n = lib.moe_prof_num_kernels()
     names = [lib.moe_prof_kernel_name(i) for i in range(n)]

@@ -88,6 +88,10 @@ SMALL = {
     "sigmoid_top1": lambda: _custom(T=257, D=192, I=128, E=4, K=1, score=1, seed=106),
     # one token
     "one_token": lambda: _custom(T=1, D=64, I=64, E=8, K=2, score=0, seed=107),
+    # the maximum expert count: 1024 experts, most of them empty
+    "e1024": lambda: _custom(T=200, D=64, I=64, E=1024, K=8, score=0, seed=110),
+    # the maximum K (64 routed copies per token)
+    "k64": lambda: _custom(T=40, D=64, I=64, E=128, K=64, score=0, seed=111),
 }
 
 
