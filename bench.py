@@ -41,7 +41,9 @@ PEAK_FP32_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
 PEAK_HBM_GBPS = 8000.0
 
 WORKLOADS = {"qwen3_30b_a3b": synth.QWEN3_30B_A3B, "llama4_scout": synth.LLAMA4_SCOUT,
-             "tiny": synth.TINY}
+             "tiny": synth.TINY,
+             # the Qwen shape with Zipf(1.2)-skewed routing over the token counts of a sweep
+             **{f"qwen3_30b_a3b_zipf_T{T}": synth.qwen_zipf(T) for T in synth.ZIPF_SWEEP_T}}
 
 
 def kernel_work(wl: synth.Workload) -> dict:
