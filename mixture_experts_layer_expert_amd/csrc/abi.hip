@@ -40,6 +40,9 @@ moe_status check_dims(const moe_dims* d) {
   const int64_t mt = (R + (int64_t)d->E * (kGemmBM - 1)) / kGemmBM;
   const int64_t nt = std::max<int64_t>(gateup_tiles(d->I), (d->D + kGemmBN - 1) / kGemmBN);
   if (mt * nt >= (int64_t(1) << 31) - 8) return MOE_ERR_UNSUPPORTED;
+  const int64_t dwt = 2 * ((d->I + kGemmBM - 1) / kGemmBM) * ((d->D + kGemmBN - 1) / kGemmBN) *
+                      (d->E + (R + kDwChunkRows - 1) / kDwChunkRows);
+  if (dwt >= (int64_t(1) << 31) - 8) return MOE_ERR_UNSUPPORTED;
   // the GEMMs address token-major operands with 32-bit buffer offsets
   if (R * std::max<int64_t>(d->D, 2 * (int64_t)d->I) * 2 >= (int64_t(1) << 31) ||
       (int64_t)d->I * d->D * 2 >= (int64_t(1) << 31))
@@ -68,8 +71,21 @@ struct BwdWs {
   f16_t *dgu, *hw;        // fp16 operands of the gradient GEMMs (rounded values)
   f16_t *dgu_lo, *hw_lo;  // their low parts (value - rounded value), for the dW GEMMs
   uint32_t* rowoff;       // byte offset of each routed row's token row in x / dy
+  int32_t *cstart, *pstart, *slist;  // dW row-chunk map
+  float* dw_part;         // partial dW tiles of chunks 1.. of the chunked experts
   float *gu, *dxs, *part;
 };
+
+// dW row chunks: experts with more than kDwChunkRows rows (at most R / (chunk + 1)
+// of them), the partial tiles of their chunks 1.. (fewer than R / chunk in all),
+// and an upper bound on the chunk count (E + that)
+int64_t dw_max_chunked(const moe_dims& d) {
+  return std::min<int64_t>(d.E, (int64_t)d.T * d.K / (kDwChunkRows + 1));
+}
+int64_t dw_part_slots(const moe_dims& d) {
+  return ((int64_t)d.T * d.K + kDwChunkRows - 1) / kDwChunkRows;
+}
+int64_t dw_chunks_bound(const moe_dims& d) { return d.E + dw_part_slots(d); }
 
 // router-weight-gradient partials per routed row: one per (column tile, wave column)
 int partials_per_row(const moe_dims& d) { return kGemmWN * ((d.I + kGemmBN - 1) / kGemmBN); }
@@ -100,6 +116,10 @@ size_t bwd_ws(const moe_dims& d, BwdWs* w, void* base) {
   w->xs = kGemmGatherDw ? nullptr : c.take<bf16_t>(R * d.D);
   w->dou = kGemmGatherDw ? nullptr : c.take<bf16_t>(R * d.D);
   w->rowoff = kGemmGatherDw ? c.take<uint32_t>(std::max<size_t>(1, R)) : nullptr;
+  w->cstart = c.take<int32_t>(d.E + 1);
+  w->pstart = c.take<int32_t>(d.E);
+  w->slist = c.take<int32_t>(d.E + 1);
+  w->dw_part = c.take<float>(std::max<size_t>(1, (size_t)dw_part_slots(d) * 2 * d.I * d.D));
   w->gu = c.take<float>(R * 2 * d.I);
   w->dgu = c.take<f16_t>(R * 2 * d.I);
   w->hw = c.take<f16_t>(R * d.I);
@@ -131,10 +151,12 @@ int rowgrouped_grid(const moe_dims& d, int n_tiles) {
   return (int)((tiles + kNumXcd - 1) / kNumXcd * kNumXcd);
 }
 
-int dw_grid(int nmat, int E, int M, int N) {
-  const int64_t tiles = (int64_t)nmat * E * ((M + kGemmBM - 1) / kGemmBM) *
-                        ((N + kGemmBN - 1) / kGemmBN);
-  return (int)((tiles + kNumXcd - 1) / kNumXcd * kNumXcd);
+// dW grid: (matrix, row chunk) groups of m-tiles x n-tiles, dealt round-robin
+// to the XCDs; enough workgroups per XCD for its share of the chunk bound
+int dw_grid(int nmat, int64_t chunks, int M, int N) {
+  const int64_t per_c = (int64_t)((M + kGemmBM - 1) / kGemmBM) * ((N + kGemmBN - 1) / kGemmBN);
+  const int64_t groups = (int64_t)nmat * chunks;
+  return (int)((groups + kNumXcd - 1) / kNumXcd * per_c * kNumXcd);
 }
 
 thread_local char last_error[256] = "";
@@ -369,10 +391,16 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
     g.cvt_b = 1;  // weights bf16 -> fp16
     MOE_TRY(launch_gemm(kDXs, g, rowgrouped_grid(d, g.n_tiles), st));
   }
-  // dW_down[e] = dOu_e^T Hw_e   ([D, I], reduction over the expert's rows)
+  // dW_down[e] = dOu_e^T Hw_e   ([D, I], reduction over the expert's rows, in
+  // row chunks of at most kDwChunkRows)
+  MOE_TRY(launch_dw_chunkmap(offsets, d.E, w.cstart, w.pstart, w.slist, st));
+  const int max_chunked = (int)dw_max_chunked(d);
   g = GemmArgs{};
   g.offsets = offsets;
   g.E = d.E;
+  g.cstart = w.cstart;
+  g.pstart = w.pstart;
+  g.dw_part = w.dw_part;
   if (kGemmGatherDw) {
     g.A = (const bf16_t*)dy;
     g.a_rowoff = w.rowoff;
@@ -391,7 +419,9 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   g.B_lo = w.hw_lo;
   g.Cf = dw_down;
   g.accumulate = accumulate_dw;
-  MOE_TRY(launch_gemm(kDW, g, dw_grid(1, d.E, d.D, d.I), st));
+  MOE_TRY(launch_gemm(kDW, g, dw_grid(1, dw_chunks_bound(d), d.D, d.I), st));
+  MOE_TRY(launch_dw_reduce(w.dw_part, w.slist, w.pstart, w.cstart, dw_down, nullptr, 1, d.D, d.I,
+                           d.E, max_chunked, st));
   // dW_gate[e] = dG_e^T Xs_e, dW_up[e] = dU_e^T Xs_e   ([I, D])
   g.A = w.dgu;
   g.A2 = w.dgu + d.I;
@@ -415,7 +445,9 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   g.B_lo = nullptr;
   g.Cf = dw_gate;
   g.Cf2 = dw_up;
-  MOE_TRY(launch_gemm(kDW, g, dw_grid(2, d.E, d.I, d.D), st));
+  MOE_TRY(launch_gemm(kDW, g, dw_grid(2, dw_chunks_bound(d), d.I, d.D), st));
+  MOE_TRY(launch_dw_reduce(w.dw_part, w.slist, w.pstart, w.cstart, dw_gate, dw_up, 2, d.I, d.D,
+                           d.E, max_chunked, st));
 
   if (R > 0) {
     MOE_TRY(launch_reduce_rows(w.dxs, dx, d.T, d.K, d.D, st));

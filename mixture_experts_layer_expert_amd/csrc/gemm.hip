@@ -275,18 +275,33 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
 
   // ---------------------------------------------------------------- tile decode
   int e, m0, n0, nk, rows_valid, mat = 0, k_count = 0, nk_pass = 0, nt_idx = 0;
+  int dw_chunk = 0, dw_slot = -1;  // kDW: row chunk of the expert; partial slot (chunks 1..)
   size_t kbase = 0;
   {
     int total;
     if constexpr (kRowGrouped) {
       total = p.tstart[p.E] * p.n_tiles;
     } else {
-      total = p.nmat * p.E * ceil_div(p.M, BM) * ceil_div(p.N, BN);
+      total = p.nmat * p.cstart[p.E] * ceil_div(p.M, BM) * ceil_div(p.N, BN);
     }
-    const int per = ceil_div(total, kNumXcd);
-    const int slot = blockIdx.x / kNumXcd;
-    const int tile = (blockIdx.x % kNumXcd) * per + slot;
-    if (slot >= per || tile >= total) return;
+    int tile;
+    if constexpr (kRowGrouped) {
+      // XCD x takes the x-th contiguous range of tiles (an expert's tiles share
+      // an L2); row-grouped tiles all carry about the same work
+      const int per = ceil_div(total, kNumXcd);
+      const int slot = blockIdx.x / kNumXcd;
+      tile = (blockIdx.x % kNumXcd) * per + slot;
+      if (slot >= per || tile >= total) return;
+    } else {
+      // dW: the tm x tn tiles of one (matrix, row chunk) group stay on one XCD
+      // (they share the chunk's operands in L2), and the groups are dealt to
+      // the XCDs round-robin, so the heavy chunks of a hot expert spread
+      const int per_c = ceil_div(p.M, BM) * ceil_div(p.N, BN);
+      const int slot = blockIdx.x / kNumXcd;
+      const int grp = (slot / per_c) * kNumXcd + blockIdx.x % kNumXcd;
+      tile = grp * per_c + slot % per_c;
+      if (tile >= total) return;
+    }
     if constexpr (kRowGrouped) {
       int lo = 0, hi = p.E;  // tstart[lo]*nt <= tile < tstart[hi]*nt
       while (hi - lo > 1) {
@@ -304,21 +319,34 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       n0 = nt_idx * (kGateUp ? BN / 2 : BN);  // gate/up tiles: BN/2 gate + BN/2 up rows
       nk = p.K / BK;
     } else {
+      // tiles: (matrix, row chunk, m-tile, n-tile); the chunks of expert e are
+      // cstart[e] .. cstart[e+1]-1
       const int tm = ceil_div(p.M, BM), tn = ceil_div(p.N, BN);
-      const int per_e = tm * tn;
-      mat = tile / (p.E * per_e);
-      const int rem = tile - mat * p.E * per_e;
-      e = rem / per_e;
-      const int r2 = rem - e * per_e;
+      const int per_c = tm * tn;
+      const int nchunk = p.cstart[p.E];
+      mat = tile / (nchunk * per_c);
+      const int rem = tile - mat * nchunk * per_c;
+      const int gc = rem / per_c;
+      const int r2 = rem - gc * per_c;
+      int lo = 0, hi = p.E;  // cstart[lo] <= gc < cstart[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.cstart[mid] <= gc) lo = mid;
+        else hi = mid;
+      }
+      e = lo;
+      dw_chunk = gc - p.cstart[e];
+      if (dw_chunk > 0) dw_slot = p.pstart[e] + dw_chunk - 1;
       const int mt = r2 / tn;
       nt_idx = r2 - mt * tn;
       m0 = mt * BM;
       n0 = nt_idx * BN;
-      kbase = (size_t)p.offsets[e];
-      k_count = p.offsets[e + 1] - p.offsets[e];
+      const int rows_e = p.offsets[e + 1] - p.offsets[e];
+      kbase = (size_t)p.offsets[e] + (size_t)dw_chunk * kDwChunkRows;
+      k_count = max(0, min(kDwChunkRows, rows_e - dw_chunk * kDwChunkRows));
       nk_pass = ceil_div(k_count, BK);
       // split operand (experts with many rows): a second pass with its low part
-      nk = ((p.A_lo || p.B_lo) && k_count > kDwSplitRows) ? 2 * nk_pass : nk_pass;
+      nk = ((p.A_lo || p.B_lo) && rows_e > kDwSplitRows) ? 2 * nk_pass : nk_pass;
       rows_valid = p.M - m0;
     }
   }
@@ -823,9 +851,12 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     using S = Strip<WTN, 4>;
     static_assert(NW * S::BYTES <= NS * STAGE_BYTES, "staging fits the stage buffers");
     char* const stg = lds + wave * S::BYTES;
-    float* const out = (mat == 0 ? p.Cf : p.Cf2) + (size_t)e * p.M * p.N;
+    // chunk 0 writes (or accumulates into) the expert's gradient; chunks 1..
+    // write partial tiles that launch_dw_reduce adds in chunk order
+    float* const out = dw_slot < 0 ? (mat == 0 ? p.Cf : p.Cf2) + (size_t)e * p.M * p.N
+                                    : p.dw_part + ((size_t)dw_slot * p.nmat + mat) * p.M * p.N;
     const int col0 = n0 + wn * WTN;
-    const bool accum = p.accumulate != 0;
+    const bool accum = dw_slot < 0 && p.accumulate != 0;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int rb = wm * WTM + i * 16;
@@ -840,6 +871,103 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
         });
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// dW row chunks.  One workgroup of 1024 threads: nch_e = max(1, ceil(rows_e /
+// kDwChunkRows)); cstart = exclusive prefix of nch (cstart[E] = total);
+// pstart = exclusive prefix of (nch_e - 1) (the partial slots of chunks 1..);
+// slist = the experts with nch_e > 1 in ascending order, their number in
+// slist[E].  Deterministic (integer scans).
+__global__ __launch_bounds__(1024) void dw_chunkmap_kernel(const int32_t* __restrict__ offsets,
+                                                           int E, int32_t* __restrict__ cstart,
+                                                           int32_t* __restrict__ pstart,
+                                                           int32_t* __restrict__ slist) {
+  __shared__ int wsum[3][16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int carry[3] = {0, 0, 0};
+  for (int e0 = 0; e0 < E; e0 += 1024) {
+    const int e = e0 + tid;
+    const int rows = e < E ? offsets[e + 1] - offsets[e] : 0;
+    const int nch = e < E ? max(1, (rows + kDwChunkRows - 1) / kDwChunkRows) : 0;
+    const int v[3] = {nch, nch > 1 ? nch - 1 : 0, nch > 1 ? 1 : 0};
+    int incl[3], ex[3], tot[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      incl[q] = v[q];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl[q], off);
+        if (lane >= off) incl[q] += o;
+      }
+      if (lane == 63) wsum[q][wv] = incl[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      int before = 0;
+      tot[q] = 0;
+      for (int i = 0; i < 16; ++i) {
+        if (i < wv) before += wsum[q][i];
+        tot[q] += wsum[q][i];
+      }
+      ex[q] = carry[q] + before + incl[q] - v[q];
+      carry[q] += tot[q];
+    }
+    __syncthreads();
+    if (e < E) {
+      cstart[e] = ex[0];
+      pstart[e] = ex[1];
+      if (nch > 1) slist[ex[2]] = e;
+    }
+  }
+  if (tid == 0) {
+    cstart[E] = carry[0];
+    slist[E] = carry[2];
+  }
+}
+
+// out_mat[e] += sum_{c >= 1} part[pstart[e] + c - 1][mat]  (c ascending) for
+// the chunked experts e = slist[i]; workgroup (i, stripe) strides over the
+// expert's nmat * M * N elements, 4 per thread.
+__global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict__ part,
+                                                        const int32_t* __restrict__ slist,
+                                                        const int32_t* __restrict__ pstart,
+                                                        const int32_t* __restrict__ cstart,
+                                                        float* __restrict__ out0,
+                                                        float* __restrict__ out1, int nmat, int M,
+                                                        int N, int E) {
+  const int i = blockIdx.x;
+  if (i >= slist[E]) return;
+  const int e = slist[i];
+  const int nch = cstart[e + 1] - cstart[e];
+  const size_t mn = (size_t)M * N;  // a multiple of 4 (N is a multiple of 64)
+  const size_t slot0 = (size_t)pstart[e];
+  for (size_t q = ((size_t)blockIdx.y * 256 + threadIdx.x) * 4; q < nmat * mn;
+       q += (size_t)gridDim.y * 256 * 4) {
+    const int mat = q >= mn ? 1 : 0;
+    const size_t idx = q - mat * mn;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 1; c < nch; ++c) s += *(const f32x4*)(part + ((slot0 + c - 1) * nmat + mat) * mn + idx);
+    float* o = (mat == 0 ? out0 : out1) + (size_t)e * mn + idx;
+    *(f32x4*)o = *(const f32x4*)o + s;
+  }
+}
+
+hipError_t launch_dw_chunkmap(const int32_t* offsets, int E, int32_t* cstart, int32_t* pstart,
+                              int32_t* slist, hipStream_t st) {
+  MOE_LAUNCH(kKDwChunkMap, dw_chunkmap_kernel, dim3(1), dim3(1024), 0, st, offsets, E, cstart,
+             pstart, slist);
+  return hipGetLastError();
+}
+
+hipError_t launch_dw_reduce(const float* part, const int32_t* slist, const int32_t* pstart,
+                            const int32_t* cstart, float* out0, float* out1, int nmat, int M,
+                            int N, int E, int max_chunked, hipStream_t st) {
+  if (max_chunked <= 0) return hipSuccess;
+  MOE_LAUNCH(kKDwReduce, dw_reduce_kernel, dim3(max_chunked, 64), dim3(256), 0, st, part, slist,
+             pstart, cstart, out0, out1, nmat, M, N, E);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st) {

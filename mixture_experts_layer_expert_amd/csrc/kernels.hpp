@@ -11,7 +11,8 @@ enum KernelId : int {
   kKRouteTopk, kKRouteHist, kKRouteScatter, kKTilemap, kKGather,
   kKGemmGateUpH, kKGemmGateUpGU, kKGemmDown, kKGemmDA, kKGemmDXs, kKGemmDWDown,
   kKGemmDWGateUp, kKCombine, kKReduceRows, kKReducePartials, kKGather2, kKRouterLogits,
-  kKRouterPrep, kKRouterDx, kKRouterDwr, kKRouterDwrSum, kKRowOffsets, kNumKernels
+  kKRouterPrep, kKRouterDx, kKRouterDwr, kKRouterDwrSum, kKRowOffsets, kKDwChunkMap,
+  kKDwReduce, kNumKernels
 };
 namespace prof {
 void begin(int kid, hipStream_t st);  // no-ops unless timing is enabled
@@ -97,6 +98,15 @@ constexpr int kGemmBN = MOE_GEMM_BN;  // columns of a tile (gate/up: BN/2 gate +
 // Experts with more routed rows than this get the fp16 hi + lo split of the
 // rounded dW operand (two MFMA passes); smaller ones one pass over fp16 hi.
 constexpr int kDwSplitRows = MOE_DW_SPLIT_ROWS;
+#ifndef MOE_DW_CHUNK_ROWS
+#define MOE_DW_CHUNK_ROWS 2048
+#endif
+// The weight-gradient GEMMs process an expert's rows in chunks of at most this
+// many rows, one workgroup per (chunk, output tile), so that a hot expert's
+// tiles are spread over the GPU like everyone else's.  Chunk 0 writes (or
+// accumulates into) the output; chunks 1.. write partial tiles that a
+// reduction then adds in chunk order.
+constexpr int kDwChunkRows = MOE_DW_CHUNK_ROWS;
 constexpr int kGemmPrefetch = MOE_GEMM_PREFETCH;  // L2 prefetch distance in stages
 constexpr int kGemmBK = MOE_GEMM_BK;  // reduction depth of one LDS stage (32 or 64)
 constexpr int kGemmWM = MOE_GEMM_WM;  // waves along the rows
@@ -128,6 +138,12 @@ struct GemmArgs {
   const uint32_t* a_rowoff;
   const uint32_t* b_rowoff;
   int b_rows;
+  // kDW row chunks: cstart [E+1] prefix of the per-expert chunk counts
+  // max(1, ceil(rows / kDwChunkRows)); pstart [E] first partial slot of an
+  // expert's chunks 1..; dw_part partial tiles [slot][nmat][M][N] fp32
+  const int32_t* cstart;
+  const int32_t* pstart;
+  float* dw_part;
   const bf16_t* A2;  // kDW second matrix's A (dW_up), else unused
   const bf16_t* B0;  // weights (row-grouped) or token-major activations (kDW)
   const bf16_t* B1;  // up weights (kGateUp*, kDXs)
@@ -161,5 +177,15 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st);
+
+// dW row-chunk map from the expert offsets: cstart [E+1], pstart [E], and the
+// list of chunked experts slist [E] with its length in slist[E].
+hipError_t launch_dw_chunkmap(const int32_t* offsets, int E, int32_t* cstart, int32_t* pstart,
+                              int32_t* slist, hipStream_t st);
+// Chunked experts' weight gradients: out[e] += sum over chunks 1.. of the
+// partial tiles (chunk order); max_chunked bounds the number of chunked experts.
+hipError_t launch_dw_reduce(const float* part, const int32_t* slist, const int32_t* pstart,
+                            const int32_t* cstart, float* out0, float* out1, int nmat, int M,
+                            int N, int E, int max_chunked, hipStream_t st);
 
 }  // namespace moe
