@@ -131,9 +131,10 @@ moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, cons
  *   accumulate_dw  0: overwrite dw_*;  1: add into dw_* (fp32)
  * The gate/up activations are recomputed (not read from the forward); the
  * routed rows of x and dy are gathered inside the GEMMs' operand loads.  Each
- * weight-gradient tile is produced by one workgroup that walks all of its
- * expert's rows (no atomics); experts with no rows get exact zeros (or are
- * left unchanged when accumulating).
+ * weight-gradient tile reduces over its expert's rows in chunks of at most
+ * 2048 rows, one workgroup per chunk; the chunks' partial tiles are added in
+ * chunk order (no atomics, deterministic).  Experts with no rows get exact
+ * zeros (or are left unchanged when accumulating).
  *   ws, ws_bytes   device workspace of at least moe_workspace_bytes(dims, MOE_PHASE_BWD) */
 moe_status moe_bwd(const moe_dims *dims, const void *x, const void *w_gate, const void *w_up,
                    const void *w_down, const float *topk_w, const int32_t *offsets,
