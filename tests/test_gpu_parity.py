@@ -77,6 +77,9 @@ SMALL = {
     # one expert above the 2048-row threshold of the dW operand split (two MFMA
     # passes) beside three below it (one pass), every element compared
     "split_hot": lambda: _custom(T=3000, D=128, I=64, E=4, K=2, score=0, seed=109, hot=0),
+    # every expert above 2048 rows, the hot one above 4096: three and two dW row
+    # chunks (partial tiles added in chunk order) and the two-pass split
+    "chunks3": lambda: _custom(T=6000, D=128, I=64, E=4, K=2, score=0, seed=112, hot=0),
     # skewed routing: one hot expert, three experts never chosen
     "skew_empty": lambda: _custom(T=500, D=128, I=128, E=8, K=2, score=0, seed=103, hot=1,
                                   dead=(2, 5, 7)),
