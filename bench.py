@@ -68,6 +68,8 @@ def kernel_work(wl: synth.Workload) -> dict:
         "route_scatter": ("hbm", 12.0 * R + 4.0 * E * math.ceil(R / route_chunk(R))),
         "tilemap": ("hbm", 8.0 * E),
         "row_offsets": ("hbm", 8.0 * R),
+        # split flags: the sorted-row indices and their router weights (8R), offsets, flags
+        "dw_split": ("hbm", 8.0 * R + 8.0 * E),
         # router projection and router backward (timed beside the step, not in it)
         "router_logits": ("mfma32", 2.0 * T * D * E), "router_dwr": ("mfma32", 2.0 * T * D * E),
         # dX += dl W_r^T: read and write dX (4*T*D), dl and indices (8R); W_r^T rows from L2

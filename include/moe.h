@@ -133,8 +133,11 @@ moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, cons
  * routed rows of x and dy are gathered inside the GEMMs' operand loads.  Each
  * weight-gradient tile reduces over its expert's rows in chunks of at most
  * 2048 rows, one workgroup per chunk; the chunks' partial tiles are added in
- * chunk order (no atomics, deterministic).  Experts with no rows get exact
- * zeros (or are left unchanged when accumulating).
+ * chunk order (no atomics, deterministic).  The weight-gradient GEMMs multiply
+ * fp16 operands; for an expert whose rows' squared router weights sum to more
+ * than 16 the rounded operand (dG, dU or the weighted activations) is split
+ * into fp16 high and low parts and multiplied in two passes.  Experts with no
+ * rows get exact zeros (or are left unchanged when accumulating).
  *   ws, ws_bytes   device workspace of at least moe_workspace_bytes(dims, MOE_PHASE_BWD) */
 moe_status moe_bwd(const moe_dims *dims, const void *x, const void *w_gate, const void *w_up,
                    const void *w_down, const float *topk_w, const int32_t *offsets,

@@ -72,6 +72,7 @@ struct BwdWs {
   f16_t *dgu_lo, *hw_lo;  // their low parts (value - rounded value), for the dW GEMMs
   uint32_t* rowoff;       // byte offset of each routed row's token row in x / dy
   int32_t *cstart, *pstart, *slist;  // dW row-chunk map
+  int32_t* dw_split;      // per-expert flag: dW operand split hi + lo
   float* dw_part;         // partial dW tiles of chunks 1.. of the chunked experts
   float *gu, *dxs, *part;
 };
@@ -119,6 +120,7 @@ size_t bwd_ws(const moe_dims& d, BwdWs* w, void* base) {
   w->cstart = c.take<int32_t>(d.E + 1);
   w->pstart = c.take<int32_t>(d.E);
   w->slist = c.take<int32_t>(d.E + 1);
+  w->dw_split = c.take<int32_t>(d.E);
   w->dw_part = c.take<float>(std::max<size_t>(1, (size_t)dw_part_slots(d) * 2 * d.I * d.D));
   w->gu = c.take<float>(R * 2 * d.I);
   w->dgu = c.take<f16_t>(R * 2 * d.I);
@@ -313,6 +315,9 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   hipStream_t st = (hipStream_t)stream;
   clear_stale_error();
 
+  // which experts' dW operands are split hi + lo (read by the dA epilogue and
+  // the dW GEMMs)
+  MOE_TRY(launch_dw_split(offsets, sorted_to_flat, topk_w, d.E, w.dw_split, st));
   if (R > 0) {
     // routed output gradients and the re-gathered inputs, in expert order (only
     // where the dW GEMMs cannot gather them; the row-grouped GEMMs always do)
@@ -370,6 +375,7 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
     g.s2f = sorted_to_flat;
     g.part = w.part;
     g.np = partials_per_row(d);
+    g.dw_split = w.dw_split;
     MOE_TRY(launch_gemm(kDA, g, rowgrouped_grid(d, g.n_tiles), st));
     // dXs = dG Wg + dU Wu   (reduction over 2I)
     g = GemmArgs{};
@@ -401,6 +407,7 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   g.cstart = w.cstart;
   g.pstart = w.pstart;
   g.dw_part = w.dw_part;
+  g.dw_split = w.dw_split;
   if (kGemmGatherDw) {
     g.A = (const bf16_t*)dy;
     g.a_rowoff = w.rowoff;

@@ -41,12 +41,13 @@
 //     mantissa bits than bf16, at the same matrix-core rate) and bf16 operand
 //     fragments are converted (exactly, for |v| in fp16's normal range) after
 //     the LDS read.  The dW GEMMs sum over all of an expert's rows, where the
-//     rounding error grows like the square root of the row count while the
-//     result can cancel to ~0, so for an expert with more than kDwSplitRows
-//     rows the rounded operand is split in fp16 hi + lo and multiplied in two
-//     passes into the same accumulators (error about 2^-22 sum |terms|);
-//     smaller experts take one pass over hi (error about 2^-12 times the
-//     root-sum-square of the terms);
+//     rounding error grows like the root-sum-square of the terms while the
+//     result can cancel to ~0.  Each term carries one factor of its row's
+//     router weight, so for an expert whose squared router weights sum to
+//     more than kDwSplitW2 the rounded operand is split in fp16 hi + lo and
+//     multiplied in two passes into the same accumulators (error about
+//     2^-22 sum |terms|); the others take one pass over hi (error about 2^-12
+//     times the root-sum-square of the terms);
 //   - ragged expert segments: the tile list is built on the device from the
 //     expert offsets (no host read-back, graph-capturable);
 //   - weight gradients: one workgroup owns one output tile and walks all of
@@ -345,8 +346,8 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       kbase = (size_t)p.offsets[e] + (size_t)dw_chunk * kDwChunkRows;
       k_count = max(0, min(kDwChunkRows, rows_e - dw_chunk * kDwChunkRows));
       nk_pass = ceil_div(k_count, BK);
-      // split operand (experts with many rows): a second pass with its low part
-      nk = ((p.A_lo || p.B_lo) && rows_e > kDwSplitRows) ? 2 * nk_pass : nk_pass;
+      // split operand: a second pass with its low part
+      nk = ((p.A_lo || p.B_lo) && p.dw_split[e] != 0) ? 2 * nk_pass : nk_pass;
       rows_valid = p.M - m0;
     }
   }
@@ -776,8 +777,8 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     bf16_t* const outs[6] = {p.C0, p.C1, p.C2, p.L0, p.L1, p.L2};
     const size_t ldo[6] = {(size_t)p.ldc, (size_t)p.ldc, (size_t)I,
                             (size_t)p.ldc, (size_t)p.ldc, (size_t)I};
-    // the low parts are read only by the dW GEMMs of experts with many rows
-    const bool need_lo = p.offsets[e + 1] - p.offsets[e] > kDwSplitRows;
+    // the low parts are read only by the dW GEMMs of experts with a split operand
+    const bool need_lo = p.dw_split[e] != 0;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = wm * WTM + i * 16 + frow;
@@ -925,6 +926,34 @@ __global__ __launch_bounds__(1024) void dw_chunkmap_kernel(const int32_t* __rest
     cstart[E] = carry[0];
     slist[E] = carry[2];
   }
+}
+
+// split[e] = (sum of topk_w[s2f[r]]^2 over the expert's rows r) > kDwSplitW2.
+// Workgroup e; each thread sums a fixed stride of rows, then a fixed tree.
+__global__ __launch_bounds__(256) void dw_split_kernel(const int32_t* __restrict__ offsets,
+                                                       const int32_t* __restrict__ s2f,
+                                                       const float* __restrict__ topk_w,
+                                                       int32_t* __restrict__ split) {
+  __shared__ float wsum[4];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const int r1 = offsets[e + 1];
+  float s = 0.0f;
+  for (int r = offsets[e] + tid; r < r1; r += 256) {
+    const float w = topk_w[s2f[r]];
+    s += w * w;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if ((tid & 63) == 0) wsum[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) split[e] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]) > kDwSplitW2 ? 1 : 0;
+}
+
+hipError_t launch_dw_split(const int32_t* offsets, const int32_t* s2f, const float* topk_w, int E,
+                           int32_t* split, hipStream_t st) {
+  if (E <= 0) return hipSuccess;
+  MOE_LAUNCH(kKDwSplit, dw_split_kernel, dim3(E), dim3(256), 0, st, offsets, s2f, topk_w, split);
+  return hipGetLastError();
 }
 
 // out_mat[e] += sum_{c >= 1} part[pstart[e] + c - 1][mat]  (c ascending) for

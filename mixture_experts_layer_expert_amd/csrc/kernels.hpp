@@ -12,7 +12,7 @@ enum KernelId : int {
   kKGemmGateUpH, kKGemmGateUpGU, kKGemmDown, kKGemmDA, kKGemmDXs, kKGemmDWDown,
   kKGemmDWGateUp, kKCombine, kKReduceRows, kKReducePartials, kKGather2, kKRouterLogits,
   kKRouterPrep, kKRouterDx, kKRouterDwr, kKRouterDwrSum, kKRowOffsets, kKDwChunkMap,
-  kKDwReduce, kNumKernels
+  kKDwReduce, kKDwSplit, kNumKernels
 };
 namespace prof {
 void begin(int kid, hipStream_t st);  // no-ops unless timing is enabled
@@ -92,12 +92,15 @@ constexpr int kGemmBN = MOE_GEMM_BN;  // columns of a tile (gate/up: BN/2 gate +
 #ifndef MOE_GEMM_PREFETCH
 #define MOE_GEMM_PREFETCH 1
 #endif
-#ifndef MOE_DW_SPLIT_ROWS
-#define MOE_DW_SPLIT_ROWS 2048
+#ifndef MOE_DW_SPLIT_W2
+#define MOE_DW_SPLIT_W2 16.0f
 #endif
-// Experts with more routed rows than this get the fp16 hi + lo split of the
-// rounded dW operand (two MFMA passes); smaller ones one pass over fp16 hi.
-constexpr int kDwSplitRows = MOE_DW_SPLIT_ROWS;
+// An expert whose rows' router weights have squares summing to more than this
+// gets the fp16 hi + lo split of the rounded dW operand (two MFMA passes);
+// the others one pass over fp16 hi.  The single-pass rounding error of a dW
+// entry grows like 2^-11 times the root-sum-square of its terms, and every
+// term carries one factor of the row's router weight.
+constexpr float kDwSplitW2 = MOE_DW_SPLIT_W2;
 #ifndef MOE_DW_CHUNK_ROWS
 #define MOE_DW_CHUNK_ROWS 2048
 #endif
@@ -144,6 +147,7 @@ struct GemmArgs {
   const int32_t* cstart;
   const int32_t* pstart;
   float* dw_part;
+  const int32_t* dw_split;  // [E] 1: the expert's dW operand is split hi + lo
   const bf16_t* A2;  // kDW second matrix's A (dW_up), else unused
   const bf16_t* B0;  // weights (row-grouped) or token-major activations (kDW)
   const bf16_t* B1;  // up weights (kGateUp*, kDXs)
@@ -177,6 +181,12 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st);
+
+// Per-expert hi + lo split flags of the dW operand: split[e] = 1 when the
+// squared router weights topk_w[s2f[r]]^2 of the expert's rows r sum to more
+// than kDwSplitW2 (fixed summation order, so the decision repeats bit for bit).
+hipError_t launch_dw_split(const int32_t* offsets, const int32_t* s2f, const float* topk_w, int E,
+                           int32_t* split, hipStream_t st);
 
 // dW row-chunk map from the expert offsets: cstart [E+1], pstart [E], and the
 // list of chunked experts slist [E] with its length in slist[E].

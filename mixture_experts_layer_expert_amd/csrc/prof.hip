@@ -28,7 +28,8 @@ const char* const kNames[kNumKernels] = {
     "gather",       "gemm_gateup_h", "gemm_gateup_gu", "gemm_down",    "gemm_da",
     "gemm_dxs",     "gemm_dw_down",  "gemm_dw_gateup", "combine",      "reduce_rows",
     "reduce_partials", "gather2",   "router_logits", "router_prep",  "router_dx",
-    "router_dwr",   "router_dwr_sum", "row_offsets", "dw_chunkmap", "dw_reduce"};
+    "router_dwr",   "router_dwr_sum", "row_offsets", "dw_chunkmap", "dw_reduce",
+    "dw_split"};
 
 hipEvent_t take() {
   if (!pool.empty()) {

@@ -63,7 +63,8 @@ def _full_compare(wl, data, backward=True):
 # ----------------------------------------------------------------------------- small: every element
 
 SMALL = {
-    # the tiny workload itself
+    # the tiny workload itself: five experts take the two-pass dW split (their
+    # squared router weights sum above 16), three take one pass
     "tiny": lambda: (synth.TINY, synth.generate(synth.TINY)),
     # several 256-row tiles per expert with a ragged last tile of 129..255 rows (the
     # skewed case below has last tiles of <= 128 rows, whose second wave row is all
@@ -74,11 +75,11 @@ SMALL = {
     "ragged_cols": lambda: _custom(T=300, D=320, I=64, E=16, K=3, score=0, seed=102),
     # many routed copies per token (K = 16 of 64 experts)
     "k16": lambda: _custom(T=96, D=128, I=64, E=64, K=16, score=0, seed=108),
-    # one expert above the 2048-row threshold of the dW operand split (two MFMA
-    # passes) beside three below it (one pass), every element compared
+    # a hot expert of more than 2048 rows (two dW row chunks) beside three
+    # smaller ones, all four with the two-pass dW split, every element compared
     "split_hot": lambda: _custom(T=3000, D=128, I=64, E=4, K=2, score=0, seed=109, hot=0),
     # every expert above 2048 rows, the hot one above 4096: three and two dW row
-    # chunks (partial tiles added in chunk order) and the two-pass split
+    # chunks (partial tiles added in chunk order), all with the two-pass split
     "chunks3": lambda: _custom(T=6000, D=128, I=64, E=4, K=2, score=0, seed=112, hot=0),
     # skewed routing: one hot expert, three experts never chosen
     "skew_empty": lambda: _custom(T=500, D=128, I=128, E=8, K=2, score=0, seed=103, hot=1,
@@ -101,6 +102,33 @@ SMALL = {
 @pytest.mark.parametrize("case", list(SMALL))
 def test_layer_parity_small(case):
     wl, data = SMALL[case]()
+    _full_compare(wl, data)
+
+
+# ----------------------------------------------------------------------------- random shapes
+
+def _random_cases(n=10, seed=2024):
+    """Seeded random small configurations: D, I multiples of 64, any E and K <= E,
+    either score function, some with a hot expert or dead experts.  Among them:
+    top-1 softmax (every router weight 1) with 781 rows in one expert, and 33
+    experts of which one takes the two-pass dW split and 32 one pass."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 3, 5, 8, 16, 33, 64]))
+        K = int(rng.integers(1, min(E, 8) + 1))
+        score = int(rng.integers(0, 2)) if K == 1 else 0
+        cases.append(dict(T=int(rng.integers(1, 900)), D=64 * int(rng.integers(1, 6)),
+                          I=64 * int(rng.integers(1, 5)), E=E, K=K, score=score, seed=500 + i,
+                          hot=int(rng.integers(0, E)) if rng.random() < 0.3 else None,
+                          dead=tuple(int(v) for v in rng.choice(E, size=min(E - K, 2), replace=False))
+                          if rng.random() < 0.3 and E - K >= 1 else ()))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: "T{T}_D{D}_I{I}_E{E}_K{K}_s{score}".format(**c))
+def test_layer_parity_random(case):
+    wl, data = _custom(**case)
     _full_compare(wl, data)
 
 
