@@ -169,7 +169,10 @@ def test_route_empty_batch():
 
 # ----------------------------------------------------------------------------- full size: sampled
 
-def _sampled_compare(wl, n_tokens=24, n_entries=40, seed=0):
+def _sampled_compare(wl, n_tokens=24, n_entries=40, seed=0, full_hot=False):
+    """Sampled tokens and dW entries at full size; with full_hot, every entry of
+    the hottest expert's three weight gradients as well (the oracle's dW over
+    the tokens routed to that expert, which is exact for it)."""
     data = synth.generate(wl)
     dev = G.DeviceInputs(data)
     route, y, grads = G.run_gpu(dev, wl.K, wl.score, backward=True)
@@ -200,6 +203,12 @@ def _sampled_compare(wl, n_tokens=24, n_entries=40, seed=0):
         G.assert_close(got, ref, f"{wl.name} {name}")
         for ee in np.flatnonzero(counts == 0):
             assert not G.host(grads[name][ee]).any(), f"{name}[{ee}] of an empty expert"
+    if full_hot:
+        tok_hot = np.flatnonzero((idx == hot).any(1))
+        dwg, dwu, dwd = oracle.backward_dw(L, idx, w, tokens=tok_hot)
+        for name, ref in (("dw_gate", dwg), ("dw_up", dwu), ("dw_down", dwd)):
+            G.assert_close(G.host(grads[name][hot]), ref[hot], f"{wl.name} {name}[{hot}] (all entries)")
+        del dwg, dwu, dwd
     # whole-array property at full size: outputs finite everywhere
     torch = G.torch_mod()
     for t in (y, grads["dx"], grads["dw_gate"], grads["dw_up"], grads["dw_down"], grads["d_topk_w"]):
@@ -208,18 +217,18 @@ def _sampled_compare(wl, n_tokens=24, n_entries=40, seed=0):
 
 @pytest.mark.slow
 def test_qwen3_30b_a3b_full_size():
-    _sampled_compare(synth.QWEN3_30B_A3B)
+    _sampled_compare(synth.QWEN3_30B_A3B, full_hot=True)
 
 
 @pytest.mark.slow
 def test_llama4_scout_full_size():
-    _sampled_compare(synth.LLAMA4_SCOUT, n_tokens=12, n_entries=24)
+    _sampled_compare(synth.LLAMA4_SCOUT, n_tokens=12, n_entries=512)
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("T", synth.ZIPF_SWEEP_T)
 def test_qwen_zipf_sweep(T):
-    _sampled_compare(synth.qwen_zipf(T), n_tokens=16, n_entries=24)
+    _sampled_compare(synth.qwen_zipf(T), n_tokens=16, n_entries=24, full_hot=T <= 1024)
 
 
 # ----------------------------------------------------------------------------- properties
