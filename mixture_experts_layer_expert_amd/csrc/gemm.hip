@@ -45,9 +45,9 @@
 //     result can cancel to ~0.  Each term carries one factor of its row's
 //     router weight, so for an expert whose squared router weights sum to
 //     more than kDwSplitW2 the rounded operand is split in fp16 hi + lo and
-//     multiplied in two passes into the same accumulators (error about
-//     2^-22 sum |terms|); the others take one pass over hi (error about 2^-12
-//     times the root-sum-square of the terms);
+//     both parts are multiplied into the same accumulators, block by block
+//     (error about 2^-22 sum |terms|); the others take one pass over hi
+//     (error about 2^-12 times the root-sum-square of the terms);
 //   - ragged expert segments: the tile list is built on the device from the
 //     expert offsets (no host read-back, graph-capturable);
 //   - weight gradients: one workgroup owns one output tile and walks all of
@@ -94,7 +94,7 @@ static_assert(NS * STAGE_BYTES + (PREFETCH ? NW * 256 : 0) <= 160 * 1024, "LDS b
 // slot q % RING_SLOTS, which no stage in flight still reads.
 constexpr int RING_ROWS = NW * 64, RING_SLOTS = 3;
 constexpr int RING_BYTES = RING_SLOTS * RING_ROWS * 4;
-constexpr int RING_STAGES = RING_ROWS / BK;  // stages per chunk
+constexpr int RING_STAGES = RING_ROWS / BK;  // row blocks per chunk
 static_assert(NS * STAGE_BYTES + (PREFETCH ? NW * 256 : 0) + RING_BYTES <= 160 * 1024,
               "LDS budget with the index ring");
 
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       kbase = (size_t)p.offsets[e] + (size_t)dw_chunk * kDwChunkRows;
       k_count = max(0, min(kDwChunkRows, rows_e - dw_chunk * kDwChunkRows));
       nk_pass = ceil_div(k_count, BK);
-      // split operand: a second pass with its low part
+      // split operand: every 64-row block twice, hi stage then lo stage
       nk = ((p.A_lo || p.B_lo) && p.dw_split[e] != 0) ? 2 * nk_pass : nk_pass;
       rows_valid = p.M - m0;
     }
@@ -399,14 +399,18 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   constexpr int QG = mnmajor_instrs<BM>();
   uint32_t gofs[QG] = {}, gtouch = 0;
   char* const ring = lds + kRingOff;
-  const int nch = ceil_div(nk_pass, RING_STAGES);  // index chunks per pass over the rows
-  // chunk sequence number of stage kt (the second pass of a split restarts the rows)
-  auto chunk_q = [&](int kt) { return kt < nk_pass ? kt / RING_STAGES : nch + (kt - nk_pass) / RING_STAGES; };
+  // kDW with a split operand: stage kt covers row block kt / 2, the hi part
+  // when kt is even and the lo part when it is odd, so the exact operand's
+  // lines of a block are still in L2 when its lo stage loads them again
+  const bool il = !kRowGrouped && nk != nk_pass;
+  auto blk = [&](int kt) { return il ? kt >> 1 : kt; };
+  // index chunk of stage kt
+  auto chunk_q = [&](int kt) { return blk(kt) / RING_STAGES; };
   const uint32_t* const gsrc = ga ? p.a_rowoff : gb ? p.b_rowoff : nullptr;
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(gsrc ? gsrc + kbase : nullptr,
                                               gsrc ? (size_t)k_count * 4u : 0);
   auto ring_load = [&](int q) __attribute__((always_inline)) {
-    const int rb = (q < nch ? q : q - nch) * RING_ROWS + wave * 64;
+    const int rb = q * RING_ROWS + wave * 64;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rS, LDS_PTR(void, ring + (q % RING_SLOTS) * (RING_ROWS * 4) + wave * 256), 4,
         (uint32_t)(rb + lane) * 4u, 0, 0, 0);
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   // sentinel beyond every buffer, which reads zeros).  Branch-free, so that the
   // index reads of a stage are issued together.
   auto gtok = [&](int kt, int k) -> uint32_t {
-    const int kr = (kt < nk_pass ? kt : kt - nk_pass) * BK + k;
+    const int kr = blk(kt) * BK + k;
     const uint32_t v = *(const uint32_t*)(ring + (chunk_q(kt) % RING_SLOTS) * (RING_ROWS * 4) +
                                           (kr % RING_ROWS) * 4);
     return kr < k_count ? v : 0x80000000u;
@@ -473,10 +477,10 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
                           up ? rB2 : rB, QA, q0, q1);
       }
     } else {
-      // stages [0, nk_pass): hi (or unsplit) operands; [nk_pass, 2 nk_pass): the
-      // split operand's low part against the same exact operand
-      const bool lo_pass = kt >= nk_pass;
-      const int k0 = (lo_pass ? kt - nk_pass : kt) * BK;
+      // the split operand's low part against the same exact operand on odd
+      // stages of a split tile
+      const bool lo_pass = il && (kt & 1);
+      const int k0 = blk(kt) * BK;
       issue_mnmajor<BM>(sa, wave, lane, m0, [&](int i, int k) {
         return ga ? gofs[i] : (uint32_t)(k0 + k) * lda2; }, lo_pass ? rA2 : rA, 0, q0, q1);
       issue_mnmajor<BN>(sb, wave, lane, n0, [&](int i, int k) {
@@ -491,7 +495,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   // (Capture-free, every operand by value: selecting among captured resources
   // would make the optimiser load them through the closure at a computed
   // offset, forcing the resources out of scalar registers.)
-  auto touch_stage = [](int kt, int nk_, int nk_pass_, char* dst, int wave_, int lane_,
+  auto touch_stage = [](int kt, int nk_, bool il_, char* dst, int wave_, int lane_,
                         __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t ra2,
                         __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rb2, uint32_t lda2_,
                         uint32_t ldb2_, int m0_, int n0_, int K_, uint32_t atouch_, bool ga_,
@@ -527,8 +531,8 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
         off = (uint32_t)(k0 + L / LPK) * ldb2_ + (uint32_t)(n0_ + (L % LPK) * 64) * 2u;
       }
     } else {
-      const bool lo_pass = kt >= nk_pass_;
-      const int k0 = (lo_pass ? kt - nk_pass_ : kt) * BK;
+      const bool lo_pass = il_ && (kt & 1);
+      const int k0 = (il_ ? kt >> 1 : kt) * BK;
       constexpr int LPA = BM / 64, LPB = BN / 64;
       if (opa) {
         r = lo_pass ? ra2 : ra;
@@ -542,7 +546,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   };
   char* const touch_dst = lds + NS * STAGE_BYTES + wave * 256;
   auto touch = [&](int kt) __attribute__((always_inline)) {
-    touch_stage(kt, nk, nk_pass, touch_dst, wave, lane, rA, rA2, rB, rB2, lda2, ldb2, m0, n0, p.K,
+    touch_stage(kt, nk, il, touch_dst, wave, lane, rA, rA2, rB, rB2, lda2, ldb2, m0, n0, p.K,
                 atouch, ga, gb, gtouch);
   };
 

@@ -4,9 +4,9 @@
 The kernel keeps the token-row offsets of an expert's rows in a ring of 3
 slots of one chunk each (RING_STAGES stages of rows per chunk).  Its rules,
 restated here:
-  - chunk sequence number of stage kt: kt // CS on the first pass over the
-    rows, nch + (kt - nk_pass) // CS on the second pass of a split operand;
-    chunk q lives in slot q % 3;
+  - stage kt covers row block kt (one pass), or kt // 2 when the operand is
+    split (hi and lo stages of each block alternate); chunk sequence number of
+    stage kt: its block // CS; chunk q lives in slot q % 3;
   - before the first stage: load the chunks of stages 0..2, wait, barrier;
   - at stage kt (when a next stage exists), after the stage's wait + barrier:
     load the chunk that stage kt + 3 starts, if it starts one; then read the
@@ -23,10 +23,9 @@ import pytest
 
 def simulate(nk_pass, split, cs, prefetch=1, slots=3):
     nk = 2 * nk_pass if split else nk_pass
-    nch = -(-nk_pass // cs)
 
     def q(kt):
-        return kt // cs if kt < nk_pass else nch + (kt - nk_pass) // cs
+        return (kt // 2 if split else kt) // cs
 
     slot = {}
 
