@@ -90,8 +90,8 @@ static_assert(NS * STAGE_BYTES + (PREFETCH ? NW * 256 : 0) <= 160 * 1024, "LDS b
 // Weight-gradient GEMMs with a gathered operand read its k-rows (routed rows)
 // through their token index.  The indices of an expert's rows pass through a
 // ring of RING_SLOTS chunks of RING_ROWS indices in LDS: chunk q is loaded
-// (one 4-byte-per-lane DMA per wave) three stages before its first use, into
-// slot q % RING_SLOTS, which no stage in flight still reads.
+// (one 4-byte-per-lane DMA per wave) 2 + (prefetch distance) stages before
+// its first use, into slot q % RING_SLOTS, which no stage in flight still reads.
 constexpr int RING_ROWS = NW * 64, RING_SLOTS = 3;
 constexpr int RING_BYTES = RING_SLOTS * RING_ROWS * 4;
 constexpr int RING_STAGES = RING_ROWS / BK;  // row blocks per chunk
@@ -273,9 +273,17 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   constexpr bool kF16 = MODE == kDXs || MODE == kDW;
   constexpr bool kBmn = MODE == kDA || MODE == kDXs || MODE == kDW;  // B row-contiguous
   using frag_t = typename std::conditional<kF16, f16x8, bf16x8>::type;
+  // L2 prefetch distance of this GEMM, and whether only the first tile of each
+  // group sharing an operand slice touches it
+  constexpr bool kLead = PREFETCH > 0 && kGemmTouchLead && (kGateUp || MODE == kDown);
+  constexpr int PF = kLead ? kGemmPrefetchLead : PREFETCH;
+  // the index ring is loaded RA stages ahead of its first read (the touch of
+  // stage kt + 1 + PF is read at stage kt)
+  constexpr int RA = 2 + PF;
+  static_assert(PF <= 1 || RING_STAGES >= PF, "index chunks must span the prefetch distance");
 
   // ---------------------------------------------------------------- tile decode
-  int e, m0, n0, nk, rows_valid, mat = 0, k_count = 0, nk_pass = 0, nt_idx = 0;
+  int e, m0, n0, nk, rows_valid, mat = 0, k_count = 0, nk_pass = 0, nt_idx = 0, mt_idx = 0;
   int dw_chunk = 0, dw_slot = -1;  // kDW: row chunk of the expert; partial slot (chunks 1..)
   size_t kbase = 0;
   {
@@ -315,6 +323,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       const int mcnt = p.tstart[e + 1] - p.tstart[e];
       nt_idx = local / mcnt;
       const int mt = local - nt_idx * mcnt;
+      mt_idx = mt;
       m0 = p.offsets[e] + mt * BM;
       rows_valid = min(BM, p.offsets[e + 1] - m0);
       n0 = nt_idx * (kGateUp ? BN / 2 : BN);  // gate/up tiles: BN/2 gate + BN/2 up rows
@@ -339,6 +348,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       dw_chunk = gc - p.cstart[e];
       if (dw_chunk > 0) dw_slot = p.pstart[e] + dw_chunk - 1;
       const int mt = r2 / tn;
+      mt_idx = mt;
       nt_idx = r2 - mt * tn;
       m0 = mt * BM;
       n0 = nt_idx * BN;
@@ -428,7 +438,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     constexpr int KPI = 512 / BM, LPR = BM / 8;
 #pragma unroll
     for (int i = 0; i < QG; ++i) gofs[i] = gtok(kt_load, (wave + NW * i) * KPI + lane / LPR);
-    if (PREFETCH > 0) gtouch = gtok(min(kt_touch, nk - 1), ((wave % (NW / 2)) * 64 + lane) / (BM / 64));
+    if (PF > 0) gtouch = gtok(min(kt_touch, nk - 1), ((wave % (NW / 2)) * 64 + lane) / (BM / 64));
   };
 
   // Row-grouped A: the byte offset of each A row this lane loads (one row per
@@ -445,7 +455,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     };
 #pragma unroll
     for (int i = 0; i < QA; ++i) aoff[i] = row_off(KRPI * (wave + NW * i) + lane / KCH);
-    if (PREFETCH > 0 && wave < NW / 2) atouch = row_off(wave * 64 + lane);
+    if (PF > 0 && wave < NW / 2) atouch = row_off(wave * 64 + lane);
   }
 
   // Loads of stage kt, pieces [q0, q1) of LOADS_PER_STAGE (A first, then B).
@@ -490,12 +500,12 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
 
   // L2 prefetch of stage kt: wave w touches 4 bytes of each of 64 distinct
   // 128-byte lines of the stage (waves 0 .. NW/2-1 the A lines, the rest the
-  // B lines), so the stage's direct-to-LDS loads, issued PREFETCH stages
+  // B lines), so the stage's direct-to-LDS loads, issued PF stages
   // later, find their lines in L2.  Stages past the end re-touch stage nk - 1.
   // (Capture-free, every operand by value: selecting among captured resources
   // would make the optimiser load them through the closure at a computed
   // offset, forcing the resources out of scalar registers.)
-  auto touch_stage = [](int kt, int nk_, bool il_, char* dst, int wave_, int lane_,
+  auto touch_stage = [](int kt, int nk_, bool il_, bool lead_, char* dst, int wave_, int lane_,
                         __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t ra2,
                         __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rb2, uint32_t lda2_,
                         uint32_t ldb2_, int m0_, int n0_, int K_, uint32_t atouch_, bool ga_,
@@ -542,11 +552,16 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
         off = (gb_ ? gtouch_ : (uint32_t)(k0 + L / LPB) * ldb2_) + (uint32_t)(n0_ + (L % LPB) * 64) * 2u;
       }
     }
+    if (!lead_) off = 0x80000000u;  // past every buffer: no memory traffic, same count
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, dst), 4, off, 0, 0, 0);
   };
+  // The tiles that share an operand slice (an A slice: the tiles of one row
+  // tile; a B slice: those of one column tile) run side by side on one XCD;
+  // with kLead only the first of them touches its lines.
+  const bool touch_lead = !kLead || (wave < NW / 2 ? nt_idx == 0 : mt_idx == 0);
   char* const touch_dst = lds + NS * STAGE_BYTES + wave * 256;
   auto touch = [&](int kt) __attribute__((always_inline)) {
-    touch_stage(kt, nk, il, touch_dst, wave, lane, rA, rA2, rB, rB2, lda2, ldb2, m0, n0, p.K,
+    touch_stage(kt, nk, il, touch_lead, touch_dst, wave, lane, rA, rA2, rB, rB2, lda2, ldb2, m0, n0, p.K,
                 atouch, ga, gb, gtouch);
   };
 
@@ -565,23 +580,23 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   constexpr int LOAD_SLOTS = MOE_GEMM_LOAD_SLOTS, LOAD_STRIDE = MOE_GEMM_LOAD_STRIDE;
   constexpr int LOADS_PER_SLOT = LOADS_PER_STAGE / LOAD_SLOTS;
   static_assert(LOADS_PER_SLOT * LOAD_SLOTS == LOADS_PER_STAGE &&
-                    (LOAD_SLOTS - 1) * LOAD_STRIDE + (PREFETCH > 0 ? 1 : 0) < SLOTS,
+                    (LOAD_SLOTS - 1) * LOAD_STRIDE + (PF > 0 ? 1 : 0) < SLOTS,
                 "load slots must split the stage's loads evenly and fit the MFMA rows");
   if constexpr (!kRowGrouped) {
     if ((ga || gb) && nk > 0) {
-      // the index chunks of stages 0..2, then everyone's chunks are in LDS
-      for (int s = 0; s < 3 && s < nk; ++s)
+      // the index chunks of stages 0 .. RA - 1, then everyone's chunks are in LDS
+      for (int s = 0; s < RA && s < nk; ++s)
         if (s == 0 || chunk_q(s) != chunk_q(s - 1)) ring_load(chunk_q(s));
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      gather_offsets(0, PREFETCH);
+      gather_offsets(0, PF);
     }
   }
-  if constexpr (PREFETCH > 0) {
+  if constexpr (PF > 0) {
     if (nk > 0) {
 #pragma unroll
-      for (int s = 1; s <= PREFETCH; ++s) touch(s);
+      for (int s = 1; s <= PF; ++s) touch(s);
     }
   }
 #pragma unroll
@@ -596,7 +611,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     constexpr bool kMore = decltype(more_tag)::value;
     // stage kt has landed once only the stages issued after it (at most NS - 2)
     // are still in flight
-    if constexpr (PREFETCH > 0) {
+    if constexpr (PF > 0) {
       // only the prefetch issued last (after stage kt's loads) may be in flight
       if (kt == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
@@ -607,10 +622,10 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     asm volatile("" ::: "memory");  // every wave is done reading stage kt - 1
     if constexpr (!kRowGrouped && kMore) {
       if (ga || gb) {
-        // load the index chunk that stage kt + 3 starts, if it starts one; read
+        // load the index chunk that stage kt + RA starts, if it starts one; read
         // the indices of the next stage's loads and of the prefetch touch
-        if (kt + 3 < nk && chunk_q(kt + 3) != chunk_q(kt + 2)) ring_load(chunk_q(kt + 3));
-        gather_offsets(kt + 1, kt + 1 + PREFETCH);
+        if (kt + RA < nk && chunk_q(kt + RA) != chunk_q(kt + RA - 1)) ring_load(chunk_q(kt + RA));
+        gather_offsets(kt + 1, kt + 1 + PF);
       }
     }
     if (!wave_rows) {
@@ -618,7 +633,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       // next stage (and the prefetch)
       if constexpr (kMore) {
         issue(kt + NS - 1, 0, LOADS_PER_STAGE);
-        if constexpr (PREFETCH > 0) touch(kt + NS - 1 + PREFETCH);
+        if constexpr (PF > 0) touch(kt + NS - 1 + PF);
       }
       return;
     }
@@ -672,9 +687,9 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
         // (measured: -0.6% per step)
         if (i == FM - 1) __builtin_amdgcn_s_setprio(0);
         else __builtin_amdgcn_s_setprio(1);
-        if constexpr (PREFETCH > 0) {
+        if constexpr (PF > 0) {
           if (kMore && slot == (LOAD_SLOTS - 1) * LOAD_STRIDE + 1) {
-            touch(kt + NS - 1 + PREFETCH);  // the stage's last memory instruction
+            touch(kt + NS - 1 + PF);  // the stage's last memory instruction
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
           }
         }
@@ -685,7 +700,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   for (; kt + NS - 1 < nk; ++kt) stage(kt, std::true_type{});
   for (; kt < nk; ++kt) stage(kt, std::false_type{});
   // no prefetch DMA may still be writing this workgroup's LDS when it ends
-  if constexpr (PREFETCH > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (PF > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---------------------------------------------------------------- epilogue
   // Lane holds, for fragment (i, j), row wm*WTM + i*16 + (lane % 16) and the 4

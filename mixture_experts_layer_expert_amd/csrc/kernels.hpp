@@ -111,6 +111,18 @@ constexpr float kDwSplitW2 = MOE_DW_SPLIT_W2;
 // reduction then adds in chunk order.
 constexpr int kDwChunkRows = MOE_DW_CHUNK_ROWS;
 constexpr int kGemmPrefetch = MOE_GEMM_PREFETCH;  // L2 prefetch distance in stages
+#ifndef MOE_GEMM_TOUCH_LEAD
+#define MOE_GEMM_TOUCH_LEAD 1
+#endif
+#ifndef MOE_GEMM_PREFETCH_LEAD
+#define MOE_GEMM_PREFETCH_LEAD 2
+#endif
+// L2 prefetch by the first tile of each group that shares an operand slice,
+// at distance kGemmPrefetchLead, in the gate/up and down GEMMs (the others
+// keep every tile touching at distance kGemmPrefetch, which measured faster
+// for them)
+constexpr bool kGemmTouchLead = MOE_GEMM_TOUCH_LEAD != 0;
+constexpr int kGemmPrefetchLead = MOE_GEMM_PREFETCH_LEAD;
 constexpr int kGemmBK = MOE_GEMM_BK;  // reduction depth of one LDS stage (32 or 64)
 constexpr int kGemmWM = MOE_GEMM_WM;  // waves along the rows
 constexpr int kGemmWN = MOE_GEMM_WN;  // waves along the columns

@@ -7,11 +7,13 @@ restated here:
   - stage kt covers row block kt (one pass), or kt // 2 when the operand is
     split (hi and lo stages of each block alternate); chunk sequence number of
     stage kt: its block // CS; chunk q lives in slot q % 3;
-  - before the first stage: load the chunks of stages 0..2, wait, barrier;
+  - with L2 prefetch distance P (1 or 2), RA = 2 + P;
+  - before the first stage: load the chunks of stages 0 .. RA - 1, wait,
+    barrier;
   - at stage kt (when a next stage exists), after the stage's wait + barrier:
-    load the chunk that stage kt + 3 starts, if it starts one; then read the
-    offsets for stage kt + 1 (its loads) and stage min(kt + 2, nk - 1) (the L2
-    prefetch touch);
+    load the chunk that stage kt + RA starts, if it starts one; then read the
+    offsets for stage kt + 1 (its loads) and stage min(kt + 1 + P, nk - 1)
+    (the L2 prefetch touch);
   - a load issued at stage s has completed (and is visible to every wave) at
     stage s + 1, after that stage's wait and barrier.
 Every read must find its chunk in its slot, written by a load that completed
@@ -40,7 +42,8 @@ def simulate(nk_pass, split, cs, prefetch=1, slots=3):
 
     if nk == 0:
         return 0
-    for s in range(min(3, nk)):
+    ra = 2 + prefetch
+    for s in range(min(ra, nk)):
         if s == 0 or q(s) != q(s - 1):
             load(q(s), -2)
     read(0, -1)
@@ -48,8 +51,8 @@ def simulate(nk_pass, split, cs, prefetch=1, slots=3):
     reads = 2
     for kt in range(nk):
         if kt + 1 < nk:
-            if kt + 3 < nk and q(kt + 3) != q(kt + 2):
-                load(q(kt + 3), kt)
+            if kt + ra < nk and q(kt + ra) != q(kt + ra - 1):
+                load(q(kt + ra), kt)
             read(kt + 1, kt)
             read(min(kt + 1 + prefetch, nk - 1), kt)
             reads += 2
@@ -57,10 +60,21 @@ def simulate(nk_pass, split, cs, prefetch=1, slots=3):
 
 
 @pytest.mark.parametrize("cs", [1, 2, 3, 8, 16])
-def test_ring_schedule_every_stage_count(cs):
+@pytest.mark.parametrize("prefetch", [1, 2])
+def test_ring_schedule_every_stage_count(cs, prefetch):
+    if prefetch == 2 and cs < 2:
+        pytest.skip("distance 2 needs chunks of at least 2 stages (the kernel's are 8 or more)")
     for nk_pass in range(0, 160):
         for split in (False, True):
-            simulate(nk_pass, split, cs)
+            simulate(nk_pass, split, cs, prefetch=prefetch)
+
+
+def test_ring_schedule_distance_two_needs_two_stage_chunks():
+    """With one-stage chunks the distance-2 schedule overwrites a chunk still in
+    use, which is why the kernel asserts its chunks span the distance."""
+    with pytest.raises(AssertionError):
+        for nk_pass in range(0, 64):
+            simulate(nk_pass, False, 1, prefetch=2)
 
 
 def test_ring_schedule_needs_three_slots():
