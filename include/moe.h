@@ -58,7 +58,10 @@ extern "C" {
 #define MOE_OK 0
 #define MOE_ERR_BAD_ARG 1        /* null / misaligned pointer, bad dims, K > E, T*K >= 2^31 */
 #define MOE_ERR_UNSUPPORTED 2    /* valid but unsupported: D or I not a multiple of 64,
-                                    E > 1024, K > 64, or a grid too large for 32 bits */
+                                    E > 1024, K > 64, a grid too large for 32 bits, or
+                                    an operand the GEMMs address with 32-bit byte
+                                    offsets reaching 2 GiB: T*K*max(D, 2I)*2 or I*D*2
+                                    >= 2^31 (at D = 2048, I = 768, K = 8: T <= 65535) */
 #define MOE_ERR_WORKSPACE 3      /* workspace smaller than moe_workspace_bytes() */
 #define MOE_ERR_HIP 4            /* a HIP launch or runtime call failed */
 
@@ -136,7 +139,8 @@ moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, cons
  * chunk order (no atomics, deterministic).  The weight-gradient GEMMs multiply
  * fp16 operands; for an expert whose rows' squared router weights sum to more
  * than 16 the rounded operand (dG, dU or the weighted activations) is split
- * into fp16 high and low parts and multiplied in two passes.  Experts with no
+ * into fp16 high and low parts, both multiplied into the same accumulators
+ * (row block by row block).  Experts with no
  * rows get exact zeros (or are left unchanged when accumulating).
  *   ws, ws_bytes   device workspace of at least moe_workspace_bytes(dims, MOE_PHASE_BWD) */
 moe_status moe_bwd(const moe_dims *dims, const void *x, const void *w_gate, const void *w_up,

@@ -56,6 +56,20 @@ def test_workspace_bytes_host_only(lib):
     assert 0 < small <= big
 
 
+def test_operand_size_limit(lib):
+    """The GEMMs address the routed-row operands with 32-bit byte offsets: at
+    the Qwen3-30B-A3B layer shape T = 65535 tokens is the largest batch (R * D * 2
+    just under 2^31), T = 65536 is refused before anything is launched."""
+    ok = moe.dims(65535, 2048, 768, 128, 8)
+    assert all(moe.moe_workspace_bytes(ok, ph) > 0 for ph in range(4))
+    over = moe.dims(65536, 2048, 768, 128, 8)
+    assert all(moe.moe_workspace_bytes(over, ph) == 0 for ph in range(4))
+    assert _fwd(lib, over) == 2
+    # the Scout shape's bound is the 2I-wide operands: T = 65536 gives exactly 2^31 bytes
+    assert moe.moe_workspace_bytes(moe.dims(65535, 5120, 8192, 16, 1, 1), 2) > 0
+    assert _fwd(lib, moe.dims(65536, 5120, 8192, 16, 1, 1)) == 2
+
+
 def test_backward_workspace_holds_dw_chunk_partials(lib):
     """The backward workspace grows by ceil(R / 2048) partial dW tiles of 2*I*D
     fp32 as the routed rows grow (the dW row chunks of hot experts)."""

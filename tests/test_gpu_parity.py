@@ -221,6 +221,17 @@ def test_qwen3_30b_a3b_full_size():
 
 
 @pytest.mark.slow
+def test_qwen3_30b_a3b_max_tokens():
+    """The largest batch at the Qwen3-30B-A3B layer shape: T = 65535 tokens,
+    524,280 routed rows, whose widest routed-row operands sit just under the
+    2 GiB limit of the GEMMs' 32-bit offsets.  3,688-4,617 rows per expert:
+    every dW tile takes two or three row chunks and the split operand."""
+    wl = synth.Workload("qwen3_30b_a3b_T65535", T=65535, D=2048, I=768, E=128, K=8,
+                        score=synth.SOFTMAX_TOPK, seed=5)
+    _sampled_compare(wl, n_tokens=8, n_entries=16)
+
+
+@pytest.mark.slow
 def test_llama4_scout_full_size():
     _sampled_compare(synth.LLAMA4_SCOUT, n_tokens=12, n_entries=512)
 
