@@ -69,7 +69,11 @@ def kernel_work(wl: synth.Workload) -> dict:
         "tilemap": ("hbm", 8.0 * E),
         "row_offsets": ("hbm", 8.0 * R),
         # split flags: the sorted-row indices and their router weights (8R), offsets, flags
-        "dw_split": ("hbm", 8.0 * R + 8.0 * E),
+        "bwd_prep": ("hbm", 8.0 * R + 8.0 * E),
+        # max |dy| for the gradient scale: read dy once
+        "dy_amax": ("hbm", 2.0 * T * D + 4.0 * 1024),
+        # fp16 copies of x and s dy for the dW GEMMs: read both, write both
+        "f16_operands": ("hbm", 8.0 * T * D),
         # router projection and router backward (timed beside the step, not in it)
         "router_logits": ("mfma32", 2.0 * T * D * E), "router_dwr": ("mfma32", 2.0 * T * D * E),
         # dX += dl W_r^T: read and write dX (4*T*D), dl and indices (8R); W_r^T rows from L2

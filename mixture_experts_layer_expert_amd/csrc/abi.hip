@@ -67,12 +67,15 @@ struct FwdWs {
 };
 struct BwdWs {
   int32_t* tstart;
-  bf16_t *xs, *dou;
+  bf16_t *xs, *dou;       // (copying gathers only) fp16 bits of x and s dy in expert order
   f16_t *dgu, *hw;        // fp16 operands of the gradient GEMMs (rounded values)
   f16_t *dgu_lo, *hw_lo;  // their low parts (value - rounded value), for the dW GEMMs
   uint32_t* rowoff;       // byte offset of each routed row's token row in x / dy
   int32_t *cstart, *pstart, *slist;  // dW row-chunk map
   int32_t* dw_split;      // per-expert flag: dW operand split hi + lo
+  uint32_t* amax_part;    // partial maxima of |dy|
+  float* gscale;          // gradient scale {s, 1/s}
+  f16_t *x16, *dy16;      // fp16 x and s dy, token-major: the dW GEMMs' exact operands
   float* dw_part;         // partial dW tiles of chunks 1.. of the chunked experts
   float *gu, *dxs, *part;
 };
@@ -121,6 +124,10 @@ size_t bwd_ws(const moe_dims& d, BwdWs* w, void* base) {
   w->pstart = c.take<int32_t>(d.E);
   w->slist = c.take<int32_t>(d.E + 1);
   w->dw_split = c.take<int32_t>(d.E);
+  w->amax_part = c.take<uint32_t>(kAmaxBlocks);
+  w->gscale = c.take<float>(2);
+  w->x16 = c.take<f16_t>((size_t)d.T * d.D);
+  w->dy16 = c.take<f16_t>((size_t)d.T * d.D);
   w->dw_part = c.take<float>(std::max<size_t>(1, (size_t)dw_part_slots(d) * 2 * d.I * d.D));
   w->gu = c.take<float>(R * 2 * d.I);
   w->dgu = c.take<f16_t>(R * 2 * d.I);
@@ -316,15 +323,18 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   clear_stale_error();
 
   // which experts' dW operands are split hi + lo (read by the dA epilogue and
-  // the dW GEMMs)
-  MOE_TRY(launch_dw_split(offsets, sorted_to_flat, topk_w, d.E, w.dw_split, st));
+  // the dW GEMMs), and the gradient scale from max|dy|
+  MOE_TRY(launch_amax_bf16(dy, TD, w.amax_part, st));
+  MOE_TRY(launch_bwd_prep(offsets, sorted_to_flat, topk_w, d.E, w.amax_part, w.dw_split, w.gscale,
+                          st));
+  MOE_TRY(launch_f16_operands(x, dy, w.gscale, w.x16, w.dy16, TD, st));
   if (R > 0) {
     // routed output gradients and the re-gathered inputs, in expert order (only
     // where the dW GEMMs cannot gather them; the row-grouped GEMMs always do)
     if (kGemmGatherDw)
       MOE_TRY(launch_row_offsets(sorted_to_flat, (int)R, d.K, (uint32_t)d.D * 2u, w.rowoff, st));
     else
-      MOE_TRY(launch_gather(x, dy, w.xs, w.dou, sorted_to_flat, (int)R, d.K, d.D, st));
+      MOE_TRY(launch_gather(w.x16, w.dy16, w.xs, w.dou, sorted_to_flat, (int)R, d.K, d.D, st));
     MOE_TRY(launch_tilemap(offsets, d.E, kGemmBM, w.tstart, st));
   }
   GemmArgs g{};
@@ -376,6 +386,7 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
     g.part = w.part;
     g.np = partials_per_row(d);
     g.dw_split = w.dw_split;
+    g.gscale = w.gscale;
     MOE_TRY(launch_gemm(kDA, g, rowgrouped_grid(d, g.n_tiles), st));
     // dXs = dG Wg + dU Wu   (reduction over 2I)
     g = GemmArgs{};
@@ -393,12 +404,12 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
     g.Cf = w.dxs;  // rows in flat slot order (t*K + k)
     g.ldc = d.D;
     g.s2f = sorted_to_flat;
-    g.cvt_a = 0;  // dG | dU already fp16
-    g.cvt_b = 1;  // weights bf16 -> fp16
+    g.gscale = w.gscale;
     MOE_TRY(launch_gemm(kDXs, g, rowgrouped_grid(d, g.n_tiles), st));
   }
   // dW_down[e] = dOu_e^T Hw_e   ([D, I], reduction over the expert's rows, in
-  // row chunks of at most kDwChunkRows)
+  // row chunks of at most kDwChunkRows); dOu from the fp16 s dy, the result
+  // times 1/s
   MOE_TRY(launch_dw_chunkmap(offsets, d.E, w.cstart, w.pstart, w.slist, st));
   const int max_chunked = (int)dw_max_chunked(d);
   g = GemmArgs{};
@@ -408,8 +419,9 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   g.pstart = w.pstart;
   g.dw_part = w.dw_part;
   g.dw_split = w.dw_split;
+  g.gscale = w.gscale;
   if (kGemmGatherDw) {
-    g.A = (const bf16_t*)dy;
+    g.A = (const bf16_t*)w.dy16;  // fp16 bits
     g.a_rowoff = w.rowoff;
     g.a_rows = d.T;
   } else {
@@ -421,21 +433,19 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   g.M = d.D;
   g.N = d.I;
   g.nmat = 1;
-  g.cvt_a = 1;  // dOu bf16 -> fp16
-  g.cvt_b = 0;  // Hw fp16, split hi + lo
   g.B_lo = w.hw_lo;
   g.Cf = dw_down;
   g.accumulate = accumulate_dw;
   MOE_TRY(launch_gemm(kDW, g, dw_grid(1, dw_chunks_bound(d), d.D, d.I), st));
   MOE_TRY(launch_dw_reduce(w.dw_part, w.slist, w.pstart, w.cstart, dw_down, nullptr, 1, d.D, d.I,
                            d.E, max_chunked, st));
-  // dW_gate[e] = dG_e^T Xs_e, dW_up[e] = dU_e^T Xs_e   ([I, D])
+  // dW_gate[e] = dG_e^T Xs_e, dW_up[e] = dU_e^T Xs_e   ([I, D]); Xs from the fp16 x
   g.A = w.dgu;
   g.A2 = w.dgu + d.I;
   g.a_rowoff = nullptr;
   g.lda = 2 * d.I;
   if (kGemmGatherDw) {
-    g.B0 = (const bf16_t*)x;
+    g.B0 = (const bf16_t*)w.x16;  // fp16 bits
     g.b_rowoff = w.rowoff;
     g.b_rows = d.T;
   } else {
@@ -445,8 +455,6 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   g.M = d.I;
   g.N = d.D;
   g.nmat = 2;
-  g.cvt_a = 0;  // dG | dU fp16, split hi + lo
-  g.cvt_b = 1;  // Xs bf16 -> fp16
   g.A_lo = w.dgu_lo;
   g.A2_lo = w.dgu_lo + d.I;
   g.B_lo = nullptr;

@@ -38,10 +38,16 @@
 //     by the SwiGLU backward and the router-weight gradient) and the per-row
 //     dX partials (summed over the K routed copies) stay fp32.  The gradient
 //     GEMMs (dXs, dW) multiply fp16: dG/dU/Hw are rounded to fp16 (3 more
-//     mantissa bits than bf16, at the same matrix-core rate) and bf16 operand
-//     fragments are converted (exactly, for |v| in fp16's normal range) after
-//     the LDS read.  The dW GEMMs sum over all of an expert's rows, where the
-//     rounding error grows like the root-sum-square of the terms while the
+//     mantissa bits than bf16, at the same matrix-core rate); dXs converts
+//     its bf16 weight fragments after the LDS read, and the dW GEMMs read fp16
+//     copies of x and s dy written once per backward (exact for |v| in fp16's
+//     normal range).  s, a power of two with s max|dy| in [1, 2), keeps the
+//     gradient operands (s dy, s dG, s dU) clear of fp16's subnormal range
+//     and of its overflow whatever the loss scale; dXs and dW multiply their
+//     fp32 results by 1/s, so at any scale the results equal those of unit-
+//     scale gradients times the scale, bit for bit.  The dW GEMMs sum over
+//     all of an expert's rows, where the rounding error grows like the
+//     root-sum-square of the terms while the
 //     result can cancel to ~0.  Each term carries one factor of its row's
 //     router weight, so for an expert whose squared router weights sum to
 //     more than kDwSplitW2 the rounded operand is split in fp16 hi + lo and
@@ -565,6 +571,9 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
                 atouch, ga, gb, gtouch);
   };
 
+  // gradient scale {s, 1/s} of the backward GEMMs (1 where unused)
+  const float gsc = p.gscale ? p.gscale[0] : 1.0f;
+  const float ginv = p.gscale ? p.gscale[1] : 1.0f;
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -658,13 +667,10 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
           bfr[j] = read_kmajor<frag_t>(sb, wn * WTN + j * 16, kk, lane);
         }
       }
-      if constexpr (kF16) {
-        if (p.cvt_a)
+      // dXs: the weights (B) are bf16; every other fp16 operand is stored as fp16
+      if constexpr (MODE == kDXs) {
 #pragma unroll
-          for (int i = 0; i < FM; ++i) af[i] = frag_to_f16(af[i]);
-        if (p.cvt_b)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) bfr[j] = frag_to_f16(bfr[j]);
+        for (int j = 0; j < FN; ++j) bfr[j] = frag_to_f16(bfr[j]);
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -762,7 +768,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       for (int j = 0; j < FN; ++j) {
         const int cl = j * 16 + cq;
         const f32x4 v = acc[i][j];
-        if constexpr (MODE == kDXs) strip_put<S>(stg, frow, cl, v);
+        if constexpr (MODE == kDXs) strip_put<S>(stg, frow, cl, v * ginv);
         else strip_put<S>(stg, frow, cl, u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
       }
       const int nrows = rows_valid - rb, ncols = p.N - col0;
@@ -804,6 +810,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       const bool row_ok = r < rows_valid;
       const size_t m = (size_t)(m0 + (row_ok ? r : 0));
       const float wr = row_ok ? p.topk_w[p.s2f[m]] : 0.0f;
+      const float wrs = wr * gsc;  // dG, dU carry the gradient scale
       float dot = 0.0f;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -824,7 +831,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
           const float sg = sigmoidf_(g);
           const float h = g * sg * u;
           if (ok) dot += da * h;
-          const float dh = wr * da;
+          const float dh = wrs * da;
           dg[q] = dh * u * sg * (1.0f + g * (1.0f - sg));
           du[q] = dh * g * sg;
           hw[q] = wr * h;
@@ -885,7 +892,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       strip_out<S>(stg, lane, rows_valid - rb, p.N - col0, [&](int r) {
         return (char*)(out + (size_t)(m0 + rb + r) * p.N + col0); },
         [&](char* dst, u32x4 v) {
-          f32x4 x = __builtin_bit_cast(f32x4, v);
+          f32x4 x = __builtin_bit_cast(f32x4, v) * ginv;
           if (accum) x += *(const f32x4*)dst;
           __builtin_nontemporal_store(x, (f32x4*)dst);
         });
@@ -947,13 +954,19 @@ __global__ __launch_bounds__(1024) void dw_chunkmap_kernel(const int32_t* __rest
   }
 }
 
-// split[e] = (sum of topk_w[s2f[r]]^2 over the expert's rows r) > kDwSplitW2.
-// Workgroup e; each thread sums a fixed stride of rows, then a fixed tree.
-__global__ __launch_bounds__(256) void dw_split_kernel(const int32_t* __restrict__ offsets,
+// Workgroup e: split[e] = (sum of topk_w[s2f[r]]^2 over the expert's rows r)
+// > kDwSplitW2, each thread summing a fixed stride of rows, then a fixed tree.
+// Workgroup 0 also turns the kAmaxBlocks partial maxima of |dy| into the
+// gradient scale {s, 1/s}: s = 2^(1 - x) for max|dy| = m 2^x, m in [0.5, 1),
+// with x clamped to [-64, 64]; s = 1 when dy is all zero or not finite.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const int32_t* __restrict__ offsets,
                                                        const int32_t* __restrict__ s2f,
                                                        const float* __restrict__ topk_w,
-                                                       int32_t* __restrict__ split) {
+                                                       const uint32_t* __restrict__ amax_part,
+                                                       int32_t* __restrict__ split,
+                                                       float* __restrict__ gscale) {
   __shared__ float wsum[4];
+  __shared__ uint32_t wmax[4];
   const int e = blockIdx.x, tid = threadIdx.x;
   const int r1 = offsets[e + 1];
   float s = 0.0f;
@@ -964,14 +977,35 @@ __global__ __launch_bounds__(256) void dw_split_kernel(const int32_t* __restrict
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
   if ((tid & 63) == 0) wsum[tid >> 6] = s;
+  if (e == 0) {
+    uint32_t m = 0;
+    for (int b = tid; b < kAmaxBlocks; b += 256) m = max(m, amax_part[b]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  }
   __syncthreads();
   if (tid == 0) split[e] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]) > kDwSplitW2 ? 1 : 0;
+  if (e == 0 && tid == 0) {
+    const uint32_t m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    float sc = 1.0f;
+    if (m != 0 && m < 0x7f80u) {  // finite, nonzero
+      int x;
+      frexpf(__uint_as_float(m << 16), &x);
+      x = min(64, max(-64, x));
+      sc = ldexpf(1.0f, 1 - x);
+    }
+    gscale[0] = sc;
+    gscale[1] = 1.0f / sc;
+  }
 }
 
-hipError_t launch_dw_split(const int32_t* offsets, const int32_t* s2f, const float* topk_w, int E,
-                           int32_t* split, hipStream_t st) {
+hipError_t launch_bwd_prep(const int32_t* offsets, const int32_t* s2f, const float* topk_w, int E,
+                           const uint32_t* amax_part, int32_t* split, float* gscale,
+                           hipStream_t st) {
   if (E <= 0) return hipSuccess;
-  MOE_LAUNCH(kKDwSplit, dw_split_kernel, dim3(E), dim3(256), 0, st, offsets, s2f, topk_w, split);
+  MOE_LAUNCH(kKBwdPrep, bwd_prep_kernel, dim3(E), dim3(256), 0, st, offsets, s2f, topk_w,
+             amax_part, split, gscale);
   return hipGetLastError();
 }
 

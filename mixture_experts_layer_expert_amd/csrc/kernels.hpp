@@ -12,7 +12,7 @@ enum KernelId : int {
   kKGemmGateUpH, kKGemmGateUpGU, kKGemmDown, kKGemmDA, kKGemmDXs, kKGemmDWDown,
   kKGemmDWGateUp, kKCombine, kKReduceRows, kKReducePartials, kKGather2, kKRouterLogits,
   kKRouterPrep, kKRouterDx, kKRouterDwr, kKRouterDwrSum, kKRowOffsets, kKDwChunkMap,
-  kKDwReduce, kKDwSplit, kNumKernels
+  kKDwReduce, kKBwdPrep, kKDyAmax, kKF16Operands, kNumKernels
 };
 namespace prof {
 void begin(int kid, hipStream_t st);  // no-ops unless timing is enabled
@@ -49,6 +49,15 @@ hipError_t launch_reduce_partials(const float* part, const int32_t* f2s, float* 
 // rowoff[p] = (sorted_to_flat[p] / K) * row_bytes: byte offset of routed row p's token row
 hipError_t launch_row_offsets(const int32_t* s2f, int R, int K, uint32_t row_bytes,
                               uint32_t* rowoff, hipStream_t st);
+// Largest |v| over the n bf16 values of src (n a multiple of 8): kAmaxBlocks
+// workgroup maxima (bit patterns of |v|, ordered like the values) into part.
+constexpr int kAmaxBlocks = 1024;
+hipError_t launch_amax_bf16(const void* src, size_t n, uint32_t* part, hipStream_t st);
+// fp16 operands of the weight-gradient GEMMs from the bf16 inputs (n values
+// each, a multiple of 8): x16 = x, dy16 = s dy with s = gscale[0] (exact in
+// fp16's normal range; rounded toward zero below it).
+hipError_t launch_f16_operands(const void* x, const void* dy, const float* gscale, void* x16,
+                               void* dy16, size_t n, hipStream_t st);
 
 // ---- router projection and router backward (router.hip)
 hipError_t launch_router_logits(const void* x, const float* w_r, float* logits, int T, int D,
@@ -160,6 +169,9 @@ struct GemmArgs {
   const int32_t* pstart;
   float* dw_part;
   const int32_t* dw_split;  // [E] 1: the expert's dW operand is split hi + lo
+  // backward gradient scale {s, 1/s} (see launch_bwd_prep), or null (s = 1):
+  // kDA scales dG and dU by s; kDXs and kDW multiply their results by 1/s
+  const float* gscale;
   const bf16_t* A2;  // kDW second matrix's A (dW_up), else unused
   const bf16_t* B0;  // weights (row-grouped) or token-major activations (kDW)
   const bf16_t* B1;  // up weights (kGateUp*, kDXs)
@@ -170,7 +182,6 @@ struct GemmArgs {
   int lda, ldb;
   int n_tiles;  // row-grouped: column tiles per m-tile (gate/up: ceil(I/128), else ceil(N/256))
   int nmat;     // kDW: matrices in this launch (1 or 2)
-  int cvt_a, cvt_b;  // kDXs / kDW: operand stored as bf16, convert to fp16 when staging
   const f16_t* A_lo;   // kDW: low fp16 parts of a split A (mat 0) / A2 (mat 1), or null
   const f16_t* A2_lo;
   const f16_t* B_lo;   // kDW: low fp16 part of a split B, or null
@@ -194,11 +205,18 @@ struct GemmArgs {
 
 hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st);
 
-// Per-expert hi + lo split flags of the dW operand: split[e] = 1 when the
-// squared router weights topk_w[s2f[r]]^2 of the expert's rows r sum to more
-// than kDwSplitW2 (fixed summation order, so the decision repeats bit for bit).
-hipError_t launch_dw_split(const int32_t* offsets, const int32_t* s2f, const float* topk_w, int E,
-                           int32_t* split, hipStream_t st);
+// Backward preparation, one workgroup per expert:
+//   split[e] = 1 when the squared router weights topk_w[s2f[r]]^2 of expert
+//     e's rows r sum to more than kDwSplitW2 (fixed summation order, so the
+//     decision repeats bit for bit): its dW operand is split hi + lo;
+//   gscale = {s, 1/s} (workgroup 0), the power of two s with s * max|dy| in
+//     [1, 2) (s = 1 for an all-zero or non-finite dy), from the kAmaxBlocks
+//     maxima that launch_amax_bf16 left in amax_part.  The gradient GEMMs
+//     carry s * dy, s * dG, s * dU in fp16, away from its subnormal range, and
+//     multiply their fp32 results by 1/s (all exact).
+hipError_t launch_bwd_prep(const int32_t* offsets, const int32_t* s2f, const float* topk_w, int E,
+                           const uint32_t* amax_part, int32_t* split, float* gscale,
+                           hipStream_t st);
 
 // dW row-chunk map from the expert offsets: cstart [E+1], pstart [E], and the
 // list of chunked experts slist [E] with its length in slist[E].

@@ -143,6 +143,66 @@ hipError_t launch_row_offsets(const int32_t* s2f, int R, int K, uint32_t row_byt
   return hipGetLastError();
 }
 
+// part[b] = max over workgroup b's grid-stride share of |src| (bf16 values as
+// their 15-bit magnitude patterns, which order like the values; NaN patterns
+// sort above infinity).  Integer max: the result does not depend on order.
+__global__ __launch_bounds__(kPermuteThreads) void amax_bf16_kernel(
+    const u32x4* __restrict__ src, size_t n16, uint32_t* __restrict__ part) {
+  __shared__ uint32_t wmax[kPermuteThreads / 64];
+  uint32_t m = 0;
+  for (size_t c = (size_t)blockIdx.x * kPermuteThreads + threadIdx.x; c < n16;
+       c += (size_t)gridDim.x * kPermuteThreads) {
+    const u32x4 v = __builtin_nontemporal_load(src + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m = max(m, max(v[q] & 0x7fffu, (v[q] >> 16) & 0x7fffu));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t b = 0;
+    for (int w = 0; w < kPermuteThreads / 64; ++w) b = max(b, wmax[w]);
+    part[blockIdx.x] = b;
+  }
+}
+
+hipError_t launch_amax_bf16(const void* src, size_t n, uint32_t* part, hipStream_t st) {
+  // always kAmaxBlocks workgroups, so that every maximum the reader expects is written
+  MOE_LAUNCH(kKDyAmax, amax_bf16_kernel, dim3(kAmaxBlocks), dim3(kPermuteThreads), 0, st,
+             (const u32x4*)src, n / 8, part);
+  return hipGetLastError();
+}
+
+// x16 = fp16(x), dy16 = fp16(s dy), 8 values per thread and tensor.
+__global__ __launch_bounds__(kPermuteThreads) void f16_operands_kernel(
+    const u32x4* __restrict__ x, const u32x4* __restrict__ dy, const float* __restrict__ gscale,
+    u32x4* __restrict__ x16, u32x4* __restrict__ dy16, size_t n16) {
+  const float sc = gscale[0];
+  for (size_t c = (size_t)blockIdx.x * kPermuteThreads + threadIdx.x; c < n16;
+       c += (size_t)gridDim.x * kPermuteThreads) {
+    const u32x4 a = __builtin_nontemporal_load(x + c);
+    const u32x4 b = __builtin_nontemporal_load(dy + c);
+    u32x4 ao, bo;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ao[q] = bf16x2_to_f16x2(a[q]);
+      bo[q] = __builtin_bit_cast(uint32_t,
+                                 __builtin_amdgcn_cvt_pkrtz(bf16_lo(b[q]) * sc, bf16_hi(b[q]) * sc));
+    }
+    x16[c] = ao;
+    dy16[c] = bo;
+  }
+}
+
+hipError_t launch_f16_operands(const void* x, const void* dy, const float* gscale, void* x16,
+                               void* dy16, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  MOE_LAUNCH(kKF16Operands, f16_operands_kernel, dim3(grid_for(n / 8)), dim3(kPermuteThreads), 0,
+             st, (const u32x4*)x, (const u32x4*)dy, gscale, (u32x4*)x16, (u32x4*)dy16, n / 8);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather(const void* src0, const void* src1, void* dst0, void* dst1,
                          const int32_t* s2f, int R, int K, int D, hipStream_t st) {
   const int cpr = D / 8;

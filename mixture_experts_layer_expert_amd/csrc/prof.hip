@@ -29,7 +29,7 @@ const char* const kNames[kNumKernels] = {
     "gemm_dxs",     "gemm_dw_down",  "gemm_dw_gateup", "combine",      "reduce_rows",
     "reduce_partials", "gather2",   "router_logits", "router_prep",  "router_dx",
     "router_dwr",   "router_dwr_sum", "row_offsets", "dw_chunkmap", "dw_reduce",
-    "dw_split"};
+    "bwd_prep",     "dy_amax",       "f16_operands"};
 
 hipEvent_t take() {
   if (!pool.empty()) {

@@ -277,6 +277,32 @@ def test_bitwise_determinism_and_overwrite():
         assert torch.equal(out[k], 2 * g1[k]), k
 
 
+@pytest.mark.parametrize("log2c", [-20, 16])
+def test_gradient_scale_invariance(log2c):
+    """The backward of dy * 2^c is 2^c times the backward of dy, bit for bit:
+    the gradient GEMMs carry their fp16 operands at a power-of-two scale taken
+    from max|dy|, so gradients far below fp16's normal range (dy ~ 1e-6) or
+    above its largest value (dy ~ 1e5) keep the precision of unit-scale ones.
+    An all-zero dy gives exact zeros.  The case has experts with and without
+    the split dW operand."""
+    import mixture_experts_layer_expert_amd as moe
+    torch = G.torch_mod()
+    wl, data = _custom(T=900, D=256, I=192, E=16, K=2, score=0, seed=202, hot=3)
+    dev = G.DeviceInputs(data)
+    route, _, g1 = G.run_gpu(dev, wl.K, wl.score)
+    c = 2.0 ** log2c
+    dy_c = synth.f32_to_bf16_bits((synth.bf16_bits_to_f64(data["dy"]) * c).astype(np.float32))
+    g2 = moe.moe_bwd(dev.x, dev.w_gate, dev.w_up, dev.w_down, route, G.to_dev_bf16(dy_c), wl.K,
+                     wl.score)
+    zero = moe.moe_bwd(dev.x, dev.w_gate, dev.w_up, dev.w_down, route, torch.zeros_like(dev.dy),
+                       wl.K, wl.score)
+    torch.cuda.synchronize()
+    for k in g1:
+        a, b = g1[k].float() * c, g2[k].float()
+        assert torch.equal(a, b), (k, (a - b).abs().max().item())
+        assert not zero[k].float().any(), k
+
+
 def test_stream_and_graph_capture():
     """Calls run on the caller's stream and can be captured into a graph; replays
     (with eager work in between) reproduce the eager results bit for bit."""
