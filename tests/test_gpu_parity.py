@@ -303,12 +303,20 @@ def test_gradient_scale_invariance(log2c):
         assert not zero[k].float().any(), k
 
 
-def test_stream_and_graph_capture():
+@pytest.mark.parametrize("shape", ["small", "chunked"])
+def test_stream_and_graph_capture(shape):
     """Calls run on the caller's stream and can be captured into a graph; replays
-    (with eager work in between) reproduce the eager results bit for bit."""
+    (with eager work in between) reproduce the eager results bit for bit.  The
+    chunked case has experts of two and three dW row chunks, all with the split
+    operand.  A last replay after dy is scaled in place by 2^-10 gives the
+    gradients times 2^-10 exactly: the gradient scale is taken anew on every
+    replay."""
     import mixture_experts_layer_expert_amd as moe
     torch = G.torch_mod()
-    wl, data = _custom(T=384, D=128, I=128, E=8, K=2, score=0, seed=202)
+    if shape == "small":
+        wl, data = _custom(T=384, D=128, I=128, E=8, K=2, score=0, seed=202)
+    else:
+        wl, data = _custom(T=6000, D=128, I=64, E=4, K=2, score=0, seed=112, hot=0)
     dev = G.DeviceInputs(data)
     r_ref, y_ref, g_ref = G.run_gpu(dev, wl.K, wl.score)
     s = torch.cuda.Stream()
@@ -345,6 +353,12 @@ def test_stream_and_graph_capture():
             if a.dtype == torch.bfloat16:
                 a, b = a.view(torch.int16), b.view(torch.int16)
             assert torch.equal(a, b), (rep, k)
+    dev.dy.mul_(2.0 ** -10)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    for k in g_ref:
+        assert torch.equal(out[k].float(), g_ref[k].float() * 2.0 ** -10), k
 
 
 def test_empty_batch_layer():
