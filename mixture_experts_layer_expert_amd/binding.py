@@ -124,6 +124,9 @@ def _ptr(t, dtype, shape, name):
         raise TypeError(f"{name}: expected a torch tensor")
     if not t.is_cuda:
         raise MoeError(f"{name}: must be a GPU tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise MoeError(f"{name}: on {t.device}, but the current device is "
+                       f"cuda:{torch.cuda.current_device()} (the library runs there)")
     if t.dtype != dtype:
         raise MoeError(f"{name}: expected {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
