@@ -160,7 +160,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not supported "
-              "(no sharding or collectives in this build).", file=sys.stderr)
+              "(the library has no sharding or collectives).", file=sys.stderr)
         return 2
 
     import torch
