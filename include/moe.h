@@ -210,8 +210,12 @@ const char *moe_last_error(void);
  * ids run 0..moe_prof_num_kernels()-1; moe_prof_kernel_name() names them (NULL
  * for an unknown id).  Timing state is process-wide; do not enable it while
  * a stream is being captured into a graph.  Returns MOE_ERR_HIP if an event
- * query fails, MOE_ERR_BAD_ARG for null arrays with n > 0. */
+ * query fails, MOE_ERR_BAD_ARG for null arrays with n > 0.
+ * moe_prof_only(id) restricts the bracketing to one kernel id (-1: every
+ * kernel, the default), so that a timed loop carries two events per launch
+ * of that kernel instead of two per kernel; MOE_ERR_BAD_ARG for an unknown id. */
 int32_t moe_prof_enable(int32_t on);
+moe_status moe_prof_only(int32_t kernel_id);
 int32_t moe_prof_num_kernels(void);
 const char *moe_prof_kernel_name(int32_t kernel_id);
 moe_status moe_prof_read(double *total_ms, int64_t *launches, int32_t n);

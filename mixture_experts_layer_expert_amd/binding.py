@@ -75,6 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.moe_last_error.argtypes = []
         lib.moe_prof_enable.restype = ctypes.c_int32
         lib.moe_prof_enable.argtypes = [ctypes.c_int32]
+        lib.moe_prof_only.restype = ctypes.c_int32
+        lib.moe_prof_only.argtypes = [ctypes.c_int32]
         lib.moe_prof_num_kernels.restype = ctypes.c_int32
         lib.moe_prof_num_kernels.argtypes = []
         lib.moe_prof_kernel_name.restype = ctypes.c_char_p
@@ -290,6 +292,18 @@ def moe_router_bwd(x, w_r, route: dict, d_topk_w, dx, K: int,
 def moe_prof_enable(on: bool) -> None:
     """Start (True) or stop (False) per-kernel event timing; clears what was recorded."""
     load_library().moe_prof_enable(1 if on else 0)
+
+
+def moe_prof_only(kernel: str | None) -> None:
+    """Bracket only the named kernel (None: every kernel) while timing is enabled."""
+    lib = load_library()
+    kid = -1
+    if kernel is not None:
+        names = {lib.moe_prof_kernel_name(i).decode(): i for i in range(lib.moe_prof_num_kernels())}
+        if kernel not in names:
+            raise MoeError(f"unknown kernel {kernel!r}")
+        kid = names[kernel]
+    _check(lib.moe_prof_only(kid), "moe_prof_only")
 
 
 def moe_prof_read() -> dict:

@@ -529,6 +529,10 @@ MOE_EXPORT int32_t moe_prof_enable(int32_t on) { return prof::set_enabled(on); }
 
 MOE_EXPORT int32_t moe_prof_num_kernels(void) { return kNumKernels; }
 
+MOE_EXPORT moe_status moe_prof_only(int32_t kernel_id) {
+  return prof::set_only(kernel_id) == 0 ? MOE_OK : MOE_ERR_BAD_ARG;
+}
+
 MOE_EXPORT const char* moe_prof_kernel_name(int32_t kernel_id) { return prof::name(kernel_id); }
 
 MOE_EXPORT moe_status moe_prof_read(double* total_ms, int64_t* launches, int32_t n) {

@@ -19,6 +19,7 @@ void begin(int kid, hipStream_t st);  // no-ops unless timing is enabled
 void end(hipStream_t st);
 const char* name(int kid);
 int set_enabled(int on);
+int set_only(int kid);  // -1: every kernel; else only that id (-1 returned for a bad id)
 int read(double* total_ms, int64_t* launches, int n);
 }  // namespace prof
 

@@ -18,6 +18,7 @@ struct Rec {
 
 std::mutex mu;
 bool enabled = false;
+int only_kid = -1;  // >= 0: bracket only this kernel id
 std::vector<Rec> recs;        // recorded since the last enable
 std::vector<hipEvent_t> pool;  // reusable events
 int open_kid = -1;
@@ -55,6 +56,7 @@ void recycle() {
 void begin(int kid, hipStream_t st) {
   if (!enabled) return;
   std::lock_guard<std::mutex> g(mu);
+  if (only_kid >= 0 && kid != only_kid) return;
   hipEvent_t e = take();
   if (!e) return;
   hipEventRecord(e, st);
@@ -80,6 +82,13 @@ int set_enabled(int on) {
   recycle();
   open_kid = -1;
   enabled = on != 0;
+  return 0;
+}
+
+int set_only(int kid) {
+  if (kid < -1 || kid >= kNumKernels) return -1;
+  std::lock_guard<std::mutex> g(mu);
+  only_kid = kid;
   return 0;
 }
 
