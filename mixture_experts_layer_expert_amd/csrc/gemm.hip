@@ -591,15 +591,24 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   static_assert(LOADS_PER_SLOT * LOAD_SLOTS == LOADS_PER_STAGE &&
                     (LOAD_SLOTS - 1) * LOAD_STRIDE + (PF > 0 ? 1 : 0) < SLOTS,
                 "load slots must split the stage's loads evenly and fit the MFMA rows");
+  bool first_issued = false;  // stage 0's loads already issued by the gathered prologue
   if constexpr (!kRowGrouped) {
     if ((ga || gb) && nk > 0) {
-      // the index chunks of stages 0 .. RA - 1, then everyone's chunks are in LDS
+      // the index chunks of stages 0 .. RA - 1; meanwhile the operand that is
+      // not gathered needs no indices, so its part of stage 0 goes out at once
+      // and only the index loads (issued before it) are waited for
+      static_assert(QA == LOADS_PER_STAGE - QA, "gathered kDW tiles: equal A and B pieces");
       for (int s = 0; s < RA && s < nk; ++s)
         if (s == 0 || chunk_q(s) != chunk_q(s - 1)) ring_load(chunk_q(s));
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
+      if (ga) issue(0, QA, LOADS_PER_STAGE);
+      else issue(0, 0, QA);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QA) : "memory");
+      __builtin_amdgcn_s_barrier();  // everyone's index chunks are in LDS
       asm volatile("" ::: "memory");
       gather_offsets(0, PF);
+      if (ga) issue(0, 0, QA);
+      else issue(0, QA, LOADS_PER_STAGE);
+      first_issued = true;
     }
   }
   if constexpr (PF > 0) {
@@ -610,7 +619,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   }
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s, 0, LOADS_PER_STAGE);
+    if (s < nk && !(s == 0 && first_issued)) issue(s, 0, LOADS_PER_STAGE);
   // Waves whose rows all lie past a ragged expert's end (row-grouped tiles)
   // skip the fragment reads and MFMAs; wave-uniform.
   const bool wave_rows = !kRowGrouped || wm * WTM < rows_valid;
