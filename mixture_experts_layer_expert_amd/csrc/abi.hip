@@ -91,6 +91,11 @@ int64_t dw_part_slots(const moe_dims& d) {
 }
 int64_t dw_chunks_bound(const moe_dims& d) { return d.E + dw_part_slots(d); }
 
+// Launch table of the gate/up, recompute and down GEMMs: the lead prefetch
+// policy when the experts average at least kLeadMinRows routed rows (measured:
+// -1% per step at 512 rows per expert; +1.4% at 64)
+int gemm_lead(const moe_dims& d) { return (int64_t)d.T * d.K >= (int64_t)kLeadMinRows * d.E; }
+
 // router-weight-gradient partials per routed row: one per (column tile, wave column)
 int partials_per_row(const moe_dims& d) { return kGemmWN * ((d.I + kGemmBN - 1) / kGemmBN); }
 
@@ -278,6 +283,7 @@ MOE_EXPORT moe_status moe_fwd(const moe_dims* dims, const void* x, const void* w
   g.N = d.I;
   g.K = d.D;
   g.n_tiles = (int)gateup_tiles(d.I);
+  g.lead = gemm_lead(d);
   g.C0 = w.h;
   g.ldc = d.I;
   MOE_TRY(launch_gemm(kGateUpH, g, rowgrouped_grid(d, g.n_tiles), st));
@@ -354,6 +360,7 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
     g.N = d.I;
     g.K = d.D;
     g.n_tiles = (int)gateup_tiles(d.I);
+    g.lead = gemm_lead(d);
     g.Cf = w.gu;
     g.Cf2 = w.gu + d.I;
     g.ldc = 2 * d.I;

@@ -264,7 +264,9 @@ __device__ __forceinline__ void strip_out(const char* stg, int lane, int nrows, 
   }
 }
 
-template <int MODE>
+// LEAD: the L2 prefetch policy of the gate/up and down GEMMs (see kLead); the
+// host picks it per launch from the shape (GemmArgs::lead).
+template <int MODE, bool LEAD = false>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void grouped_gemm_kernel(
     GemmArgs p) {
   // NS stages, then (with L2 prefetch) 256 bytes per wave that the prefetch
@@ -281,7 +283,8 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   using frag_t = typename std::conditional<kF16, f16x8, bf16x8>::type;
   // L2 prefetch distance of this GEMM, and whether only the first tile of each
   // group sharing an operand slice touches it
-  constexpr bool kLead = PREFETCH > 0 && kGemmTouchLead && (kGateUp || MODE == kDown);
+  static_assert(!LEAD || kGateUp || MODE == kDown, "the lead policy is for gate/up and down");
+  constexpr bool kLead = PREFETCH > 0 && LEAD;
   constexpr int PF = kLead ? kGemmPrefetchLead : PREFETCH;
   // the index ring is loaded RA stages ahead of its first read (the touch of
   // stage kt + 1 + PF is read at stage kt)
@@ -1066,13 +1069,24 @@ hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st) {
   const bool dw_gateup = mode == kDW && a.nmat == 2;
   switch (mode) {
     case kGateUpH:
-      MOE_LAUNCH(kKGemmGateUpH, grouped_gemm_kernel<kGateUpH>, dim3(grid), dim3(NTH), 0, st, a);
+      if (a.lead)
+        MOE_LAUNCH(kKGemmGateUpH, (grouped_gemm_kernel<kGateUpH, true>), dim3(grid), dim3(NTH), 0,
+                   st, a);
+      else
+        MOE_LAUNCH(kKGemmGateUpH, grouped_gemm_kernel<kGateUpH>, dim3(grid), dim3(NTH), 0, st, a);
       break;
     case kGateUpGU:
-      MOE_LAUNCH(kKGemmGateUpGU, grouped_gemm_kernel<kGateUpGU>, dim3(grid), dim3(NTH), 0, st, a);
+      if (a.lead)
+        MOE_LAUNCH(kKGemmGateUpGU, (grouped_gemm_kernel<kGateUpGU, true>), dim3(grid), dim3(NTH), 0,
+                   st, a);
+      else
+        MOE_LAUNCH(kKGemmGateUpGU, grouped_gemm_kernel<kGateUpGU>, dim3(grid), dim3(NTH), 0, st, a);
       break;
     case kDown:
-      MOE_LAUNCH(kKGemmDown, grouped_gemm_kernel<kDown>, dim3(grid), dim3(NTH), 0, st, a);
+      if (a.lead)
+        MOE_LAUNCH(kKGemmDown, (grouped_gemm_kernel<kDown, true>), dim3(grid), dim3(NTH), 0, st, a);
+      else
+        MOE_LAUNCH(kKGemmDown, grouped_gemm_kernel<kDown>, dim3(grid), dim3(NTH), 0, st, a);
       break;
     case kDA:
       MOE_LAUNCH(kKGemmDA, grouped_gemm_kernel<kDA>, dim3(grid), dim3(NTH), 0, st, a);

@@ -121,18 +121,17 @@ constexpr float kDwSplitW2 = MOE_DW_SPLIT_W2;
 // reduction then adds in chunk order.
 constexpr int kDwChunkRows = MOE_DW_CHUNK_ROWS;
 constexpr int kGemmPrefetch = MOE_GEMM_PREFETCH;  // L2 prefetch distance in stages
-#ifndef MOE_GEMM_TOUCH_LEAD
-#define MOE_GEMM_TOUCH_LEAD 1
-#endif
 #ifndef MOE_GEMM_PREFETCH_LEAD
 #define MOE_GEMM_PREFETCH_LEAD 2
 #endif
-// L2 prefetch by the first tile of each group that shares an operand slice,
-// at distance kGemmPrefetchLead, in the gate/up and down GEMMs (the others
-// keep every tile touching at distance kGemmPrefetch, which measured faster
-// for them)
-constexpr bool kGemmTouchLead = MOE_GEMM_TOUCH_LEAD != 0;
+// The "lead" prefetch policy of the gate/up and down GEMMs: only the first
+// tile of each group that shares an operand slice touches it, at distance
+// kGemmPrefetchLead.  The launch table (abi.hip) picks it when the experts
+// average at least kLeadMinRows routed rows (their tiles then run side by
+// side on an XCD); with fewer rows, and in the other GEMMs, every tile
+// touches its own lines at distance kGemmPrefetch, which measured faster.
 constexpr int kGemmPrefetchLead = MOE_GEMM_PREFETCH_LEAD;
+constexpr int kLeadMinRows = 256;
 constexpr int kGemmBK = MOE_GEMM_BK;  // reduction depth of one LDS stage (32 or 64)
 constexpr int kGemmWM = MOE_GEMM_WM;  // waves along the rows
 constexpr int kGemmWN = MOE_GEMM_WN;  // waves along the columns
@@ -183,6 +182,7 @@ struct GemmArgs {
   int lda, ldb;
   int n_tiles;  // row-grouped: column tiles per m-tile (gate/up: ceil(I/128), else ceil(N/256))
   int nmat;     // kDW: matrices in this launch (1 or 2)
+  int lead;     // gate/up, down: 1 = the lead prefetch policy (kLeadMinRows)
   const f16_t* A_lo;   // kDW: low fp16 parts of a split A (mat 0) / A2 (mat 1), or null
   const f16_t* A2_lo;
   const f16_t* B_lo;   // kDW: low fp16 part of a split B, or null
