@@ -56,12 +56,19 @@
 //     (error about 2^-12 times the root-sum-square of the terms);
 //   - ragged expert segments: the tile list is built on the device from the
 //     expert offsets (no host read-back, graph-capturable);
-//   - weight gradients: one workgroup owns one output tile and walks all of
-//     its expert's rows (no atomics, deterministic); an expert with no rows
-//     writes zeros;
+//   - weight gradients: one workgroup owns one output tile of one row chunk
+//     (at most kDwChunkRows of its expert's rows); chunk 0 writes the tile,
+//     later chunks write partial tiles that dw_reduce_kernel adds in chunk
+//     order (no atomics, deterministic); an expert with no rows writes zeros;
 //   - XCD-aware tile order: workgroup b runs on XCD b % 8, so each XCD takes a
 //     contiguous range of the (expert, column tile, row tile) list and the
-//     tiles sharing one expert's operands share that XCD's L2.
+//     tiles sharing one expert's operands share that XCD's L2; the dW GEMMs
+//     deal their (matrix, row chunk) groups of tiles to the XCDs round-robin;
+//   - L2 prefetch: each stage also touches the lines of a later stage (one
+//     4-byte DMA per lane into a scratch LDS area), either every tile its own
+//     lines one stage ahead, or, for gate/up and down when the launch asks
+//     for the lead policy, only the first tile of each group sharing an
+//     operand slice, two stages ahead.
 #include <type_traits>
 
 #include "kernels.hpp"
