@@ -1,7 +1,9 @@
 // Memory-bound kernels around the expert GEMMs (gfx950): gather into expert
-// order, router-weighted combine, and the reduction of routed gradients back
-// onto tokens.  Each thread moves 16-byte chunks; rows are contiguous, so
-// every wave reads and writes whole 16-byte-aligned row segments.
+// order, router-weighted combine, the reduction of routed gradients back onto
+// tokens, and the backward's operand preparation (max|dy| for the gradient
+// scale; fp16 copies of x and s dy for the weight-gradient GEMMs).  Each
+// thread moves 16-byte chunks; rows are contiguous, so every wave reads and
+// writes whole 16-byte-aligned row segments.
 //
 // Method: LigerCute README (liger-cute-kernels 0.8.3), "LigerMoE design":
 //   - Forward pass: the sorted tokens are copied into the expert-ordered
