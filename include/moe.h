@@ -140,7 +140,10 @@ moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, cons
  * fp16 operands; for an expert whose rows' squared router weights sum to more
  * than 16 the rounded operand (dG, dU or the weighted activations) is split
  * into fp16 high and low parts, both multiplied into the same accumulators
- * (row block by row block).  Experts with no
+ * (row block by row block).  The fp16 gradient operands carry a power-of-two
+ * scale s with s * max|dy| in [1, 2), removed from the fp32 results, so the
+ * gradients of 2^c dy are exactly 2^c times those of dy whatever c (within
+ * fp32 range): no loss scaling is needed.  Experts with no
  * rows get exact zeros (or are left unchanged when accumulating).
  *   ws, ws_bytes   device workspace of at least moe_workspace_bytes(dims, MOE_PHASE_BWD) */
 moe_status moe_bwd(const moe_dims *dims, const void *x, const void *w_gate, const void *w_up,
