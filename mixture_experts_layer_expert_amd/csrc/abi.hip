@@ -40,9 +40,12 @@ moe_status check_dims(const moe_dims* d) {
   const int64_t mt = (R + (int64_t)d->E * (kGemmBM - 1)) / kGemmBM;
   const int64_t nt = std::max<int64_t>(gateup_tiles(d->I), (d->D + kGemmBN - 1) / kGemmBN);
   if (mt * nt >= (int64_t(1) << 31) - 8) return MOE_ERR_UNSUPPORTED;
-  const int64_t dwt = 2 * ((d->I + kGemmBM - 1) / kGemmBM) * ((d->D + kGemmBN - 1) / kGemmBN) *
-                      (d->E + (R + kDwChunkRows - 1) / kDwChunkRows);
-  if (dwt >= (int64_t(1) << 31) - 8) return MOE_ERR_UNSUPPORTED;
+  // the dW grids as launched (dw_grid below: the (matrix, row chunk) groups
+  // rounded up to a multiple of the XCD count)
+  const int64_t per_c = ((d->I + kGemmBM - 1) / kGemmBM) * ((d->D + kGemmBN - 1) / kGemmBN);
+  const int64_t groups = 2 * (d->E + (R + kDwChunkRows - 1) / kDwChunkRows);
+  if ((groups + kNumXcd - 1) / kNumXcd * kNumXcd * per_c >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
   // the GEMMs address token-major operands with 32-bit buffer offsets
   if (R * std::max<int64_t>(d->D, 2 * (int64_t)d->I) * 2 >= (int64_t(1) << 31) ||
       (int64_t)d->I * d->D * 2 >= (int64_t(1) << 31))
