@@ -143,7 +143,10 @@ moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, cons
  * (row block by row block).  The fp16 gradient operands carry a power-of-two
  * scale s with s * max|dy| in [1, 2), removed from the fp32 results, so the
  * gradients of 2^c dy are exactly 2^c times those of dy whatever c (within
- * fp32 range): no loss scaling is needed.  Experts with no
+ * fp32 range): no loss scaling is needed.  x enters the weight gradients as
+ * fp16 without a scale: |x| above 65504 saturates there, and values below
+ * 2^-14 keep less relative precision (activations are far inside that
+ * range).  Experts with no
  * rows get exact zeros (or are left unchanged when accumulating).
  *   ws, ws_bytes   device workspace of at least moe_workspace_bytes(dims, MOE_PHASE_BWD) */
 moe_status moe_bwd(const moe_dims *dims, const void *x, const void *w_gate, const void *w_up,
