@@ -98,6 +98,16 @@ def test_router_qwen3_30b_a3b_full_size():
     _check_router(wl, data, drw, dx_in)
 
 
+@pytest.mark.slow
+def test_router_llama4_scout_full_size():
+    """Every element of logits, dW_r and dX at the Llama-4-Scout layer shape
+    (T = 8192, D = 5120, E = 16, top-1 sigmoid)."""
+    wl = synth.LLAMA4_SCOUT
+    data = synth.generate(wl, with_dy=False)
+    drw, dx_in = _router_inputs(wl, 4343)
+    _check_router(wl, data, drw, dx_in)
+
+
 def test_router_in_the_layer():
     """Router + layer end to end: the GPU's dX after moe_bwd and moe_router_bwd is
     the full input gradient of the layer (expert path + router path), and dW_r is
