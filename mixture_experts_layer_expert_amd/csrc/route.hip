@@ -16,21 +16,23 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Top-K: one wave per token.  Lane l holds experts l, l+64, ... (coalesced
-// loads).  K rounds of a wave-wide arg-max under the (value desc, id asc)
-// order; the winner's owner lane marks it taken.
-template <int NPL>
+// Top-K: a group of L lanes per token (L a power of two, K <= L; 64 / L tokens
+// per wave).  Lane l of the group holds experts l, l+L, ... (NPL of them).
+// K rounds of a group-wide arg-max under the (value desc, id asc) order; the
+// winner's owner lane marks it taken; lane k of the group keeps round k's
+// winner.
+template <int NPL, int L>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                    int K, int score, int32_t* __restrict__ idx,
                                                    float* __restrict__ w) {
-  const int token = (blockIdx.x * 256 + threadIdx.x) >> 6;
-  const int lane = threadIdx.x & 63;
-  if (token >= T) return;  // uniform per wave
+  const int token = (blockIdx.x * 256 + threadIdx.x) / L;
+  const int gl = threadIdx.x & (L - 1);  // lane within the token's group
+  if (token >= T) return;  // uniform per group; shuffles stay inside a group
   const float* l = logits + (size_t)token * E;
   float v[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
-    const int e = lane + 64 * j;
+    const int e = gl + L * j;
     v[j] = e < E ? l[e] : 0.0f;
   }
   uint32_t taken = 0;
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     int be = -1;  // -1: no candidate
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
-      const int e = lane + 64 * j;
+      const int e = gl + L * j;
       if (e < E && !((taken >> j) & 1u)) {
         if (be < 0 || v[j] > bv || (v[j] == bv && e < be)) {
           bv = v[j];
@@ -50,7 +52,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
       }
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
+    for (int off = L / 2; off >= 1; off >>= 1) {
       const float ov = __shfl_xor(bv, off);
       const int oe = __shfl_xor(be, off);
       if (oe >= 0 && (be < 0 || ov > bv || (ov == bv && oe < be))) {
@@ -58,8 +60,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
         be = oe;
       }
     }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == k) {
+    if ((be & (L - 1)) == gl) taken |= 1u << (be / L);
+    if (gl == k) {
       my_e = be;
       my_v = bv;
     }
@@ -67,17 +69,17 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   }
   float wk;
   if (score == MOE_SCORE_SOFTMAX_TOPK) {
-    const float ex = lane < K ? expf(my_v - top_v) : 0.0f;
+    const float ex = gl < K ? expf(my_v - top_v) : 0.0f;
     float s = ex;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    for (int off = L / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
     wk = ex / s;
   } else {
     wk = 1.0f / (1.0f + expf(-my_v));
   }
-  if (lane < K) {
-    idx[(size_t)token * K + lane] = my_e;
-    w[(size_t)token * K + lane] = wk;
+  if (gl < K) {
+    idx[(size_t)token * K + gl] = my_e;
+    w[(size_t)token * K + gl] = wk;
   }
 }
 
@@ -242,16 +244,30 @@ hipError_t launch_route_sort(const moe_dims& d, const float* logits, int32_t* id
                              int32_t* hist, hipStream_t st) {
   const int R = d.T * d.K;
   if (d.T > 0) {
-    const int blocks = (d.T + 3) / 4;
-    const int npl = (d.E + 63) / 64;
-#define MOE_TOPK(N)                                                                      \
-  MOE_LAUNCH(kKRouteTopk, topk_kernel<N>, dim3(blocks), dim3(256), 0, st, logits, d.T, d.E, \
-             d.K, d.score, idx, w)
-    if (npl <= 1) MOE_TOPK(1);
-    else if (npl <= 2) MOE_TOPK(2);
-    else if (npl <= 4) MOE_TOPK(4);
-    else if (npl <= 8) MOE_TOPK(8);
-    else MOE_TOPK(16);
+    // lanes per token: the smallest of 8, 16, 32, 64 that holds the K winners
+    // with at most 16 logits per lane (E <= 1024)
+    int L = 8;
+    while (L < 64 && (L < d.K || (d.E + L - 1) / L > 16)) L *= 2;
+    const int npl = (d.E + L - 1) / L;
+    const int blocks = (int)(((int64_t)d.T * L + 255) / 256);
+#define MOE_TOPK(N, LL)                                                                        \
+  MOE_LAUNCH(kKRouteTopk, (topk_kernel<N, LL>), dim3(blocks), dim3(256), 0, st, logits, d.T, \
+             d.E, d.K, d.score, idx, w)
+#define MOE_TOPK_L(LL)                  \
+  do {                                  \
+    if (npl <= 1) MOE_TOPK(1, LL);      \
+    else if (npl <= 2) MOE_TOPK(2, LL); \
+    else if (npl <= 4) MOE_TOPK(4, LL); \
+    else if (npl <= 8) MOE_TOPK(8, LL); \
+    else MOE_TOPK(16, LL);              \
+  } while (0)
+    switch (L) {
+      case 8: MOE_TOPK_L(8); break;
+      case 16: MOE_TOPK_L(16); break;
+      case 32: MOE_TOPK_L(32); break;
+      default: MOE_TOPK_L(64); break;
+    }
+#undef MOE_TOPK_L
 #undef MOE_TOPK
   }
   const int chunk = route_chunk(R);
