@@ -134,8 +134,11 @@ def test_layer_parity_random(case):
 
 # ----------------------------------------------------------------------------- routing only
 
+# the top-K kernel's lane group per token: 8 lanes (128/8, 65/3, 7/7, 1/1, 16/1),
+# 16 (256/8), 32 (300/20, 512/4) and 64 (1024/64)
 ROUTE_CASES = [(T, E, K) for (T, E, K) in [(1000, 128, 8), (513, 65, 3), (300, 1024, 64),
-                                           (64, 1, 1), (200, 7, 7), (4096, 16, 1)]]
+                                           (64, 1, 1), (200, 7, 7), (4096, 16, 1), (600, 256, 8),
+                                           (700, 300, 20), (500, 512, 4)]]
 
 
 @pytest.mark.parametrize("T,E,K", ROUTE_CASES)
