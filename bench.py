@@ -14,9 +14,10 @@ value = counted FLOPs per step / step time, with 6*D*I FLOPs per routed row
 forward and 12*D*I backward (the activation recompute is not counted).
 
 Prints ONE JSON line.  Also reports the dominant kernel against its roofline
-(per-kernel durations from HIP events recorded on the launch stream over the
-timed steps) and the CPU oracle timed on a bounded sample of the same
-workload.
+(its duration from HIP events on its launch stream over the timed steps, in
+which no other kernel carries events; the per-kernel table comes from K
+instrumented steps before them) and the CPU oracle timed on a bounded sample
+of the same workload.
 """
 from __future__ import annotations
 

@@ -1,0 +1,34 @@
+"""CPU checks of bench.py's host logic: its table of algorithmic work per
+kernel names only kernels the library has, and prices every grouped GEMM in
+matrix FLOPs and every other kernel of the step in HBM bytes."""
+import bench
+import synth
+import mixture_experts_layer_expert_amd as moe
+
+
+def _kernel_names():
+    lib = moe.load_library()
+    return {lib.moe_prof_kernel_name(i).decode() for i in range(lib.moe_prof_num_kernels())}
+
+
+def test_work_table_names_library_kernels():
+    names = _kernel_names()
+    for wl in (synth.QWEN3_30B_A3B, synth.LLAMA4_SCOUT, synth.TINY):
+        work = bench.kernel_work(wl)
+        assert set(work) <= names, set(work) - names
+        gemms = {n for n in names if n.startswith("gemm_")}
+        assert gemms <= set(work)
+        for n, (bound, amount) in work.items():
+            assert bound in ("mfma", "mfma32", "hbm"), n
+            assert amount >= 0, n
+            assert (bound == "mfma") == n.startswith("gemm_"), n
+
+
+def test_gemm_flops_add_up_to_the_counted_step():
+    """The seven grouped GEMMs' algorithmic FLOPs are the step's counted 18 D I
+    per routed row plus the recompute's 4 D I."""
+    wl = synth.QWEN3_30B_A3B
+    work = bench.kernel_work(wl)
+    total = sum(a for n, (b, a) in work.items() if b == "mfma")
+    assert total == (18 + 4) * wl.D * wl.I * wl.R
+    assert wl.flops_fwd() + wl.flops_bwd() == 18 * wl.D * wl.I * wl.R
