@@ -137,8 +137,9 @@ moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, cons
  * weight-gradient tile reduces over its expert's rows in chunks of at most
  * 2048 rows, one workgroup per chunk; the chunks' partial tiles are added in
  * chunk order (no atomics, deterministic).  The weight-gradient GEMMs multiply
- * fp16 operands; for an expert whose rows' squared router weights sum to more
- * than 16 the rounded operand (dG, dU or the weighted activations) is split
+ * fp16 operands; for an expert with n rows whose squared router weights sum
+ * to S, with S * (1 + 100 / n) * max(1, 3 D / (8 I)) > 16, the rounded
+ * operand (dG, dU or the weighted activations) is split
  * into fp16 high and low parts, both multiplied into the same accumulators
  * (row block by row block).  The fp16 gradient operands carry a power-of-two
  * scale s with s * max|dy| in [1, 2), removed from the fp32 results, so the

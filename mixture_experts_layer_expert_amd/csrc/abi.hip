@@ -334,8 +334,9 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   // which experts' dW operands are split hi + lo (read by the dA epilogue and
   // the dW GEMMs), and the gradient scale from max|dy|
   MOE_TRY(launch_amax_bf16(dy, TD, w.amax_part, st));
-  MOE_TRY(launch_bwd_prep(offsets, sorted_to_flat, topk_w, d.E, w.amax_part, w.dw_split, w.gscale,
-                          st));
+  const float dim_factor = std::max(1.0f, 3.0f * (float)d.D / (8.0f * (float)d.I));
+  MOE_TRY(launch_bwd_prep(offsets, sorted_to_flat, topk_w, d.E, dim_factor, w.amax_part,
+                          w.dw_split, w.gscale, st));
   MOE_TRY(launch_f16_operands(x, dy, w.gscale, w.x16, w.dy16, TD, st));
   if (R > 0) {
     // routed output gradients and the re-gathered inputs, in expert order (only

@@ -50,7 +50,8 @@
 //     root-sum-square of the terms while the
 //     result can cancel to ~0.  Each term carries one factor of its row's
 //     router weight, so for an expert whose squared router weights sum to
-//     more than kDwSplitW2 the rounded operand is split in fp16 hi + lo and
+//     more than kDwSplitW2 (weighted up for experts with few rows and for a
+//     wide D against I) the rounded operand is split in fp16 hi + lo and
 //     both parts are multiplied into the same accumulators, block by block
 //     (error about 2^-22 sum |terms|); the others take one pass over hi
 //     (error about 2^-12 times the root-sum-square of the terms);
@@ -973,23 +974,25 @@ __global__ __launch_bounds__(1024) void dw_chunkmap_kernel(const int32_t* __rest
   }
 }
 
-// Workgroup e: split[e] = (sum of topk_w[s2f[r]]^2 over the expert's rows r)
-// > kDwSplitW2, each thread summing a fixed stride of rows, then a fixed tree.
+// Workgroup e: S = sum of topk_w[s2f[r]]^2 over the expert's n rows r, each
+// thread summing a fixed stride of rows, then a fixed tree, and
+// split[e] = S * (1 + kDwSplitRows / n) * dim_factor > kDwSplitW2.
 // Workgroup 0 also turns the kAmaxBlocks partial maxima of |dy| into the
 // gradient scale {s, 1/s}: s = 2^(1 - x) for max|dy| = m 2^x, m in [0.5, 1),
 // with x clamped to [-64, 64]; s = 1 when dy is all zero or not finite.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const int32_t* __restrict__ offsets,
                                                        const int32_t* __restrict__ s2f,
                                                        const float* __restrict__ topk_w,
+                                                       float dim_factor,
                                                        const uint32_t* __restrict__ amax_part,
                                                        int32_t* __restrict__ split,
                                                        float* __restrict__ gscale) {
   __shared__ float wsum[4];
   __shared__ uint32_t wmax[4];
   const int e = blockIdx.x, tid = threadIdx.x;
-  const int r1 = offsets[e + 1];
+  const int r0 = offsets[e], r1 = offsets[e + 1];
   float s = 0.0f;
-  for (int r = offsets[e] + tid; r < r1; r += 256) {
+  for (int r = r0 + tid; r < r1; r += 256) {
     const float w = topk_w[s2f[r]];
     s += w * w;
   }
@@ -1004,7 +1007,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const int32_t* __restrict
     if ((tid & 63) == 0) wmax[tid >> 6] = m;
   }
   __syncthreads();
-  if (tid == 0) split[e] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]) > kDwSplitW2 ? 1 : 0;
+  if (tid == 0) {
+    const float sw2 = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    const int n = r1 - r0;
+    split[e] = n > 0 && sw2 * (1.0f + kDwSplitRows / (float)n) * dim_factor > kDwSplitW2 ? 1 : 0;
+  }
   if (e == 0 && tid == 0) {
     const uint32_t m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
     float sc = 1.0f;
@@ -1020,11 +1027,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const int32_t* __restrict
 }
 
 hipError_t launch_bwd_prep(const int32_t* offsets, const int32_t* s2f, const float* topk_w, int E,
-                           const uint32_t* amax_part, int32_t* split, float* gscale,
-                           hipStream_t st) {
+                           float dim_factor, const uint32_t* amax_part, int32_t* split,
+                           float* gscale, hipStream_t st) {
   if (E <= 0) return hipSuccess;
   MOE_LAUNCH(kKBwdPrep, bwd_prep_kernel, dim3(E), dim3(256), 0, st, offsets, s2f, topk_w,
-             amax_part, split, gscale);
+             dim_factor, amax_part, split, gscale);
   return hipGetLastError();
 }
 

@@ -105,12 +105,20 @@ constexpr int kGemmBN = MOE_GEMM_BN;  // columns of a tile (gate/up: BN/2 gate +
 #ifndef MOE_DW_SPLIT_W2
 #define MOE_DW_SPLIT_W2 16.0f
 #endif
-// An expert whose rows' router weights have squares summing to more than this
-// gets the fp16 hi + lo split of the rounded dW operand (two MFMA passes);
+#ifndef MOE_DW_SPLIT_ROWS
+#define MOE_DW_SPLIT_ROWS 100.0f
+#endif
+// An expert with n rows whose router weights have squares summing to S gets
+// the fp16 hi + lo split of the rounded dW operand (two MFMA passes) when
+//   S * (1 + kDwSplitRows / n) * max(1, 3 D / (8 I)) > kDwSplitW2,
 // the others one pass over fp16 hi.  The single-pass rounding error of a dW
 // entry grows like 2^-11 times the root-sum-square of its terms, and every
-// term carries one factor of the row's router weight.
+// term carries one factor of the row's router weight, hence S.  Few rows
+// give the per-entry sums of squares a heavier tail over the D x I entries,
+// and a wide D against I makes the gate/up gradient terms larger, hence the
+// two factors.
 constexpr float kDwSplitW2 = MOE_DW_SPLIT_W2;
+constexpr float kDwSplitRows = MOE_DW_SPLIT_ROWS;
 #ifndef MOE_DW_CHUNK_ROWS
 #define MOE_DW_CHUNK_ROWS 2048
 #endif
@@ -207,8 +215,10 @@ struct GemmArgs {
 hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st);
 
 // Backward preparation, one workgroup per expert:
-//   split[e] = 1 when the squared router weights topk_w[s2f[r]]^2 of expert
-//     e's rows r sum to more than kDwSplitW2 (fixed summation order, so the
+//   split[e] = 1 when S, the sum of the squared router weights
+//     topk_w[s2f[r]]^2 over expert e's n rows r, has
+//     S * (1 + kDwSplitRows / n) * dim_factor > kDwSplitW2, where the caller
+//     passes dim_factor = max(1, 3 D / (8 I)) (fixed summation order, so the
 //     decision repeats bit for bit): its dW operand is split hi + lo;
 //   gscale = {s, 1/s} (workgroup 0), the power of two s with s * max|dy| in
 //     [1, 2) (s = 1 for an all-zero or non-finite dy), from the kAmaxBlocks
@@ -216,8 +226,8 @@ hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st);
 //     carry s * dy, s * dG, s * dU in fp16, away from its subnormal range, and
 //     multiply their fp32 results by 1/s (all exact).
 hipError_t launch_bwd_prep(const int32_t* offsets, const int32_t* s2f, const float* topk_w, int E,
-                           const uint32_t* amax_part, int32_t* split, float* gscale,
-                           hipStream_t st);
+                           float dim_factor, const uint32_t* amax_part, int32_t* split,
+                           float* gscale, hipStream_t st);
 
 // dW row-chunk map from the expert offsets: cstart [E+1], pstart [E], and the
 // list of chunked experts slist [E] with its length in slist[E].

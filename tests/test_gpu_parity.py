@@ -63,8 +63,9 @@ def _full_compare(wl, data, backward=True):
 # ----------------------------------------------------------------------------- small: every element
 
 SMALL = {
-    # the tiny workload itself: five experts take the two-pass dW split (their
-    # squared router weights sum above 16), three take one pass
+    # the tiny workload itself: every expert takes the two-pass dW split (few
+    # rows with large router weights); the one-pass path is covered by k16, e1024,
+    # k64, the random cases and the full-size workloads
     "tiny": lambda: (synth.TINY, synth.generate(synth.TINY)),
     # several 256-row tiles per expert with a ragged last tile of 129..255 rows (the
     # skewed case below has last tiles of <= 128 rows, whose second wave row is all
@@ -86,7 +87,8 @@ SMALL = {
                                   dead=(2, 5, 7)),
     # a single expert, K = 1: the dense SwiGLU MLP
     "one_expert": lambda: _custom(T=130, D=64, I=64, E=1, K=1, score=0, seed=104),
-    # every expert chosen by every token (K = E)
+    # every expert chosen by every token (K = E); three of the four take the
+    # two-pass dW split, one a single pass
     "k_equals_e": lambda: _custom(T=100, D=128, I=64, E=4, K=4, score=0, seed=105),
     # sigmoid score, top-1 (the Scout reading) at a small size
     "sigmoid_top1": lambda: _custom(T=257, D=192, I=128, E=4, K=1, score=1, seed=106),
