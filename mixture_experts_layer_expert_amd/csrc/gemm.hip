@@ -259,8 +259,9 @@ __device__ __forceinline__ void strip_put(char* stg, int row, int col, V v) {
 }
 
 // Copies the staged strip out: strip row r (< nrows) goes to the byte address
-// row_ptr(r) of its column 0; chunks past ncols columns are skipped.  op(dst,
-// v) stores (or accumulates) one 16-byte chunk.
+// row_ptr(r, h) of its column 0, h being the copy instruction (r = h * RPI +
+// lane / CPR); chunks past ncols columns are skipped.  op(dst, v) stores (or
+// accumulates) one 16-byte chunk.
 template <class S, class RowPtr, class Op>
 __device__ __forceinline__ void strip_out(const char* stg, int lane, int nrows, int ncols,
                                           RowPtr row_ptr, Op op) {
@@ -268,7 +269,7 @@ __device__ __forceinline__ void strip_out(const char* stg, int lane, int nrows, 
   for (int h = 0; h < 16 / S::RPI; ++h) {
     const int r = h * S::RPI + lane / S::CPR, ch = lane % S::CPR;
     const u32x4 v = *(const u32x4*)(stg + r * S::SP + ch * 16);
-    if (r < nrows && ch * (16 / S::ELEM) < ncols) op(row_ptr(r) + ch * 16, v);
+    if (r < nrows && ch * (16 / S::ELEM) < ncols) op(row_ptr(r, h) + ch * 16, v);
   }
 }
 
@@ -767,12 +768,12 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       }
       const int nrows = rows_valid - rb, ncols = p.N - col0;
       if constexpr (MODE == kGateUpH) {
-        strip_out<S>(stg, lane, nrows, ncols, [&](int r) {
+        strip_out<S>(stg, lane, nrows, ncols, [&](int r, int) {
           return (char*)(p.C0 + (size_t)(m0 + rb + r) * p.ldc + col0); }, store16);
       } else {
-        strip_out<S>(stg, lane, nrows, ncols, [&](int r) {
+        strip_out<S>(stg, lane, nrows, ncols, [&](int r, int) {
           return (char*)(p.Cf + (size_t)(m0 + rb + r) * p.ldc + col0); }, store16);
-        strip_out<S>(stg + S::BYTES, lane, nrows, ncols, [&](int r) {
+        strip_out<S>(stg + S::BYTES, lane, nrows, ncols, [&](int r, int) {
           return (char*)(p.Cf2 + (size_t)(m0 + rb + r) * p.ldc + col0); }, store16);
       }
     }
@@ -781,6 +782,21 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     static_assert(NW * S::BYTES <= NS * STAGE_BYTES, "staging fits the stage buffers");
     char* const stg = lds + wave * S::BYTES;
     const int col0 = n0 + wn * WTN;
+    // dXs: the flat slots of the rows this lane copies out, all read before
+    // the first store.  Read next to the stores, each read would wait for
+    // every store issued before it (loads and stores retire in issue order
+    // under one counter), a store round trip per copy instruction.
+    constexpr int NH = 16 / S::RPI;
+    int flat[MODE == kDXs ? FM : 1][NH];
+    if constexpr (MODE == kDXs) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const int r = wm * WTM + i * 16 + h * S::RPI + lane / S::CPR;
+          flat[i][h] = p.s2f[m0 + (r < rows_valid ? r : 0)];
+        }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int rb = wm * WTM + i * 16;
@@ -795,10 +811,10 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       if constexpr (MODE == kDXs) {
         // fp32 rows at their flat slot t*K + k: the K copies of a token sit
         // together for the reduction
-        strip_out<S>(stg, lane, nrows, ncols, [&](int r) {
-          return (char*)(p.Cf + (size_t)p.s2f[m0 + rb + r] * p.ldc + col0); }, store16);
+        strip_out<S>(stg, lane, nrows, ncols, [&](int, int h) {
+          return (char*)(p.Cf + (size_t)flat[i][h] * p.ldc + col0); }, store16);
       } else {
-        strip_out<S>(stg, lane, nrows, ncols, [&](int r) {
+        strip_out<S>(stg, lane, nrows, ncols, [&](int r, int) {
           return (char*)(p.C0 + (size_t)(m0 + rb + r) * p.ldc + col0); }, store16);
       }
     }
@@ -824,12 +840,48 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
                             (size_t)p.ldc, (size_t)p.ldc, (size_t)I};
     // the low parts are read only by the dW GEMMs of experts with a split operand
     const bool need_lo = p.dw_split[e] != 0;
+    // The router weights of the lane's FM rows are read up front and the G|U
+    // values one row block ahead of their use: the compiler cannot move a
+    // block's loads above the previous block's output stores (it cannot rule
+    // out aliasing), so each block would otherwise wait a full memory latency
+    // (two, with the sort-permutation read in front of the weight read).  The
+    // loads are unconditional, from clamped in-bounds addresses (row m0, column
+    // 0), and padding is zeroed where the values are used: a load under a
+    // branch makes the compiler's wait counts assume the worst at the join,
+    // which would wait for the next block's loads too.
+    auto src_of = [&](int i) {
+      const int r = wm * WTM + i * 16 + frow;
+      return p.s2f[m0 + (r < rows_valid ? r : 0)];
+    };
+    int src_next = src_of(0);
+    float wr_next = p.topk_w[src_next];
+    if (FM > 1) src_next = src_of(1);
+    f32x4 gbuf[2][FN], ubuf[2][FN];
+    auto load_gu = [&](int i, f32x4 (&gv)[FN], f32x4 (&uv)[FN]) {
+      const int r = wm * WTM + i * 16 + frow;
+      const size_t m = (size_t)(m0 + (r < rows_valid ? r : 0));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn * WTN + j * 16 + cq;
+        const float* src = p.GU + m * (2 * (size_t)I) + (col < I ? col : 0);
+        gv[j] = *(const f32x4*)src;
+        uv[j] = *(const f32x4*)(src + I);
+      }
+    };
+    load_gu(0, gbuf[0], ubuf[0]);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      // block i + 1's G|U, its router weight, and block i + 2's source row
+      const float wr_i = wr_next;
+      if (i + 1 < FM) {
+        load_gu(i + 1, gbuf[(i + 1) & 1], ubuf[(i + 1) & 1]);
+        wr_next = p.topk_w[src_next];
+        if (i + 2 < FM) src_next = src_of(i + 2);
+      }
       const int r = wm * WTM + i * 16 + frow;
       const bool row_ok = r < rows_valid;
       const size_t m = (size_t)(m0 + (row_ok ? r : 0));
-      const float wr = row_ok ? p.topk_w[p.s2f[m]] : 0.0f;
+      const float wr = row_ok ? wr_i : 0.0f;
       const float wrs = wr * gsc;  // dG, dU carry the gradient scale
       float dot = 0.0f;
 #pragma unroll
@@ -837,11 +889,8 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
         const int cl = j * 16 + cq;  // column within the wave's WTN
         const int col = n0 + wn * WTN + cl;
         const bool ok = row_ok && col < I;
-        f32x4 gv = {0.f, 0.f, 0.f, 0.f}, uv = {0.f, 0.f, 0.f, 0.f};
-        if (ok) {
-          gv = *(const f32x4*)(p.GU + m * (2 * (size_t)I) + col);
-          uv = *(const f32x4*)(p.GU + m * (2 * (size_t)I) + I + col);
-        }
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 gv = ok ? gbuf[i & 1][j] : zero, uv = ok ? ubuf[i & 1][j] : zero;
         float dg[4], du[4], hw[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -909,7 +958,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       const int rb = wm * WTM + i * 16;
 #pragma unroll
       for (int j = 0; j < FN; ++j) strip_put<S>(stg, frow, j * 16 + cq, acc[i][j]);
-      strip_out<S>(stg, lane, rows_valid - rb, p.N - col0, [&](int r) {
+      strip_out<S>(stg, lane, rows_valid - rb, p.N - col0, [&](int r, int) {
         return (char*)(out + (size_t)(m0 + rb + r) * p.N + col0); },
         [&](char* dst, u32x4 v) {
           f32x4 x = __builtin_bit_cast(f32x4, v) * ginv;
