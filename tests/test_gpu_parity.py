@@ -92,6 +92,11 @@ SMALL = {
     "k_equals_e": lambda: _custom(T=100, D=128, I=64, E=4, K=4, score=0, seed=105),
     # sigmoid score, top-1 (the Scout reading) at a small size
     "sigmoid_top1": lambda: _custom(T=257, D=192, I=128, E=4, K=1, score=1, seed=106),
+    # 33 experts of about 20 rows each, top-1 sigmoid (router weights near 1): the
+    # few-row experts whose one-pass dW reached 0.77 of the bar before the split
+    # rule weighed the row count; now they take the two-pass split
+    "few_rows_sigmoid": lambda: _custom(T=652, D=320, I=64, E=33, K=1, score=1, seed=512,
+                                        dead=(22, 31)),
     # one token
     "one_token": lambda: _custom(T=1, D=64, I=64, E=8, K=2, score=0, seed=107),
     # the maximum expert count: 1024 experts, most of them empty
