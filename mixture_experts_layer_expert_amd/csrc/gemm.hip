@@ -840,11 +840,12 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
                             (size_t)p.ldc, (size_t)p.ldc, (size_t)I};
     // the low parts are read only by the dW GEMMs of experts with a split operand
     const bool need_lo = p.dw_split[e] != 0;
-    // The router weights of the lane's FM rows are read up front and the G|U
-    // values one row block ahead of their use: the compiler cannot move a
-    // block's loads above the previous block's output stores (it cannot rule
-    // out aliasing), so each block would otherwise wait a full memory latency
-    // (two, with the sort-permutation read in front of the weight read).  The
+    // The G|U values and the router weight of each 16-row block are read one
+    // block ahead of their use, the sort-permutation entry behind the weight
+    // two blocks ahead: the compiler cannot move a block's loads above the
+    // previous block's output stores (it cannot rule out aliasing), so each
+    // block would otherwise wait a full memory latency (two, with the
+    // permutation read in front of the weight read).  The
     // loads are unconditional, from clamped in-bounds addresses (row m0, column
     // 0), and padding is zeroed where the values are used: a load under a
     // branch makes the compiler's wait counts assume the worst at the join,
