@@ -386,3 +386,10 @@ def test_empty_batch_layer():
     assert y.shape == (0, D)
     for k in ("dw_gate", "dw_up", "dw_down"):
         assert not out[k].any()
+    # accumulating: every expert has no rows, so the gradients stay as they were
+    acc = {k: torch.full_like(out[k], 1.5) for k in ("dw_gate", "dw_up", "dw_down")}
+    acc["dx"], acc["d_topk_w"] = out["dx"], out["d_topk_w"]
+    out2 = moe.moe_bwd(x, wg, wg, wd, route, x, K, 0, out=acc, accumulate_dw=True)
+    torch.cuda.synchronize()
+    for k in ("dw_gate", "dw_up", "dw_down"):
+        assert bool((out2[k] == 1.5).all()), f"{k} changed by an empty accumulating backward"
