@@ -137,12 +137,40 @@ def cpu_baseline(wl: synth.Workload, data: dict, n_tokens: int) -> dict:
     t2 = time.perf_counter()
     rows = n_tokens * wl.K
     flops = 18.0 * wl.D * wl.I * rows
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = oracle.threads()
+    host = host_cpu()
     return {"value": flops / (t2 - t0) / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", **host,
             "sample": (f"first {n_tokens} tokens ({rows} routed rows) of the {wl.name} workload: "
                        f"oracle forward {t1 - t0:.2f} s + backward incl. weight gradients "
-                       f"{t2 - t1:.2f} s, float64, {threads} OpenMP threads")}
+                       f"{t2 - t1:.2f} s, float64, {threads} OpenMP threads on "
+                       f"{host['cpu_model']}")}
+
+
+def host_cpu() -> dict:
+    """The host CPU: model string, logical CPUs of the machine and of this process."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": usable, "cpus_on_host": os.cpu_count() or usable}
+
+
+def step_stats(step_ms: list) -> dict:
+    """Median, 10th and 90th percentile and spread of per-step times (ms)."""
+    a = np.sort(np.asarray(step_ms, dtype=np.float64))
+    return {"median": round(float(np.median(a)), 4),
+            "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4),
+            "min": round(float(a[0]), 4), "max": round(float(a[-1]), 4), "n": int(a.size)}
 
 
 def main() -> int:
@@ -218,15 +246,20 @@ def main() -> int:
     dom = max(gemms, key=lambda k: gemms[k][0])
 
     # timed region: K full steps; only the dominant kernel is bracketed by HIP
-    # events (on its launch stream), for its live average duration
+    # events (on its launch stream), for its live average duration, and an
+    # event on the launch stream marks every step boundary (per-step times)
     moe.moe_prof_only(dom)
     moe.moe_prof_enable(True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     dom_ms, dom_n = moe.moe_prof_read()[dom]
     moe.moe_prof_enable(False)
     moe.moe_prof_only(None)
@@ -304,6 +337,7 @@ def main() -> int:
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "step_ms": step_stats(step_ms),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}_fwd_bwd", "T": wl.T, "D": wl.D, "I": wl.I, "E": wl.E,

@@ -165,8 +165,10 @@ moe_status moe_bwd(const moe_dims *dims, const void *x, const void *w_gate, cons
  *   w_r      device fp32 [D, E]   router projection (note: [in, out], so that
  *                                 logits = x w_r)
  *   logits   device fp32 [T, E]   out
- * Computed on the fp32 matrix cores (bf16 x converted exactly to fp32), fp32
- * accumulation.  Only dims->T, D, E are used; the other dims must still be
+ * Computed on the bf16 matrix cores: each fp32 weight is split exactly into
+ * three bf16 terms (w0 = bf16(w), w1 = bf16(w - w0), w2 = w - w0 - w1), every
+ * product of a bf16 x with a term is exact in fp32, and the three products are
+ * accumulated in fp32 -- the precision of fp32 products at the bf16 rate.  Only dims->T, D, E are used; the other dims must still be
  * valid (the router is part of the layer the dims describe). */
 moe_status moe_router_fwd(const moe_dims *dims, const void *x, const float *w_r, float *logits,
                           void *stream);
@@ -215,8 +217,10 @@ const char *moe_last_error(void);
  * recorded events and writes, for kernel ids 0..n-1, the summed elapsed time
  * in milliseconds and the number of launches since the last enable.  Kernel
  * ids run 0..moe_prof_num_kernels()-1; moe_prof_kernel_name() names them (NULL
- * for an unknown id).  Timing state is process-wide; do not enable it while
- * a stream is being captured into a graph.  Returns MOE_ERR_HIP if an event
+ * for an unknown id).  Timing state (the flag and the records) is process-wide
+ * and thread-safe; each launch's two events are paired per host thread.
+ * Launches on a stream that is being captured into a graph are not timed.
+ * Returns MOE_ERR_HIP if an event
  * query fails, MOE_ERR_BAD_ARG for null arrays with n > 0.
  * moe_prof_only(id) restricts the bracketing to one kernel id (-1: every
  * kernel, the default), so that a timed loop carries two events per launch

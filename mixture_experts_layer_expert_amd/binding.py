@@ -1,7 +1,7 @@
 """ctypes binding of libmoe (include/moe.h).
 
-Argument marshalling only: torch supplies device memory and the current HIP
-stream; every step of the layer runs in the library's HIP kernels.  There is
+Argument marshalling only: torch supplies device memory and the HIP stream
+(the current one, or the `stream=` argument); every step of the layer runs in the library's HIP kernels.  There is
 no CPU fallback: if the library is missing or a call fails, an exception is
 raised.
 """
@@ -138,10 +138,21 @@ def _ptr(t, dtype, shape, name):
     return _vp(t.data_ptr())
 
 
-def _stream(stream):
+def _launch_stream(stream):
+    """The stream the library's kernels go to: `stream`, else the current one."""
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
-    return _vp(s.cuda_stream)
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _alloc_on(stream):
+    """Context in which this call allocates its workspace and default outputs.
+
+    The caching allocator ties a block to the stream that was current when it
+    was allocated and hands it out again, once freed, only to later work on
+    that stream.  Allocating on the launch stream keeps a workspace freed when
+    the call returns from being reused by other streams while the kernels
+    queued on `stream` may still use it."""
+    return _torch().cuda.stream(stream)
 
 
 def _workspace(d, phase, ws, device):
@@ -164,14 +175,16 @@ def moe_route_sort(logits, K: int, score: int = MOE_SCORE_SOFTMAX_TOPK, *, out=N
     T, E = logits.shape
     d = dims(T, 64, 64, E, K, score)
     dev = logits.device
-    if out is None:
-        out = dict(topk_idx=torch.empty((T, K), dtype=torch.int32, device=dev),
-                   topk_w=torch.empty((T, K), dtype=torch.float32, device=dev),
-                   counts=torch.empty(E, dtype=torch.int32, device=dev),
-                   offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
-                   sorted_to_flat=torch.empty(T * K, dtype=torch.int32, device=dev),
-                   flat_to_sorted=torch.empty(T * K, dtype=torch.int32, device=dev))
-    ws, need = _workspace(d, MOE_PHASE_ROUTE, ws, dev)
+    st = _launch_stream(stream)
+    with _alloc_on(st):
+        if out is None:
+            out = dict(topk_idx=torch.empty((T, K), dtype=torch.int32, device=dev),
+                       topk_w=torch.empty((T, K), dtype=torch.float32, device=dev),
+                       counts=torch.empty(E, dtype=torch.int32, device=dev),
+                       offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                       sorted_to_flat=torch.empty(T * K, dtype=torch.int32, device=dev),
+                       flat_to_sorted=torch.empty(T * K, dtype=torch.int32, device=dev))
+        ws, need = _workspace(d, MOE_PHASE_ROUTE, ws, dev)
     i32, f32 = torch.int32, torch.float32
     rc = load_library().moe_route_sort(
         ctypes.byref(d), _ptr(logits, f32, (T, E), "logits"),
@@ -179,7 +192,7 @@ def moe_route_sort(logits, K: int, score: int = MOE_SCORE_SOFTMAX_TOPK, *, out=N
         _ptr(out["counts"], i32, (E,), "counts"), _ptr(out["offsets"], i32, (E + 1,), "offsets"),
         _ptr(out["sorted_to_flat"], i32, (T * K,), "sorted_to_flat"),
         _ptr(out["flat_to_sorted"], i32, (T * K,), "flat_to_sorted"),
-        _vp(ws.data_ptr()), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream))
+        _vp(ws.data_ptr()), ctypes.c_size_t(ws.numel() * ws.element_size()), _vp(st.cuda_stream))
     _check(rc, "moe_route_sort")
     return out
 
@@ -197,9 +210,11 @@ def moe_fwd(x, w_gate, w_up, w_down, route: dict, K: int, score: int = MOE_SCORE
     torch = _torch()
     d = _layer_dims(x, w_gate, K, score)
     T, D, I, E = d.T, d.D, d.I, d.E
-    if y is None:
-        y = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
-    ws, need = _workspace(d, MOE_PHASE_FWD, ws, x.device)
+    st = _launch_stream(stream)
+    with _alloc_on(st):
+        if y is None:
+            y = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+        ws, need = _workspace(d, MOE_PHASE_FWD, ws, x.device)
     b, i32, f32 = torch.bfloat16, torch.int32, torch.float32
     rc = load_library().moe_fwd(
         ctypes.byref(d), _ptr(x, b, (T, D), "x"), _ptr(w_gate, b, (E, I, D), "w_gate"),
@@ -208,7 +223,7 @@ def moe_fwd(x, w_gate, w_up, w_down, route: dict, K: int, score: int = MOE_SCORE
         _ptr(route["sorted_to_flat"], i32, (T * K,), "sorted_to_flat"),
         _ptr(route["flat_to_sorted"], i32, (T * K,), "flat_to_sorted"),
         _ptr(y, b, (T, D), "y"), _vp(ws.data_ptr()), ctypes.c_size_t(ws.numel() * ws.element_size()),
-        _stream(stream))
+        _vp(st.cuda_stream))
     _check(rc, "moe_fwd")
     return y
 
@@ -221,13 +236,15 @@ def moe_bwd(x, w_gate, w_up, w_down, route: dict, dy, K: int, score: int = MOE_S
     d = _layer_dims(x, w_gate, K, score)
     T, D, I, E = d.T, d.D, d.I, d.E
     dev = x.device
-    if out is None:
-        out = dict(dx=torch.empty((T, D), dtype=torch.bfloat16, device=dev),
-                   dw_gate=torch.empty((E, I, D), dtype=torch.float32, device=dev),
-                   dw_up=torch.empty((E, I, D), dtype=torch.float32, device=dev),
-                   dw_down=torch.empty((E, D, I), dtype=torch.float32, device=dev),
-                   d_topk_w=torch.empty((T, K), dtype=torch.float32, device=dev))
-    ws, need = _workspace(d, MOE_PHASE_BWD, ws, dev)
+    st = _launch_stream(stream)
+    with _alloc_on(st):
+        if out is None:
+            out = dict(dx=torch.empty((T, D), dtype=torch.bfloat16, device=dev),
+                       dw_gate=torch.empty((E, I, D), dtype=torch.float32, device=dev),
+                       dw_up=torch.empty((E, I, D), dtype=torch.float32, device=dev),
+                       dw_down=torch.empty((E, D, I), dtype=torch.float32, device=dev),
+                       d_topk_w=torch.empty((T, K), dtype=torch.float32, device=dev))
+        ws, need = _workspace(d, MOE_PHASE_BWD, ws, dev)
     b, i32, f32 = torch.bfloat16, torch.int32, torch.float32
     rc = load_library().moe_bwd(
         ctypes.byref(d), _ptr(x, b, (T, D), "x"), _ptr(w_gate, b, (E, I, D), "w_gate"),
@@ -239,7 +256,7 @@ def moe_bwd(x, w_gate, w_up, w_down, route: dict, dy, K: int, score: int = MOE_S
         _ptr(out["dw_gate"], f32, (E, I, D), "dw_gate"), _ptr(out["dw_up"], f32, (E, I, D), "dw_up"),
         _ptr(out["dw_down"], f32, (E, D, I), "dw_down"), _ptr(out["d_topk_w"], f32, (T, K), "d_topk_w"),
         ctypes.c_int32(1 if accumulate_dw else 0),
-        _vp(ws.data_ptr()), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream))
+        _vp(ws.data_ptr()), ctypes.c_size_t(ws.numel() * ws.element_size()), _vp(st.cuda_stream))
     _check(rc, "moe_bwd")
     return out
 
@@ -255,12 +272,14 @@ def moe_router_fwd(x, w_r, *, logits=None, stream=None):
     torch = _torch()
     d = _router_dims(x, w_r, 1, MOE_SCORE_SOFTMAX_TOPK)
     T, D, E = d.T, d.D, d.E
+    st = _launch_stream(stream)
     if logits is None:
-        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+        with _alloc_on(st):
+            logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
     rc = load_library().moe_router_fwd(
         ctypes.byref(d), _ptr(x, torch.bfloat16, (T, D), "x"),
         _ptr(w_r, torch.float32, (D, E), "w_r"), _ptr(logits, torch.float32, (T, E), "logits"),
-        _stream(stream))
+        _vp(st.cuda_stream))
     _check(rc, "moe_router_fwd")
     return logits
 
@@ -273,16 +292,18 @@ def moe_router_bwd(x, w_r, route: dict, d_topk_w, dx, K: int,
     torch = _torch()
     d = _router_dims(x, w_r, K, score)
     T, D, E = d.T, d.D, d.E
-    if dw_r is None:
-        dw_r = torch.empty((D, E), dtype=torch.float32, device=x.device)
-    ws, need = _workspace(d, MOE_PHASE_ROUTER_BWD, ws, x.device)
+    st = _launch_stream(stream)
+    with _alloc_on(st):
+        if dw_r is None:
+            dw_r = torch.empty((D, E), dtype=torch.float32, device=x.device)
+        ws, need = _workspace(d, MOE_PHASE_ROUTER_BWD, ws, x.device)
     b, i32, f32 = torch.bfloat16, torch.int32, torch.float32
     rc = load_library().moe_router_bwd(
         ctypes.byref(d), _ptr(x, b, (T, D), "x"), _ptr(w_r, f32, (D, E), "w_r"),
         _ptr(route["topk_idx"], i32, (T, K), "topk_idx"), _ptr(route["topk_w"], f32, (T, K), "topk_w"),
         _ptr(d_topk_w, f32, (T, K), "d_topk_w"), _ptr(dx, b, (T, D), "dx"),
         _ptr(dw_r, f32, (D, E), "dw_r"), ctypes.c_int32(1 if accumulate_dwr else 0),
-        _vp(ws.data_ptr()), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream))
+        _vp(ws.data_ptr()), ctypes.c_size_t(ws.numel() * ws.element_size()), _vp(st.cuda_stream))
     _check(rc, "moe_router_bwd")
     return dw_r
 

@@ -1,7 +1,11 @@
 // Optional per-kernel timing: when enabled, every kernel launch of the
 // library is bracketed by two hipEvents recorded on the launch stream; the
 // host later sums the elapsed times per kernel.  Off by default; when off the
-// launch path does nothing extra.
+// launch path reads one atomic flag and does nothing else.  A launch's two
+// events are paired per host thread, so launches from several threads are
+// timed correctly; launches on a stream that is being captured into a graph
+// are not timed (no event records end up in the graph).
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -16,13 +20,19 @@ struct Rec {
   hipEvent_t start, stop;
 };
 
-std::mutex mu;
-bool enabled = false;
+std::mutex mu;  // guards recs, pool, only_kid
+std::atomic<bool> enabled{false};
 int only_kid = -1;  // >= 0: bracket only this kernel id
 std::vector<Rec> recs;        // recorded since the last enable
 std::vector<hipEvent_t> pool;  // reusable events
-int open_kid = -1;
-hipEvent_t open_start = nullptr;
+// the launch this host thread has begun and not yet ended
+thread_local int open_kid = -1;
+thread_local hipEvent_t open_start = nullptr;
+
+bool capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
+}
 
 const char* const kNames[kNumKernels] = {
     "route_topk",   "route_hist",    "route_scatter", "tilemap",
@@ -54,7 +64,8 @@ void recycle() {
 }  // namespace
 
 void begin(int kid, hipStream_t st) {
-  if (!enabled) return;
+  open_kid = -1;
+  if (!enabled.load(std::memory_order_acquire) || capturing(st)) return;
   std::lock_guard<std::mutex> g(mu);
   if (only_kid >= 0 && kid != only_kid) return;
   hipEvent_t e = take();
@@ -65,14 +76,21 @@ void begin(int kid, hipStream_t st) {
 }
 
 void end(hipStream_t st) {
-  if (!enabled) return;
-  std::lock_guard<std::mutex> g(mu);
   if (open_kid < 0) return;
-  hipEvent_t e = take();
-  if (!e) return;
-  hipEventRecord(e, st);
-  recs.push_back(Rec{open_kid, open_start, e});
+  std::lock_guard<std::mutex> g(mu);
+  const int kid = open_kid;
   open_kid = -1;
+  if (!enabled.load(std::memory_order_acquire)) {  // disabled in between: drop the pair
+    pool.push_back(open_start);
+    return;
+  }
+  hipEvent_t e = take();
+  if (!e) {
+    pool.push_back(open_start);
+    return;
+  }
+  hipEventRecord(e, st);
+  recs.push_back(Rec{kid, open_start, e});
 }
 
 const char* name(int kid) { return (kid >= 0 && kid < kNumKernels) ? kNames[kid] : nullptr; }
@@ -80,8 +98,7 @@ const char* name(int kid) { return (kid >= 0 && kid < kNumKernels) ? kNames[kid]
 int set_enabled(int on) {
   std::lock_guard<std::mutex> g(mu);
   recycle();
-  open_kid = -1;
-  enabled = on != 0;
+  enabled.store(on != 0, std::memory_order_release);
   return 0;
 }
 

@@ -208,3 +208,10 @@ def router_backward(x: np.ndarray, w_r: np.ndarray, idx, w, drw, score: int):
     _check(lib.moe_oracle_router_backward(ctypes.byref(d), _p(x), _p(w_r), _p(idx), _p(w),
                                           _p(drw), _p(dl), _p(dw_r), _p(dx_r)), "router_backward")
     return dl, dw_r, dx_r
+
+
+def threads() -> int:
+    """Number of OpenMP threads the oracle's parallel loops use."""
+    lib = _load()
+    lib.moe_oracle_threads.restype = ctypes.c_int32
+    return int(lib.moe_oracle_threads())

@@ -44,6 +44,7 @@
  * the projection weights and the layer input.
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -541,3 +542,6 @@ int moe_oracle_router_backward(const moe_oracle_dims *d, const double *x,
     }
     return ORACLE_OK;
 }
+
+/* Threads the OpenMP loops above run on (what a timing of the oracle used). */
+int32_t moe_oracle_threads(void) { return (int32_t)omp_get_max_threads(); }

@@ -32,3 +32,11 @@ def test_gemm_flops_add_up_to_the_counted_step():
     total = sum(a for n, (b, a) in work.items() if b == "mfma")
     assert total == (18 + 4) * wl.D * wl.I * wl.R
     assert wl.flops_fwd() + wl.flops_bwd() == 18 * wl.D * wl.I * wl.R
+
+
+def test_step_stats_and_host_cpu():
+    st = bench.step_stats([3.0, 1.0, 2.0, 4.0, 5.0])
+    assert st["median"] == 3.0 and st["min"] == 1.0 and st["max"] == 5.0 and st["n"] == 5
+    assert st["p10"] <= st["median"] <= st["p90"]
+    h = bench.host_cpu()
+    assert h["nproc"] >= 1 and h["cpus_on_host"] >= h["nproc"] and isinstance(h["cpu_model"], str)
