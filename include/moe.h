@@ -21,7 +21,9 @@
  *     row-major (last index contiguous), 16-byte aligned.  bf16 arrays are
  *     passed as `void*` (raw bfloat16 bits).
  *   - The caller owns every buffer, including the workspace; the library never
- *     allocates, frees or keeps a pointer after the call returns.
+ *     allocates, frees or keeps a pointer after the call returns (the one
+ *     exception, moe_route_sort_noalloc, uses a static device array of the
+ *     library's own instead of a workspace).
  *   - `stream` is a hipStream_t passed as `void*` (NULL = the default stream).
  *     Work is enqueued asynchronously; nothing synchronises with the host.
  *   - Host-side validation only.  On any error nothing is launched and the
@@ -48,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* Router score functions. */
 #define MOE_SCORE_SOFTMAX_TOPK 0 /* softmax over E, keep top K, renormalise over the K */
@@ -64,6 +66,9 @@ extern "C" {
                                     >= 2^31 (at D = 2048, I = 768, K = 8: T <= 65535) */
 #define MOE_ERR_WORKSPACE 3      /* workspace smaller than moe_workspace_bytes() */
 #define MOE_ERR_HIP 4            /* a HIP launch or runtime call failed */
+#define MOE_ERR_SCRATCH 5        /* the shape needs more than the static scratch buffer of
+                                    moe_route_sort_noalloc (never for dims that pass the
+                                    other checks: E <= 1024 needs at most 1 MiB) */
 
 /* Workspace phases for moe_workspace_bytes(). */
 #define MOE_PHASE_ROUTE 0
@@ -103,6 +108,21 @@ moe_status moe_route_sort(const moe_dims *dims, const float *logits, int32_t *to
                           float *topk_w, int32_t *counts, int32_t *offsets,
                           int32_t *sorted_to_flat, int32_t *flat_to_sorted, void *ws,
                           size_t ws_bytes, void *stream);
+
+/* moe_route_sort without a workspace, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments (minus ws, ws_bytes), same kernels and bitwise
+ * the same outputs as moe_route_sort.  The per-block expert histograms live in
+ * a static 1 MiB device array inside the library, one copy per GPU, held until
+ * the process ends and looked up on each device's first call; the call
+ * allocates and frees nothing.  Every call on one GPU shares that array, so
+ * calls that overlap on one GPU (concurrent streams, or host threads) race:
+ * serialise them.  MOE_ERR_SCRATCH if the shape would need more than 1 MiB of
+ * histograms (at most E * 256 blocks * 4 bytes, so no accepted shape does). */
+moe_status moe_route_sort_noalloc(const moe_dims *dims, const float *logits, int32_t *topk_idx,
+                                  float *topk_w, int32_t *counts, int32_t *offsets,
+                                  int32_t *sorted_to_flat, int32_t *flat_to_sorted,
+                                  void *stream);
 
 /* Forward ("LigerMoE design / Forward pass"): grouped gate/up GEMM over the
  * routed rows in expert order (gathered from x inside the GEMM's operand

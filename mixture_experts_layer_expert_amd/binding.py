@@ -57,6 +57,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.moe_workspace_bytes.argtypes = [ctypes.POINTER(moe_dims), ctypes.c_int32]
         lib.moe_route_sort.restype = ctypes.c_int32
         lib.moe_route_sort.argtypes = [ctypes.POINTER(moe_dims)] + [_vp] * 7 + [_vp, ctypes.c_size_t, _vp]
+        lib.moe_route_sort_noalloc.restype = ctypes.c_int32
+        lib.moe_route_sort_noalloc.argtypes = [ctypes.POINTER(moe_dims)] + [_vp] * 7 + [_vp]
         lib.moe_fwd.restype = ctypes.c_int32
         lib.moe_fwd.argtypes = [ctypes.POINTER(moe_dims)] + [_vp] * 9 + [_vp, ctypes.c_size_t, _vp]
         lib.moe_bwd.restype = ctypes.c_int32
@@ -194,6 +196,26 @@ def moe_route_sort(logits, K: int, score: int = MOE_SCORE_SOFTMAX_TOPK, *, out=N
         _ptr(out["flat_to_sorted"], i32, (T * K,), "flat_to_sorted"),
         _vp(ws.data_ptr()), ctypes.c_size_t(ws.numel() * ws.element_size()), _vp(st.cuda_stream))
     _check(rc, "moe_route_sort")
+    return out
+
+
+def moe_route_sort_noalloc(logits, K: int, score: int = MOE_SCORE_SOFTMAX_TOPK, *, out,
+                           stream=None) -> dict:
+    """moe_route_sort without a workspace: the library's static scratch holds the
+    histograms.  `out` (the dict moe_route_sort returns) must be given, so that
+    the call allocates nothing."""
+    torch = _torch()
+    T, E = logits.shape
+    d = dims(T, 64, 64, E, K, score)
+    st = _launch_stream(stream)
+    i32, f32 = torch.int32, torch.float32
+    rc = load_library().moe_route_sort_noalloc(
+        ctypes.byref(d), _ptr(logits, f32, (T, E), "logits"),
+        _ptr(out["topk_idx"], i32, (T, K), "topk_idx"), _ptr(out["topk_w"], f32, (T, K), "topk_w"),
+        _ptr(out["counts"], i32, (E,), "counts"), _ptr(out["offsets"], i32, (E + 1,), "offsets"),
+        _ptr(out["sorted_to_flat"], i32, (T * K,), "sorted_to_flat"),
+        _ptr(out["flat_to_sorted"], i32, (T * K,), "flat_to_sorted"), _vp(st.cuda_stream))
+    _check(rc, "moe_route_sort_noalloc")
     return out
 
 

@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kernels.hpp"
 
@@ -244,6 +245,78 @@ MOE_EXPORT moe_status moe_route_sort(const moe_dims* dims, const float* logits,
   return hip_status(launch_route_sort(*dims, logits, topk_idx, topk_w, counts, offsets,
                                       sorted_to_flat, flat_to_sorted, hist, (hipStream_t)stream),
                     "route_sort");
+}
+
+// ---- allocation-free routing
+//
+// moe_route_sort_noalloc runs the same kernels as moe_route_sort, with the
+// per-block expert histograms in `scratch` instead of a caller workspace.
+// Each GPU the library runs on holds its own copy of the array until the
+// process ends; host code reaches it only through the device address that
+// hipGetSymbolAddress returns on that device (the array's name in host code
+// is a stand-in, not a device address).  The histograms are fully written by
+// the histogram kernel before the scatter kernel reads them, so nothing needs
+// clearing between calls, but calls that overlap on one GPU share the array
+// and race.
+namespace moe {
+namespace {
+
+constexpr size_t kScratchBytes = size_t(1) << 20;  // >= E * 256 blocks * 4 for every E <= 1024
+constexpr int kMaxDevices = 64;
+static_assert((size_t)kMaxE * 256 * sizeof(int32_t) <= kScratchBytes,
+              "the routing histograms of every accepted shape fit the scratch buffer");
+
+static __device__ __align__(256) int32_t scratch[kScratchBytes / sizeof(int32_t)];
+
+std::mutex scratch_mutex;
+void* scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+hipError_t scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_addr[dev] = p;
+  }
+  *out = scratch_addr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+}  // namespace moe
+
+MOE_EXPORT moe_status moe_route_sort_noalloc(const moe_dims* dims, const float* logits,
+                                             int32_t* topk_idx, float* topk_w, int32_t* counts,
+                                             int32_t* offsets, int32_t* sorted_to_flat,
+                                             int32_t* flat_to_sorted, void* stream) {
+  moe_status s = check_dims(dims);
+  if (s != MOE_OK) return s;
+  const size_t R = (size_t)dims->T * dims->K;
+  if (!ptr_ok(logits, (size_t)dims->T * dims->E, 4) || !ptr_ok(topk_idx, R, 4) ||
+      !ptr_ok(topk_w, R, 4) || !ptr_ok(sorted_to_flat, R, 4) || !ptr_ok(flat_to_sorted, R, 4) ||
+      !ptr_ok(counts, dims->E, 4) || !ptr_ok(offsets, dims->E + 1, 4))
+    return MOE_ERR_BAD_ARG;
+  int32_t* hist;
+  const size_t need = route_ws(*dims, &hist, nullptr);
+  clear_stale_error();
+  if (need > kScratchBytes) {
+    snprintf(last_error, sizeof(last_error),
+             "route_sort_noalloc: %zu bytes of histograms exceed the %zu-byte static scratch", need,
+             kScratchBytes);
+    return MOE_ERR_SCRATCH;
+  }
+  void* base = nullptr;
+  MOE_TRY(scratch_ptr(&base));
+  route_ws(*dims, &hist, base);
+  return hip_status(launch_route_sort(*dims, logits, topk_idx, topk_w, counts, offsets,
+                                      sorted_to_flat, flat_to_sorted, hist, (hipStream_t)stream),
+                    "route_sort_noalloc");
 }
 
 MOE_EXPORT moe_status moe_fwd(const moe_dims* dims, const void* x, const void* w_gate,
@@ -528,6 +601,7 @@ MOE_EXPORT const char* moe_status_string(moe_status status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape (D and I must be multiples of 64, E <= 1024, K <= 64)";
     case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes()";
     case MOE_ERR_HIP: return "HIP launch or runtime error";
+    case MOE_ERR_SCRATCH: return "shape needs more than the static scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

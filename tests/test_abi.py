@@ -36,7 +36,7 @@ def test_no_torch_dependency(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     for code in range(6):
         assert moe.status_string(code)
 
@@ -102,6 +102,32 @@ def test_bad_dims_rejected(lib, dims, code):
     d = moe.dims(*dims)
     assert _fwd(lib, d) == code
     assert lib.moe_route_sort(ctypes.byref(d), *([FAKE] * 8), ctypes.c_size_t(1 << 40), None) == code
+    assert lib.moe_route_sort_noalloc(ctypes.byref(d), *([FAKE] * 7), None) == code
+
+
+def test_noalloc_route_validates_before_touching_a_device(lib):
+    """The allocation-free routing call checks its arguments on the host first
+    (no device is needed to reject them)."""
+    d = moe.dims(16, 64, 64, 4, 2)
+    assert lib.moe_route_sort_noalloc(None, *([FAKE] * 7), None) == 1
+    assert lib.moe_route_sort_noalloc(ctypes.byref(d), ctypes.c_void_p(0), *([FAKE] * 6),
+                                      None) == 1                        # null logits
+    assert lib.moe_route_sort_noalloc(ctypes.byref(d), FAKE, ctypes.c_void_p((1 << 20) + 2),
+                                      *([FAKE] * 5), None) == 1         # misaligned topk_idx
+
+
+def test_noalloc_route_source_allocates_nothing():
+    """moe_route_sort_noalloc and its scratch lookup call no allocating routine."""
+    src = open(os.path.join(os.path.dirname(moe.__file__), "csrc", "abi.hip")).read()
+    start = src.index("// ---- allocation-free routing")
+    end = src.index("MOE_EXPORT moe_status moe_fwd(")
+    body = src[start:end]
+    assert "hipGetSymbolAddress" in body and "HIP_SYMBOL(scratch)" in body
+    for banned in ("hipMalloc", "hipFree", "hipHostMalloc", "hipExtMalloc", "hipMallocAsync",
+                   "new ", "malloc("):
+        assert banned not in body, banned
+    # kernels get the looked-up device address, never the host-side name of the array
+    assert "launch_route_sort(" in body and "scratch," not in body.split("launch_route_sort(")[1]
 
 
 def test_bad_pointers_and_workspace(lib):
