@@ -3,8 +3,8 @@
 
 One step = the whole hot path over one batch: routing + sort by expert,
 forward (gate/up GEMM + SwiGLU over the routed rows gathered in its loads,
-down GEMM, weighted combine) and backward (recompute, dA + SwiGLU backward,
-dX GEMM, dW GEMMs, all gathering x / dy rows in their loads; dX and
+down GEMM, weighted combine) and backward (dA GEMM, recompute + SwiGLU
+backward, dX GEMM, dW GEMMs, all gathering x / dy rows in their loads; dX and
 dRouterWeights reductions), all through the C ABI on device-resident
 inputs.  Workload: the Qwen3-30B-A3B layer shape (T=8192 tokens, D=2048,
 I=768, E=128 experts, top-8, softmax-renormalised routing), synthetic seeded
@@ -62,7 +62,9 @@ def kernel_work(wl: synth.Workload) -> dict:
         "combine": ("hbm", 2.0 * R * D + 8 * R + 2.0 * T * D),
         # dX reduce: read the fp32 per-row partials (R*D*4) and indices, write dX (T*D*2)
         "reduce_rows": ("hbm", 4.0 * R * D + 4 * R + 2.0 * T * D),
-        "reduce_partials": ("hbm", 4.0 * R * (2 * math.ceil(I / 256)) + 8 * R),
+        # dRouterWeights: read the per-row partials (one per gate/up column tile and wave
+        # column, 4 * ceil(I / 128) per row) and the indices, write one value per row
+        "reduce_partials": ("hbm", 4.0 * R * (4 * math.ceil(I / 128)) + 8 * R),
         "route_topk": ("hbm", 4.0 * T * E + 8 * R),
         "route_hist": ("hbm", 4.0 * R),
         # scatter: read the ids (4R) and the histogram table once, write both permutations (8R)

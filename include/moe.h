@@ -152,7 +152,9 @@ moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, cons
  *   dw_down   device fp32 [E, D, I] out: dL/dW_down
  *   d_topk_w  device fp32 [T, K]   out: dL/dtopk_w[t,k] = <dy[t], o[t,k]>
  *   accumulate_dw  0: overwrite dw_*;  1: add into dw_* (fp32)
- * The gate/up activations are recomputed (not read from the forward); the
+ * dA = dOu W_down runs first (fp32); the gate/up activations are then
+ * recomputed (not read from the forward), and the SwiGLU backward and the
+ * router-weight gradient come out of that recompute GEMM's epilogue; the
  * routed rows of x and dy are gathered inside the GEMMs' operand loads.  Each
  * weight-gradient tile reduces over its expert's rows in chunks of at most
  * 2048 rows, one workgroup per chunk; the chunks' partial tiles are added in

@@ -81,7 +81,7 @@ struct BwdWs {
   float* gscale;          // gradient scale {s, 1/s}
   f16_t *x16, *dy16;      // fp16 x and s dy, token-major: the dW GEMMs' exact operands
   float* dw_part;         // partial dW tiles of chunks 1.. of the chunked experts
-  float *gu, *dxs, *part;
+  float *da, *dxs, *part;  // dA [R, I], dX rows [R, D] (flat order), dRW partials
 };
 
 // dW row chunks: experts with more than kDwChunkRows rows (at most R / (chunk + 1)
@@ -100,8 +100,9 @@ int64_t dw_chunks_bound(const moe_dims& d) { return d.E + dw_part_slots(d); }
 // -1% per step at 512 rows per expert; +1.4% at 64)
 int gemm_lead(const moe_dims& d) { return (int64_t)d.T * d.K >= (int64_t)kLeadMinRows * d.E; }
 
-// router-weight-gradient partials per routed row: one per (column tile, wave column)
-int partials_per_row(const moe_dims& d) { return kGemmWN * ((d.I + kGemmBN - 1) / kGemmBN); }
+// router-weight-gradient partials per routed row: one per (gate/up column
+// tile, wave column) of the recompute GEMM
+int partials_per_row(const moe_dims& d) { return kGemmWN * (int)gateup_tiles(d.I); }
 
 size_t route_ws(const moe_dims& d, int32_t** hist, void* base) {
   Carve c{(char*)base};
@@ -138,7 +139,7 @@ size_t bwd_ws(const moe_dims& d, BwdWs* w, void* base) {
   w->x16 = c.take<f16_t>((size_t)d.T * d.D);
   w->dy16 = c.take<f16_t>((size_t)d.T * d.D);
   w->dw_part = c.take<float>(std::max<size_t>(1, (size_t)dw_part_slots(d) * 2 * d.I * d.D));
-  w->gu = c.take<float>(R * 2 * d.I);
+  w->da = c.take<float>(R * d.I);
   w->dgu = c.take<f16_t>(R * 2 * d.I);
   w->hw = c.take<f16_t>(R * d.I);
   w->dgu_lo = c.take<f16_t>(R * 2 * d.I);
@@ -404,8 +405,8 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   hipStream_t st = (hipStream_t)stream;
   clear_stale_error();
 
-  // which experts' dW operands are split hi + lo (read by the dA epilogue and
-  // the dW GEMMs), and the gradient scale from max|dy|
+  // which experts' dW operands are split hi + lo (read by the recompute
+  // GEMM's epilogue and the dW GEMMs), and the gradient scale from max|dy|
   MOE_TRY(launch_amax_bf16(dy, TD, w.amax_part, st));
   const float dim_factor = std::max(1.0f, 3.0f * (float)d.D / (8.0f * (float)d.I));
   MOE_TRY(launch_bwd_prep(offsets, sorted_to_flat, topk_w, d.E, dim_factor, w.amax_part,
@@ -425,7 +426,27 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   g.tstart = w.tstart;
   g.E = d.E;
   if (R > 0) {
-    // recompute G, U (fp32) into GU[R, 2I], the routed rows gathered from x
+    // dA = dOu Wd (fp32 [R, I]), dOu = the routed rows gathered from dy
+    g.A = (const bf16_t*)dy;
+    g.a_gather = sorted_to_flat;
+    g.a_div = d.K;
+    g.a_rows = d.T;
+    g.lda = d.D;
+    g.B0 = (const bf16_t*)w_down;
+    g.ldb = d.I;
+    g.N = d.I;
+    g.K = d.D;
+    g.n_tiles = (d.I + kGemmBN - 1) / kGemmBN;
+    g.Cf = w.da;
+    g.ldc = d.I;
+    MOE_TRY(launch_gemm(kDA, g, rowgrouped_grid(d, g.n_tiles), st));
+    // recompute G, U from the routed rows of x (gathered in the loads) and,
+    // in the epilogue, the SwiGLU backward from dA: dG | dU, Hw (fp16 hi and,
+    // for split experts, lo) and the router-weight partials
+    g = GemmArgs{};
+    g.offsets = offsets;
+    g.tstart = w.tstart;
+    g.E = d.E;
     g.A = (const bf16_t*)x;
     g.a_gather = sorted_to_flat;
     g.a_div = d.K;
@@ -438,25 +459,6 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
     g.K = d.D;
     g.n_tiles = (int)gateup_tiles(d.I);
     g.lead = gemm_lead(d);
-    g.Cf = w.gu;
-    g.Cf2 = w.gu + d.I;
-    g.ldc = 2 * d.I;
-    MOE_TRY(launch_gemm(kGateUpGU, g, rowgrouped_grid(d, g.n_tiles), st));
-    // dA = dOu Wd, SwiGLU backward, Hw, router-weight partials
-    g = GemmArgs{};
-    g.offsets = offsets;
-    g.tstart = w.tstart;
-    g.E = d.E;
-    g.A = (const bf16_t*)dy;  // dOu: the routed rows gathered from dy
-    g.a_gather = sorted_to_flat;
-    g.a_div = d.K;
-    g.a_rows = d.T;
-    g.lda = d.D;
-    g.B0 = (const bf16_t*)w_down;
-    g.ldb = d.I;
-    g.N = d.I;
-    g.K = d.D;
-    g.n_tiles = (d.I + kGemmBN - 1) / kGemmBN;
     g.C0 = w.dgu;
     g.C1 = w.dgu + d.I;
     g.C2 = w.hw;
@@ -464,14 +466,14 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
     g.L1 = w.dgu_lo + d.I;
     g.L2 = w.hw_lo;
     g.ldc = 2 * d.I;
-    g.GU = w.gu;
+    g.DA = w.da;
     g.topk_w = topk_w;
     g.s2f = sorted_to_flat;
     g.part = w.part;
     g.np = partials_per_row(d);
     g.dw_split = w.dw_split;
     g.gscale = w.gscale;
-    MOE_TRY(launch_gemm(kDA, g, rowgrouped_grid(d, g.n_tiles), st));
+    MOE_TRY(launch_gemm(kGateUpBwd, g, rowgrouped_grid(d, g.n_tiles), st));
     // dXs = dG Wg + dU Wu   (reduction over 2I)
     g = GemmArgs{};
     g.offsets = offsets;

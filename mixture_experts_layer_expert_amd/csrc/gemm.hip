@@ -34,9 +34,11 @@
 //     with 4 consecutive output columns of one row (8-byte bf16 or 16-byte
 //     fp32 stores);
 //   - precision: every product accumulates in fp32.  The forward multiplies
-//     bf16 (H is stored as bf16 for the down GEMM).  The recomputed G/U (used
-//     by the SwiGLU backward and the router-weight gradient) and the per-row
-//     dX partials (summed over the K routed copies) stay fp32.  The gradient
+//     bf16 (H is stored as bf16 for the down GEMM).  The backward runs dA =
+//     dOu Wd first and stores it fp32; the recompute GEMM then holds G and U
+//     in its fp32 accumulators and does the SwiGLU backward and the
+//     router-weight partials in its epilogue.  The per-row dX partials
+//     (summed over the K routed copies) stay fp32.  The gradient
 //     GEMMs (dXs, dW) multiply fp16: dG/dU/Hw are rounded to fp16 (3 more
 //     mantissa bits than bf16, at the same matrix-core rate); dXs converts
 //     its bf16 weight fragments after the LDS read, and the dW GEMMs read fp16
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   constexpr bool kRowGrouped = MODE != kDW;
-  constexpr bool kGateUp = MODE == kGateUpH || MODE == kGateUpGU;
+  constexpr bool kGateUp = MODE == kGateUpH || MODE == kGateUpBwd;
   constexpr bool kF16 = MODE == kDXs || MODE == kDW;
   constexpr bool kBmn = MODE == kDA || MODE == kDXs || MODE == kDW;  // B row-contiguous
   using frag_t = typename std::conditional<kF16, f16x8, bf16x8>::type;
@@ -741,12 +743,12 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   // Results are written once and not re-read by this kernel: non-temporal
   // stores keep them from evicting lines that later kernels still read.
   auto store16 = [](char* dst, u32x4 v) { __builtin_nontemporal_store(v, (u32x4*)dst); };
-  if constexpr (MODE == kGateUpH || MODE == kGateUpGU) {
+  if constexpr (MODE == kGateUpH) {
     // the wave's WTN/2 gate columns and the matching up columns
     constexpr int CW = WTN / 2;
-    using S = Strip<CW, MODE == kGateUpH ? 2 : 4>;
-    static_assert(NW * 2 * S::BYTES <= NS * STAGE_BYTES, "staging fits the stage buffers");
-    char* const stg = lds + wave * 2 * S::BYTES;
+    using S = Strip<CW, 2>;
+    static_assert(NW * S::BYTES <= NS * STAGE_BYTES, "staging fits the stage buffers");
+    char* const stg = lds + wave * S::BYTES;
     const int col0 = n0 + wn * CW;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -755,29 +757,130 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       for (int j = 0; j < FN / 2; ++j) {
         const int cl = j * 16 + cq;
         const f32x4 g = acc[i][j], u = acc[i][j + FN / 2];
-        if constexpr (MODE == kGateUpH) {
-          float h[4];
+        float h[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) h[q] = g[q] * sigmoidf_(g[q]) * u[q];
-          strip_put<S>(stg, frow, cl, u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])});
-        } else {
-          // recomputed gate/up pre-activations stay fp32 for the SwiGLU backward
-          strip_put<S>(stg, frow, cl, g);
-          strip_put<S>(stg + S::BYTES, frow, cl, u);
+        for (int q = 0; q < 4; ++q) h[q] = g[q] * sigmoidf_(g[q]) * u[q];
+        strip_put<S>(stg, frow, cl, u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])});
+      }
+      strip_out<S>(stg, lane, rows_valid - rb, p.N - col0, [&](int r, int) {
+        return (char*)(p.C0 + (size_t)(m0 + rb + r) * p.ldc + col0); }, store16);
+    }
+  } else if constexpr (MODE == kGateUpBwd) {
+    // Recomputed g, u (fp32 accumulators) and dA = dOu Wd (fp32, read back),
+    // with w the router weight of the row and s the gradient scale:
+    //   h = silu(g) u;   partial dRW = sum of dA h over the wave's gate columns;
+    //   dH = s w dA;  dG = dH u silu'(g);  dU = dH silu(g);  Hw = w h
+    // (Hw: the weighted activations that dW_down needs).  The six fp16
+    // outputs (dG, dU, Hw, each as hi = round(v) and, for experts whose dW
+    // operand is split, lo = round(v - hi)) leave through per-wave LDS strips
+    // as whole row segments.
+    constexpr int CW = WTN / 2;  // gate columns of this wave
+    constexpr int FJ = FN / 2;   // gate fragments of this wave
+    using S = Strip<CW, 2>;
+    static_assert(NW * 6 * S::BYTES <= NS * STAGE_BYTES, "staging fits the stage buffers");
+    char* const stg = lds + wave * 6 * S::BYTES;
+    const int I = p.N;
+    const int col0 = n0 + wn * CW;  // the wave's first i column
+    bf16_t* const outs[6] = {p.C0, p.C1, p.C2, p.L0, p.L1, p.L2};
+    const size_t ldo[6] = {(size_t)p.ldc, (size_t)p.ldc, (size_t)I,
+                            (size_t)p.ldc, (size_t)p.ldc, (size_t)I};
+    // the low parts are read only by the dW GEMMs of experts with a split operand
+    const bool need_lo = p.dw_split[e] != 0;
+    // dA and the router weight of each 16-row block are read one block ahead
+    // of their use, the sort-permutation entry behind the weight two blocks
+    // ahead: the compiler cannot move a block's loads above the previous
+    // block's output stores (it cannot rule out aliasing), so each block would
+    // otherwise wait a full memory latency.  The loads are unconditional, from
+    // clamped in-bounds addresses (row m0, column 0), and padding is zeroed
+    // where the values are used: a load under a branch makes the compiler's
+    // wait counts assume the worst at the join.
+    auto src_of = [&](int i) {
+      const int r = wm * WTM + i * 16 + frow;
+      return p.s2f[m0 + (r < rows_valid ? r : 0)];
+    };
+    int src_next = src_of(0);
+    float wr_next = p.topk_w[src_next];
+    if (FM > 1) src_next = src_of(1);
+    f32x4 dbuf[2][FJ];
+    auto load_da = [&](int i, f32x4 (&dv)[FJ]) {
+      const int r = wm * WTM + i * 16 + frow;
+      const size_t m = (size_t)(m0 + (r < rows_valid ? r : 0));
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+        const int col = col0 + j * 16 + cq;
+        dv[j] = *(const f32x4*)(p.DA + m * (size_t)I + (col < I ? col : 0));
+      }
+    };
+    load_da(0, dbuf[0]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      // block i + 1's dA, its router weight, and block i + 2's source row
+      const float wr_i = wr_next;
+      if (i + 1 < FM) {
+        load_da(i + 1, dbuf[(i + 1) & 1]);
+        wr_next = p.topk_w[src_next];
+        if (i + 2 < FM) src_next = src_of(i + 2);
+      }
+      const int rb = wm * WTM + i * 16;
+      const int r = rb + frow;
+      const bool row_ok = r < rows_valid;
+      const float wr = row_ok ? wr_i : 0.0f;
+      const float wrs = wr * gsc;  // dG, dU carry the gradient scale
+      float dot = 0.0f;
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+        const int cl = j * 16 + cq;  // column within the wave's CW
+        const bool ok = row_ok && col0 + cl < I;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 dav = ok ? dbuf[i & 1][j] : zero;
+        const f32x4 gv = acc[i][j], uv = acc[i][j + FJ];
+        float dg[4], du[4], hw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float g = gv[q];
+          const float u = uv[q];
+          const float da = dav[q];
+          const float sg = sigmoidf_(g);
+          const float h = g * sg * u;
+          dot += da * h;
+          const float dh = wrs * da;
+          dg[q] = dh * u * sg * (1.0f + g * (1.0f - sg));
+          du[q] = dh * g * sg;
+          hw[q] = wr * h;
+        }
+        // fp16 hi = round(v) and lo = round(v - hi): the dX GEMM reads hi, the
+        // dW GEMMs read hi and lo
+        const u32x2 hi_dg = {pack_f16x2(dg[0], dg[1]), pack_f16x2(dg[2], dg[3])};
+        const u32x2 hi_du = {pack_f16x2(du[0], du[1]), pack_f16x2(du[2], du[3])};
+        const u32x2 hi_hw = {pack_f16x2(hw[0], hw[1]), pack_f16x2(hw[2], hw[3])};
+        strip_put<S>(stg + 0 * S::BYTES, frow, cl, hi_dg);
+        strip_put<S>(stg + 1 * S::BYTES, frow, cl, hi_du);
+        strip_put<S>(stg + 2 * S::BYTES, frow, cl, hi_hw);
+        if (need_lo) {
+          u32x2 lo_dg, lo_du, lo_hw;
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            lo_dg[h2] = f16x2_residual(dg[2 * h2], dg[2 * h2 + 1], hi_dg[h2]);
+            lo_du[h2] = f16x2_residual(du[2 * h2], du[2 * h2 + 1], hi_du[h2]);
+            lo_hw[h2] = f16x2_residual(hw[2 * h2], hw[2 * h2 + 1], hi_hw[h2]);
+          }
+          strip_put<S>(stg + 3 * S::BYTES, frow, cl, lo_dg);
+          strip_put<S>(stg + 4 * S::BYTES, frow, cl, lo_du);
+          strip_put<S>(stg + 5 * S::BYTES, frow, cl, lo_hw);
         }
       }
-      const int nrows = rows_valid - rb, ncols = p.N - col0;
-      if constexpr (MODE == kGateUpH) {
-        strip_out<S>(stg, lane, nrows, ncols, [&](int r, int) {
-          return (char*)(p.C0 + (size_t)(m0 + rb + r) * p.ldc + col0); }, store16);
-      } else {
-        strip_out<S>(stg, lane, nrows, ncols, [&](int r, int) {
-          return (char*)(p.Cf + (size_t)(m0 + rb + r) * p.ldc + col0); }, store16);
-        strip_out<S>(stg + S::BYTES, lane, nrows, ncols, [&](int r, int) {
-          return (char*)(p.Cf2 + (size_t)(m0 + rb + r) * p.ldc + col0); }, store16);
+      // this wave's strips are staged (a wave's LDS accesses complete in order)
+#pragma unroll
+      for (int o = 0; o < 6; ++o) {
+        if (o >= 3 && !need_lo) break;
+        strip_out<S>(stg + o * S::BYTES, lane, rows_valid - rb, I - col0, [&](int rr, int) {
+          return (char*)(outs[o] + (size_t)(m0 + rb + rr) * ldo[o] + col0); }, store16);
       }
+      dot += __shfl_xor(dot, 16);
+      dot += __shfl_xor(dot, 32);
+      if (row_ok && lane < 16) p.part[(size_t)(m0 + r) * p.np + nt_idx * WN + wn] = dot;
     }
-  } else if constexpr (MODE == kDown || MODE == kDXs) {
+  } else if constexpr (MODE == kDown || MODE == kDXs || MODE == kDA) {
     using S = Strip<WTN, MODE == kDown ? 2 : 4>;
     static_assert(NW * S::BYTES <= NS * STAGE_BYTES, "staging fits the stage buffers");
     char* const stg = lds + wave * S::BYTES;
@@ -805,6 +908,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
         const int cl = j * 16 + cq;
         const f32x4 v = acc[i][j];
         if constexpr (MODE == kDXs) strip_put<S>(stg, frow, cl, v * ginv);
+        else if constexpr (MODE == kDA) strip_put<S>(stg, frow, cl, v);
         else strip_put<S>(stg, frow, cl, u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
       }
       const int nrows = rows_valid - rb, ncols = p.N - col0;
@@ -813,136 +917,13 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
         // together for the reduction
         strip_out<S>(stg, lane, nrows, ncols, [&](int, int h) {
           return (char*)(p.Cf + (size_t)flat[i][h] * p.ldc + col0); }, store16);
+      } else if constexpr (MODE == kDA) {
+        strip_out<S>(stg, lane, nrows, ncols, [&](int r, int) {
+          return (char*)(p.Cf + (size_t)(m0 + rb + r) * p.ldc + col0); }, store16);
       } else {
         strip_out<S>(stg, lane, nrows, ncols, [&](int r, int) {
           return (char*)(p.C0 + (size_t)(m0 + rb + r) * p.ldc + col0); }, store16);
       }
-    }
-  } else if constexpr (MODE == kDA) {
-    // dA = dY_routed Wd (fp32).  With g, u recomputed (fp32) and w the router
-    // weight of the row:  h = silu(g) u;  partial dRW = sum dA h over the
-    // wave's WTN columns;  dH = w dA;  dG = dH u silu'(g);  dU = dH silu(g);
-    // Hw = w h (the weighted activations that dW_down needs).
-    //
-    // The six fp16 outputs (dG, dU, Hw, each as hi = round(v) and lo =
-    // round(v - hi)) leave through LDS: each wave stages one 16-row strip of
-    // all six in its own area (the stage buffers are free now) and writes
-    // them back as whole 128-byte row segments, 16 bytes per lane, instead of
-    // 8-byte pieces of 16 rows per store.
-    const int I = p.N;
-    constexpr int SP = WTN * 2 + 16;   // staged row pitch (bytes; padded, 16-byte aligned)
-    constexpr int OB = 16 * SP;        // one output's staged strip
-    constexpr int CPR = WTN * 2 / 16;  // 16-byte chunks per staged row
-    static_assert(NW * 6 * OB <= NS * STAGE_BYTES && 64 % CPR == 0, "epilogue staging layout");
-    char* const stg = lds + wave * 6 * OB;
-    bf16_t* const outs[6] = {p.C0, p.C1, p.C2, p.L0, p.L1, p.L2};
-    const size_t ldo[6] = {(size_t)p.ldc, (size_t)p.ldc, (size_t)I,
-                            (size_t)p.ldc, (size_t)p.ldc, (size_t)I};
-    // the low parts are read only by the dW GEMMs of experts with a split operand
-    const bool need_lo = p.dw_split[e] != 0;
-    // The G|U values and the router weight of each 16-row block are read one
-    // block ahead of their use, the sort-permutation entry behind the weight
-    // two blocks ahead: the compiler cannot move a block's loads above the
-    // previous block's output stores (it cannot rule out aliasing), so each
-    // block would otherwise wait a full memory latency (two, with the
-    // permutation read in front of the weight read).  The
-    // loads are unconditional, from clamped in-bounds addresses (row m0, column
-    // 0), and padding is zeroed where the values are used: a load under a
-    // branch makes the compiler's wait counts assume the worst at the join,
-    // which would wait for the next block's loads too.
-    auto src_of = [&](int i) {
-      const int r = wm * WTM + i * 16 + frow;
-      return p.s2f[m0 + (r < rows_valid ? r : 0)];
-    };
-    int src_next = src_of(0);
-    float wr_next = p.topk_w[src_next];
-    if (FM > 1) src_next = src_of(1);
-    f32x4 gbuf[2][FN], ubuf[2][FN];
-    auto load_gu = [&](int i, f32x4 (&gv)[FN], f32x4 (&uv)[FN]) {
-      const int r = wm * WTM + i * 16 + frow;
-      const size_t m = (size_t)(m0 + (r < rows_valid ? r : 0));
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * WTN + j * 16 + cq;
-        const float* src = p.GU + m * (2 * (size_t)I) + (col < I ? col : 0);
-        gv[j] = *(const f32x4*)src;
-        uv[j] = *(const f32x4*)(src + I);
-      }
-    };
-    load_gu(0, gbuf[0], ubuf[0]);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      // block i + 1's G|U, its router weight, and block i + 2's source row
-      const float wr_i = wr_next;
-      if (i + 1 < FM) {
-        load_gu(i + 1, gbuf[(i + 1) & 1], ubuf[(i + 1) & 1]);
-        wr_next = p.topk_w[src_next];
-        if (i + 2 < FM) src_next = src_of(i + 2);
-      }
-      const int r = wm * WTM + i * 16 + frow;
-      const bool row_ok = r < rows_valid;
-      const size_t m = (size_t)(m0 + (row_ok ? r : 0));
-      const float wr = row_ok ? wr_i : 0.0f;
-      const float wrs = wr * gsc;  // dG, dU carry the gradient scale
-      float dot = 0.0f;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int cl = j * 16 + cq;  // column within the wave's WTN
-        const int col = n0 + wn * WTN + cl;
-        const bool ok = row_ok && col < I;
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 gv = ok ? gbuf[i & 1][j] : zero, uv = ok ? ubuf[i & 1][j] : zero;
-        float dg[4], du[4], hw[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float g = gv[q];
-          const float u = uv[q];
-          const float da = acc[i][j][q];
-          const float sg = sigmoidf_(g);
-          const float h = g * sg * u;
-          if (ok) dot += da * h;
-          const float dh = wrs * da;
-          dg[q] = dh * u * sg * (1.0f + g * (1.0f - sg));
-          du[q] = dh * g * sg;
-          hw[q] = wr * h;
-        }
-        // fp16 hi = round(v) and lo = round(v - hi): the dX GEMM reads hi, the
-        // dW GEMMs read hi and lo
-        const u32x2 hi_dg = {pack_f16x2(dg[0], dg[1]), pack_f16x2(dg[2], dg[3])};
-        const u32x2 hi_du = {pack_f16x2(du[0], du[1]), pack_f16x2(du[2], du[3])};
-        const u32x2 hi_hw = {pack_f16x2(hw[0], hw[1]), pack_f16x2(hw[2], hw[3])};
-        u32x2 lo_dg, lo_du, lo_hw;
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          lo_dg[h2] = f16x2_residual(dg[2 * h2], dg[2 * h2 + 1], hi_dg[h2]);
-          lo_du[h2] = f16x2_residual(du[2 * h2], du[2 * h2 + 1], hi_du[h2]);
-          lo_hw[h2] = f16x2_residual(hw[2 * h2], hw[2 * h2 + 1], hi_hw[h2]);
-        }
-        char* const sp = stg + frow * SP + cl * 2;
-        *(u32x2*)(sp + 0 * OB) = hi_dg;
-        *(u32x2*)(sp + 1 * OB) = hi_du;
-        *(u32x2*)(sp + 2 * OB) = hi_hw;
-        *(u32x2*)(sp + 3 * OB) = lo_dg;
-        *(u32x2*)(sp + 4 * OB) = lo_du;
-        *(u32x2*)(sp + 5 * OB) = lo_hw;
-      }
-      // this wave's strip is staged (a wave's LDS accesses complete in order):
-      // write it back as row segments, CPR lanes per row
-#pragma unroll
-      for (int o = 0; o < 6; ++o) {
-        if (o >= 3 && !need_lo) break;
-#pragma unroll
-        for (int h = 0; h < 16 * CPR / 64; ++h) {
-          const int srow = h * (64 / CPR) + lane / CPR, ch = lane % CPR;
-          const u32x4 v = *(const u32x4*)(stg + o * OB + srow * SP + ch * 16);
-          const int rr = wm * WTM + i * 16 + srow;
-          const int cg = n0 + wn * WTN + ch * 8;
-          if (rr < rows_valid && cg < I) *(u32x4*)(outs[o] + (size_t)(m0 + rr) * ldo[o] + cg) = v;
-        }
-      }
-      dot += __shfl_xor(dot, 16);
-      dot += __shfl_xor(dot, 32);
-      if (row_ok && lane < 16) p.part[m * p.np + nt_idx * WN + wn] = dot;
     }
   } else {  // kDW
     using S = Strip<WTN, 4>;
@@ -1139,12 +1120,12 @@ hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st) {
       else
         MOE_LAUNCH(kKGemmGateUpH, grouped_gemm_kernel<kGateUpH>, dim3(grid), dim3(NTH), 0, st, a);
       break;
-    case kGateUpGU:
+    case kGateUpBwd:
       if (a.lead)
-        MOE_LAUNCH(kKGemmGateUpGU, (grouped_gemm_kernel<kGateUpGU, true>), dim3(grid), dim3(NTH), 0,
+        MOE_LAUNCH(kKGemmGateUpGU, (grouped_gemm_kernel<kGateUpBwd, true>), dim3(grid), dim3(NTH), 0,
                    st, a);
       else
-        MOE_LAUNCH(kKGemmGateUpGU, grouped_gemm_kernel<kGateUpGU>, dim3(grid), dim3(NTH), 0, st, a);
+        MOE_LAUNCH(kKGemmGateUpGU, grouped_gemm_kernel<kGateUpBwd>, dim3(grid), dim3(NTH), 0, st, a);
       break;
     case kDown:
       if (a.lead)

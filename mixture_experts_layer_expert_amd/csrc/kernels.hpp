@@ -150,13 +150,13 @@ constexpr int kGemmNS = MOE_GEMM_NS;  // K stages resident in LDS
 constexpr bool kGemmGatherDw = kGemmBM == kGemmBN && kGemmNS == 2;
 
 enum GemmMode : int {
-  kGateUpH = 0,   // H  = silu(Xs Wg^T) * (Xs Wu^T)                       bf16 [R, I]
-  kGateUpGU = 1,  // G  = Xs Wg^T,  U = Xs Wu^T                          fp32 [R, 2I]
-  kDown = 2,      // O  = H Wd^T                                         bf16 [R, D]
-  kDA = 3,        // dA = dOu Wd; SwiGLU backward (dG, dU, Hw in fp16) and router-weight
-                  // partials in the epilogue
-  kDXs = 4,       // dXs = dG Wg + dU Wu            fp32 [R, D], row f = flat slot of the routed row
-  kDW = 5,        // dW[e] = A_e^T B_e over the expert's rows              fp32
+  kGateUpH = 0,    // H  = silu(Xs Wg^T) * (Xs Wu^T)                       bf16 [R, I]
+  kGateUpBwd = 1,  // recompute G = Xs Wg^T, U = Xs Wu^T; the SwiGLU backward in the
+                   // epilogue from dA: dG, dU, Hw (fp16) and router-weight partials
+  kDown = 2,       // O  = H Wd^T                                         bf16 [R, D]
+  kDA = 3,         // dA = dOu Wd                                         fp32 [R, I]
+  kDXs = 4,        // dXs = dG Wg + dU Wu            fp32 [R, D], row f = flat slot of the routed row
+  kDW = 5,         // dW[e] = A_e^T B_e over the expert's rows              fp32
 };
 
 struct GemmArgs {
@@ -178,7 +178,7 @@ struct GemmArgs {
   float* dw_part;
   const int32_t* dw_split;  // [E] 1: the expert's dW operand is split hi + lo
   // backward gradient scale {s, 1/s} (see launch_bwd_prep), or null (s = 1):
-  // kDA scales dG and dU by s; kDXs and kDW multiply their results by 1/s
+  // kGateUpBwd scales dG and dU by s; kDXs and kDW multiply their results by 1/s
   const float* gscale;
   const bf16_t* A2;  // kDW second matrix's A (dW_up), else unused
   const bf16_t* B0;  // weights (row-grouped) or token-major activations (kDW)
@@ -198,17 +198,17 @@ struct GemmArgs {
   bf16_t* C0;
   bf16_t* C1;
   bf16_t* C2;
-  f16_t* L0;  // kDA: low fp16 parts of dG, dU, Hw
+  f16_t* L0;  // kGateUpBwd: low fp16 parts of dG, dU, Hw
   f16_t* L1;
   f16_t* L2;
   int ldc;
   float* Cf;
   float* Cf2;
   int accumulate;
-  const float* GU;   // kDA: recomputed G | U, fp32 [R, 2I]
+  const float* DA;   // kGateUpBwd: dA = dOu Wd, fp32 [R, I] (sorted rows)
   const float* topk_w;
   const int32_t* s2f;
-  float* part;  // kDA: router-weight-gradient partials [R, np]
+  float* part;  // kGateUpBwd: router-weight-gradient partials [R, np]
   int np;
 };
 
