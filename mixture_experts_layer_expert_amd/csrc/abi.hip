@@ -47,6 +47,14 @@ moe_status check_dims(const moe_dims* d) {
   const int64_t groups = 2 * (d->E + (R + kDwChunkRows - 1) / kDwChunkRows);
   if ((groups + kNumXcd - 1) / kNumXcd * kNumXcd * per_c >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
+  // the fused backward launch: the dXs grid and both dW grids in one
+  const int64_t ntd = (d->D + kGemmBN - 1) / kGemmBN;
+  const int64_t chunks = d->E + (R + kDwChunkRows - 1) / kDwChunkRows;
+  const int64_t per_d = ((d->D + kGemmBM - 1) / kGemmBM) * ((d->I + kGemmBN - 1) / kGemmBN);
+  const int64_t per_g = ((d->I + kGemmBM - 1) / kGemmBM) * ((d->D + kGemmBN - 1) / kGemmBN);
+  const int64_t fused = (mt * ntd + kNumXcd) + (chunks + kNumXcd) * per_d +
+                        (2 * chunks + kNumXcd) * per_g;
+  if (fused >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   // the GEMMs address token-major operands with 32-bit buffer offsets
   if (R * std::max<int64_t>(d->D, 2 * (int64_t)d->I) * 2 >= (int64_t(1) << 31) ||
       (int64_t)d->I * d->D * 2 >= (int64_t(1) << 31))
@@ -80,7 +88,9 @@ struct BwdWs {
   uint32_t* amax_part;    // partial maxima of |dy|
   float* gscale;          // gradient scale {s, 1/s}
   f16_t *x16, *dy16;      // fp16 x and s dy, token-major: the dW GEMMs' exact operands
-  float* dw_part;         // partial dW tiles of chunks 1.. of the chunked experts
+  // partial dW tiles of chunks 1.. of the chunked experts: dW_gate | dW_up, and
+  // dW_down apart (the two dW GEMMs run in one launch)
+  float *dw_part, *dw_part_down;
   float *da, *dxs, *part;  // dA [R, I], dX rows [R, D] (flat order), dRW partials
 };
 
@@ -139,6 +149,7 @@ size_t bwd_ws(const moe_dims& d, BwdWs* w, void* base) {
   w->x16 = c.take<f16_t>((size_t)d.T * d.D);
   w->dy16 = c.take<f16_t>((size_t)d.T * d.D);
   w->dw_part = c.take<float>(std::max<size_t>(1, (size_t)dw_part_slots(d) * 2 * d.I * d.D));
+  w->dw_part_down = c.take<float>(std::max<size_t>(1, (size_t)dw_part_slots(d) * d.I * d.D));
   w->da = c.take<float>(R * d.I);
   w->dgu = c.take<f16_t>(R * 2 * d.I);
   w->hw = c.take<f16_t>(R * d.I);
@@ -474,79 +485,83 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
     g.dw_split = w.dw_split;
     g.gscale = w.gscale;
     MOE_TRY(launch_gemm(kGateUpBwd, g, rowgrouped_grid(d, g.n_tiles), st));
-    // dXs = dG Wg + dU Wu   (reduction over 2I)
-    g = GemmArgs{};
-    g.offsets = offsets;
-    g.tstart = w.tstart;
-    g.E = d.E;
-    g.A = w.dgu;
-    g.lda = 2 * d.I;
-    g.B0 = (const bf16_t*)w_gate;
-    g.B1 = (const bf16_t*)w_up;
-    g.ldb = d.D;
-    g.N = d.D;
-    g.K = 2 * d.I;
-    g.n_tiles = (d.D + kGemmBN - 1) / kGemmBN;
-    g.Cf = w.dxs;  // rows in flat slot order (t*K + k)
-    g.ldc = d.D;
-    g.s2f = sorted_to_flat;
-    g.gscale = w.gscale;
-    MOE_TRY(launch_gemm(kDXs, g, rowgrouped_grid(d, g.n_tiles), st));
   }
+  // dXs = dG Wg + dU Wu   (reduction over 2I)
+  GemmArgs gx{};
+  gx.offsets = offsets;
+  gx.tstart = w.tstart;
+  gx.E = d.E;
+  gx.A = w.dgu;
+  gx.lda = 2 * d.I;
+  gx.B0 = (const bf16_t*)w_gate;
+  gx.B1 = (const bf16_t*)w_up;
+  gx.ldb = d.D;
+  gx.N = d.D;
+  gx.K = 2 * d.I;
+  gx.n_tiles = (d.D + kGemmBN - 1) / kGemmBN;
+  gx.Cf = w.dxs;  // rows in flat slot order (t*K + k)
+  gx.ldc = d.D;
+  gx.s2f = sorted_to_flat;
+  gx.gscale = w.gscale;
   // dW_down[e] = dOu_e^T Hw_e   ([D, I], reduction over the expert's rows, in
   // row chunks of at most kDwChunkRows); dOu from the fp16 s dy, the result
   // times 1/s
-  MOE_TRY(launch_dw_chunkmap(offsets, d.E, w.cstart, w.pstart, w.slist, st));
-  const int max_chunked = (int)dw_max_chunked(d);
-  g = GemmArgs{};
-  g.offsets = offsets;
-  g.E = d.E;
-  g.cstart = w.cstart;
-  g.pstart = w.pstart;
-  g.dw_part = w.dw_part;
-  g.dw_split = w.dw_split;
-  g.gscale = w.gscale;
+  GemmArgs gd{};
+  gd.offsets = offsets;
+  gd.E = d.E;
+  gd.cstart = w.cstart;
+  gd.pstart = w.pstart;
+  gd.dw_part = w.dw_part_down;
+  gd.dw_split = w.dw_split;
+  gd.gscale = w.gscale;
   if (kGemmGatherDw) {
-    g.A = (const bf16_t*)w.dy16;  // fp16 bits
-    g.a_rowoff = w.rowoff;
-    g.a_rows = d.T;
+    gd.A = (const bf16_t*)w.dy16;  // fp16 bits
+    gd.a_rowoff = w.rowoff;
+    gd.a_rows = d.T;
   } else {
-    g.A = w.dou;
+    gd.A = w.dou;
   }
-  g.lda = d.D;
-  g.B0 = w.hw;
-  g.ldb = d.I;
-  g.M = d.D;
-  g.N = d.I;
-  g.nmat = 1;
-  g.B_lo = w.hw_lo;
-  g.Cf = dw_down;
-  g.accumulate = accumulate_dw;
-  MOE_TRY(launch_gemm(kDW, g, dw_grid(1, dw_chunks_bound(d), d.D, d.I), st));
-  MOE_TRY(launch_dw_reduce(w.dw_part, w.slist, w.pstart, w.cstart, dw_down, nullptr, 1, d.D, d.I,
-                           d.E, max_chunked, st));
+  gd.lda = d.D;
+  gd.B0 = w.hw;
+  gd.ldb = d.I;
+  gd.M = d.D;
+  gd.N = d.I;
+  gd.nmat = 1;
+  gd.B_lo = w.hw_lo;
+  gd.Cf = dw_down;
+  gd.accumulate = accumulate_dw;
   // dW_gate[e] = dG_e^T Xs_e, dW_up[e] = dU_e^T Xs_e   ([I, D]); Xs from the fp16 x
-  g.A = w.dgu;
-  g.A2 = w.dgu + d.I;
-  g.a_rowoff = nullptr;
-  g.lda = 2 * d.I;
+  GemmArgs gg = gd;
+  gg.dw_part = w.dw_part;
+  gg.A = w.dgu;
+  gg.A2 = w.dgu + d.I;
+  gg.a_rowoff = nullptr;
+  gg.lda = 2 * d.I;
   if (kGemmGatherDw) {
-    g.B0 = (const bf16_t*)w.x16;  // fp16 bits
-    g.b_rowoff = w.rowoff;
-    g.b_rows = d.T;
+    gg.B0 = (const bf16_t*)w.x16;  // fp16 bits
+    gg.b_rowoff = w.rowoff;
+    gg.b_rows = d.T;
   } else {
-    g.B0 = w.xs;
+    gg.B0 = w.xs;
   }
-  g.ldb = d.D;
-  g.M = d.I;
-  g.N = d.D;
-  g.nmat = 2;
-  g.A_lo = w.dgu_lo;
-  g.A2_lo = w.dgu_lo + d.I;
-  g.B_lo = nullptr;
-  g.Cf = dw_gate;
-  g.Cf2 = dw_up;
-  MOE_TRY(launch_gemm(kDW, g, dw_grid(2, dw_chunks_bound(d), d.I, d.D), st));
+  gg.ldb = d.D;
+  gg.M = d.I;
+  gg.N = d.D;
+  gg.nmat = 2;
+  gg.A_lo = w.dgu_lo;
+  gg.A2_lo = w.dgu_lo + d.I;
+  gg.B_lo = nullptr;
+  gg.Cf = dw_gate;
+  gg.Cf2 = dw_up;
+  // the three read only the recompute GEMM's outputs: one launch (no tail
+  // between them); the chunk map first, the chunk partials after
+  MOE_TRY(launch_dw_chunkmap(offsets, d.E, w.cstart, w.pstart, w.slist, st));
+  MOE_TRY(launch_bwd_fused(gx, R > 0 ? rowgrouped_grid(d, gx.n_tiles) : 0, gd,
+                           dw_grid(1, dw_chunks_bound(d), d.D, d.I), gg,
+                           dw_grid(2, dw_chunks_bound(d), d.I, d.D), st));
+  const int max_chunked = (int)dw_max_chunked(d);
+  MOE_TRY(launch_dw_reduce(w.dw_part_down, w.slist, w.pstart, w.cstart, dw_down, nullptr, 1, d.D, d.I,
+                           d.E, max_chunked, st));
   MOE_TRY(launch_dw_reduce(w.dw_part, w.slist, w.pstart, w.cstart, dw_gate, dw_up, 2, d.I, d.D,
                            d.E, max_chunked, st));
 

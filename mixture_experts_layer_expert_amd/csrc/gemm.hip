@@ -275,15 +275,20 @@ __device__ __forceinline__ void strip_out(const char* stg, int lane, int nrows, 
   }
 }
 
+// LDS of one workgroup tile: NS stages, then (with L2 prefetch) 256 bytes per
+// wave that the prefetch DMA writes and nothing reads, then (kDW) the ring of
+// gathered row indices.
+constexpr int kRingOff = NS * STAGE_BYTES + (PREFETCH ? NW * 256 : 0);
+template <int MODE>
+constexpr int tile_lds_bytes() { return kRingOff + (MODE == kDW ? RING_BYTES : 0); }
+
+// One workgroup tile of a grouped GEMM: `block` plays the role of the block
+// index in the GEMM's own grid (tile decode and XCD order); lds holds at
+// least tile_lds_bytes<MODE>() bytes, 1024-byte aligned.
 // LEAD: the L2 prefetch policy of the gate/up and down GEMMs (see kLead); the
 // host picks it per launch from the shape (GemmArgs::lead).
 template <int MODE, bool LEAD = false>
-__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void grouped_gemm_kernel(
-    GemmArgs p) {
-  // NS stages, then (with L2 prefetch) 256 bytes per wave that the prefetch
-  // DMA writes and nothing reads, then (kDW) the ring of gathered row indices
-  constexpr int kRingOff = NS * STAGE_BYTES + (PREFETCH ? NW * 256 : 0);
-  __shared__ __attribute__((aligned(1024))) char lds[kRingOff + (MODE == kDW ? RING_BYTES : 0)];
+__device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, char* const lds) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
@@ -318,16 +323,16 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       // XCD x takes the x-th contiguous range of tiles (an expert's tiles share
       // an L2); row-grouped tiles all carry about the same work
       const int per = ceil_div(total, kNumXcd);
-      const int slot = blockIdx.x / kNumXcd;
-      tile = (blockIdx.x % kNumXcd) * per + slot;
+      const int slot = block / kNumXcd;
+      tile = (block % kNumXcd) * per + slot;
       if (slot >= per || tile >= total) return;
     } else {
       // dW: the tm x tn tiles of one (matrix, row chunk) group stay on one XCD
       // (they share the chunk's operands in L2), and the groups are dealt to
       // the XCDs round-robin, so the heavy chunks of a hot expert spread
       const int per_c = ceil_div(p.M, BM) * ceil_div(p.N, BN);
-      const int slot = blockIdx.x / kNumXcd;
-      const int grp = (slot / per_c) * kNumXcd + blockIdx.x % kNumXcd;
+      const int slot = block / kNumXcd;
+      const int grp = (slot / per_c) * kNumXcd + block % kNumXcd;
       tile = grp * per_c + slot % per_c;
       if (tile >= total) return;
     }
@@ -951,6 +956,30 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   }
 }
 
+
+template <int MODE, bool LEAD = false>
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void grouped_gemm_kernel(
+    GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) char lds[tile_lds_bytes<MODE>()];
+  gemm_tile<MODE, LEAD>(p, blockIdx.x, lds);
+}
+
+// The three backward GEMMs that read only the recompute GEMM's outputs (dXs,
+// dW_down, dW_gate + dW_up) in one launch: blocks [0, g1) run the dXs grid,
+// [g1, g1 + g2) the dW_down grid, the rest the dW_gate/up grid.  None reads
+// another's results, so no workgroup waits for another; the GPU starts the dW
+// tiles as soon as CUs come free from the dXs tiles, with no tail between
+// launches.  g1 and g2 are multiples of the XCD count, so every block runs on
+// the XCD its own grid's tile order intends.
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void bwd_fused_kernel(
+    GemmArgs dxs, GemmArgs dw_down, GemmArgs dw_gateup, int g1, int g2) {
+  __shared__ __attribute__((aligned(1024))) char lds[tile_lds_bytes<kDW>()];
+  static_assert(tile_lds_bytes<kDW>() >= tile_lds_bytes<kDXs>(), "one LDS size serves both");
+  const int b = blockIdx.x;
+  if (b < g1) gemm_tile<kDXs>(dxs, b, lds);
+  else if (b < g1 + g2) gemm_tile<kDW>(dw_down, b - g1, lds);
+  else gemm_tile<kDW>(dw_gateup, b - g1 - g2, lds);
+}
 // ---------------------------------------------------------------------------
 // dW row chunks.  One workgroup of 1024 threads: nch_e = max(1, ceil(rows_e /
 // kDwChunkRows)); cstart = exclusive prefix of nch (cstart[E] = total);
@@ -1109,9 +1138,18 @@ hipError_t launch_dw_reduce(const float* part, const int32_t* slist, const int32
   return hipGetLastError();
 }
 
+hipError_t launch_bwd_fused(const GemmArgs& dxs, int g1, const GemmArgs& dw_down, int g2,
+                            const GemmArgs& dw_gateup, int g3, hipStream_t st) {
+  if (g1 % kNumXcd || g2 % kNumXcd) return hipErrorInvalidValue;
+  const int grid = g1 + g2 + g3;
+  if (grid <= 0) return hipSuccess;
+  MOE_LAUNCH(kKGemmBwdFused, bwd_fused_kernel, dim3(grid), dim3(NTH), 0, st, dxs, dw_down,
+             dw_gateup, g1, g2);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  const bool dw_gateup = mode == kDW && a.nmat == 2;
   switch (mode) {
     case kGateUpH:
       if (a.lead)
@@ -1135,13 +1173,6 @@ hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st) {
       break;
     case kDA:
       MOE_LAUNCH(kKGemmDA, grouped_gemm_kernel<kDA>, dim3(grid), dim3(NTH), 0, st, a);
-      break;
-    case kDXs:
-      MOE_LAUNCH(kKGemmDXs, grouped_gemm_kernel<kDXs>, dim3(grid), dim3(NTH), 0, st, a);
-      break;
-    case kDW:
-      MOE_LAUNCH(dw_gateup ? kKGemmDWGateUp : kKGemmDWDown, grouped_gemm_kernel<kDW>, dim3(grid),
-                 dim3(NTH), 0, st, a);
       break;
     default:
       return hipErrorInvalidValue;

@@ -9,10 +9,9 @@ namespace moe {
 // ---- per-kernel timing (prof.hip)
 enum KernelId : int {
   kKRouteTopk, kKRouteHist, kKRouteScatter, kKTilemap, kKGather,
-  kKGemmGateUpH, kKGemmGateUpGU, kKGemmDown, kKGemmDA, kKGemmDXs, kKGemmDWDown,
-  kKGemmDWGateUp, kKCombine, kKReduceRows, kKReducePartials, kKGather2, kKRouterLogits,
+  kKGemmGateUpH, kKGemmGateUpGU, kKGemmDown, kKGemmDA, kKCombine, kKReduceRows, kKReducePartials, kKGather2, kKRouterLogits,
   kKRouterPrep, kKRouterDx, kKRouterDwr, kKRouterDwrSum, kKRowOffsets, kKDwChunkMap,
-  kKDwReduce, kKBwdPrep, kKDyAmax, kKF16Operands, kNumKernels
+  kKDwReduce, kKBwdPrep, kKDyAmax, kKF16Operands, kKGemmBwdFused, kNumKernels
 };
 namespace prof {
 void begin(int kid, hipStream_t st);  // no-ops unless timing is enabled
@@ -212,7 +211,12 @@ struct GemmArgs {
   int np;
 };
 
+// One grouped GEMM of the row-grouped modes (kGateUpH, kGateUpBwd, kDown, kDA).
 hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st);
+// dXs (grid g1), dW_down (grid g2) and dW_gate/up (grid g3) as one launch; the
+// grids are those launch_gemm would take (g1, g2 multiples of kNumXcd).
+hipError_t launch_bwd_fused(const GemmArgs& dxs, int g1, const GemmArgs& dw_down, int g2,
+                            const GemmArgs& dw_gateup, int g3, hipStream_t st);
 
 // Backward preparation, one workgroup per expert:
 //   split[e] = 1 when S, the sum of the squared router weights

@@ -37,10 +37,10 @@ bool capturing(hipStream_t st) {
 const char* const kNames[kNumKernels] = {
     "route_topk",   "route_hist",    "route_scatter", "tilemap",
     "gather",       "gemm_gateup_h", "gemm_gateup_gu", "gemm_down",    "gemm_da",
-    "gemm_dxs",     "gemm_dw_down",  "gemm_dw_gateup", "combine",      "reduce_rows",
+    "combine",      "reduce_rows",
     "reduce_partials", "gather2",   "router_logits", "router_prep",  "router_dx",
     "router_dwr",   "router_dwr_sum", "row_offsets", "dw_chunkmap", "dw_reduce",
-    "bwd_prep",     "dy_amax",       "f16_operands"};
+    "bwd_prep",     "dy_amax",       "f16_operands", "gemm_bwd_fused"};
 
 hipEvent_t take() {
   if (!pool.empty()) {
