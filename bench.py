@@ -56,8 +56,6 @@ def kernel_work(wl: synth.Workload) -> dict:
         "gemm_down": ("mfma", 2 * dir_), "gemm_da": ("mfma", 2 * dir_),
         # dXs (4 D I R), dW_down (2 D I R) and dW_gate + dW_up (4 D I R) in one launch
         "gemm_bwd_fused": ("mfma", 10 * dir_),
-        # gather: read the routed rows of x (R*D*2) and write Xs (R*D*2), plus the index
-        "gather": ("hbm", 4.0 * R * D + 4 * R), "gather2": ("hbm", 8.0 * R * D + 4 * R),
         # combine: read O (R*D*2), weights and indices (8R), write y (T*D*2)
         "combine": ("hbm", 2.0 * R * D + 8 * R + 2.0 * T * D),
         # dX reduce: read the fp32 per-row partials (R*D*4) and indices, write dX (T*D*2)

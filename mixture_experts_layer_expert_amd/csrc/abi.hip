@@ -79,7 +79,6 @@ struct FwdWs {
 };
 struct BwdWs {
   int32_t* tstart;
-  bf16_t *xs, *dou;       // (copying gathers only) fp16 bits of x and s dy in expert order
   f16_t *dgu, *hw;        // fp16 operands of the gradient GEMMs (rounded values)
   f16_t *dgu_lo, *hw_lo;  // their low parts (value - rounded value), for the dW GEMMs
   uint32_t* rowoff;       // byte offset of each routed row's token row in x / dy
@@ -136,10 +135,7 @@ size_t bwd_ws(const moe_dims& d, BwdWs* w, void* base) {
   Carve c{(char*)base};
   const size_t R = (size_t)d.T * d.K;
   w->tstart = c.take<int32_t>(d.E + 1);
-  // routed rows in expert order, only where the dW GEMMs cannot gather them
-  w->xs = kGemmGatherDw ? nullptr : c.take<bf16_t>(R * d.D);
-  w->dou = kGemmGatherDw ? nullptr : c.take<bf16_t>(R * d.D);
-  w->rowoff = kGemmGatherDw ? c.take<uint32_t>(std::max<size_t>(1, R)) : nullptr;
+  w->rowoff = c.take<uint32_t>(std::max<size_t>(1, R));
   w->cstart = c.take<int32_t>(d.E + 1);
   w->pstart = c.take<int32_t>(d.E);
   w->slist = c.take<int32_t>(d.E + 1);
@@ -424,12 +420,9 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
                           w.dw_split, w.gscale, st));
   MOE_TRY(launch_f16_operands(x, dy, w.gscale, w.x16, w.dy16, TD, st));
   if (R > 0) {
-    // routed output gradients and the re-gathered inputs, in expert order (only
-    // where the dW GEMMs cannot gather them; the row-grouped GEMMs always do)
-    if (kGemmGatherDw)
-      MOE_TRY(launch_row_offsets(sorted_to_flat, (int)R, d.K, (uint32_t)d.D * 2u, w.rowoff, st));
-    else
-      MOE_TRY(launch_gather(w.x16, w.dy16, w.xs, w.dou, sorted_to_flat, (int)R, d.K, d.D, st));
+    // token-row byte offsets of the routed rows: the dW GEMMs gather the rows
+    // of the fp16 x and s dy through them inside their loads
+    MOE_TRY(launch_row_offsets(sorted_to_flat, (int)R, d.K, (uint32_t)d.D * 2u, w.rowoff, st));
     MOE_TRY(launch_tilemap(offsets, d.E, kGemmBM, w.tstart, st));
   }
   GemmArgs g{};
@@ -514,13 +507,9 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   gd.dw_part = w.dw_part_down;
   gd.dw_split = w.dw_split;
   gd.gscale = w.gscale;
-  if (kGemmGatherDw) {
-    gd.A = (const bf16_t*)w.dy16;  // fp16 bits
-    gd.a_rowoff = w.rowoff;
-    gd.a_rows = d.T;
-  } else {
-    gd.A = w.dou;
-  }
+  gd.A = (const bf16_t*)w.dy16;  // fp16 bits
+  gd.a_rowoff = w.rowoff;
+  gd.a_rows = d.T;
   gd.lda = d.D;
   gd.B0 = w.hw;
   gd.ldb = d.I;
@@ -537,13 +526,9 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   gg.A2 = w.dgu + d.I;
   gg.a_rowoff = nullptr;
   gg.lda = 2 * d.I;
-  if (kGemmGatherDw) {
-    gg.B0 = (const bf16_t*)w.x16;  // fp16 bits
-    gg.b_rowoff = w.rowoff;
-    gg.b_rows = d.T;
-  } else {
-    gg.B0 = w.xs;
-  }
+  gg.B0 = (const bf16_t*)w.x16;  // fp16 bits
+  gg.b_rowoff = w.rowoff;
+  gg.b_rows = d.T;
   gg.ldb = d.D;
   gg.M = d.I;
   gg.N = d.D;

@@ -11,9 +11,9 @@
 //
 //   - a 512-thread workgroup (8 waves) owns a 256 x 256 output tile; waves in
 //     2 (rows) x 4 (columns), each 128 x 64 = 8 x 4 fragments of
-//     v_mfma_f32_16x16x32_{bf16,f16} with fp32 accumulators (the geometry is
-//     a compile-time choice in kernels.hpp; 128 x 256 tiles, 4 waves and
-//     32-deep stages are the other supported settings);
+//     v_mfma_f32_16x16x32_{bf16,f16} with fp32 accumulators (a 256 x 256 fp32
+//     tile is half of a CU's register file: the largest tile one workgroup
+//     can hold; with 4 waves the compiler spills above 256 accumulators);
 //   - operands go HBM -> LDS directly (buffer_load ... lds: no VGPR staging),
 //     64-deep K stages, double-buffered (128 KB of LDS, one workgroup per CU),
 //     one barrier per stage: the next stage's loads are issued right after the
@@ -22,8 +22,8 @@
 //     as zeros in hardware;
 //   - LDS keeps each operand in its HBM orientation, XOR-swizzled instead of
 //     padded.  k-contiguous operands ([row][k], 128-byte rows of eight 16-byte
-//     chunks; chunk c of row r stored at c ^ (r/2 % 8), or for 32-deep stages
-//     64-byte rows with c ^ (r/4 % 4)) are read with ds_read_b128;
+//     chunks; chunk c of row r stored at c ^ (r/2 % 8)) are read with
+//     ds_read_b128;
 //     row-contiguous operands ([k][row], the token-major activations of the
 //     weight gradients and the weights read transposed; chunk c of k-row k
 //     stored at c ^ s(k), s(k) = 2 (k % 4) + 8 ((k/8 + k/16) % 2)) are read
@@ -89,19 +89,17 @@ constexpr int B_BYTES = BN * BK * 2;
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
 constexpr int LOADS_PER_STAGE = (A_BYTES + B_BYTES) / 1024 / NW;  // 1 KB loads per wave
 
-static_assert(BK == 32 || BK == 64, "the loaders and swizzles handle 32- or 64-deep stages");
-constexpr int KROW = BK * 2;       // bytes of one k-contiguous row in LDS (64 or 128)
-constexpr int KCH = BK / 8;        // 16-byte chunks per k-contiguous row (4 or 8)
-constexpr int KRPI = 1024 / KROW;  // k-contiguous rows per 1 KB load instruction (16 or 8)
-static_assert(BM % (16 * WM) == 0 && BN % (32 * WN) == 0 && (BM == 128 || BM == 256) &&
-                  (BN == 128 || BN == 256),
-              "unsupported tile geometry");
-static_assert(NS * STAGE_BYTES <= 160 * 1024, "LDS budget");
-static_assert(NS >= 2, "at least double buffering");
-constexpr int PREFETCH = kGemmPrefetch;  // L2 prefetch distance in stages (0: off)
-static_assert(PREFETCH == 0 || (NS == 2 && BK == 64 && BM == 256 && BN == 256 && NW == 8),
-              "the L2 prefetch covers a 256 x 256 x 64 stage with 8 waves, double-buffered");
-static_assert(NS * STAGE_BYTES + (PREFETCH ? NW * 256 : 0) <= 160 * 1024, "LDS budget");
+constexpr int KROW = BK * 2;       // bytes of one k-contiguous row in LDS (128)
+constexpr int KCH = BK / 8;        // 16-byte chunks per k-contiguous row (8)
+constexpr int KRPI = 1024 / KROW;  // k-contiguous rows per 1 KB load instruction (8)
+// The loaders, swizzles, wait counts and the L2 prefetch (one 4-byte DMA per
+// lane and wave touches 64 of a stage's 512 lines) are written for this
+// geometry: 256 x 256 tiles, 64-deep stages, double-buffered, 8 waves as 2 x 4.
+static_assert(BM == 256 && BN == 256 && BK == 64 && NS == 2 && WM == 2 && WN == 4,
+              "the one tile geometry the kernels are written for");
+constexpr int PREFETCH = kGemmPrefetch;  // L2 prefetch distance in stages
+static_assert(PREFETCH >= 1, "the stage waits count the prefetch touch");
+static_assert(NS * STAGE_BYTES + NW * 256 <= 160 * 1024, "LDS budget");
 
 // Weight-gradient GEMMs with a gathered operand read its k-rows (routed rows)
 // through their token index.  The indices of an expert's rows pass through a
@@ -111,7 +109,7 @@ static_assert(NS * STAGE_BYTES + (PREFETCH ? NW * 256 : 0) <= 160 * 1024, "LDS b
 constexpr int RING_ROWS = NW * 64, RING_SLOTS = 3;
 constexpr int RING_BYTES = RING_SLOTS * RING_ROWS * 4;
 constexpr int RING_STAGES = RING_ROWS / BK;  // row blocks per chunk
-static_assert(NS * STAGE_BYTES + (PREFETCH ? NW * 256 : 0) + RING_BYTES <= 160 * 1024,
+static_assert(NS * STAGE_BYTES + NW * 256 + RING_BYTES <= 160 * 1024,
               "LDS budget with the index ring");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -132,9 +130,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_wave_b
 // same k-chunk land in 16 distinct 16-byte bank groups.  swz_mn: the four
 // 16-lane groups of a transposing read (k-rows 8g..8g+3) split into two pairs
 // that each cover all 64 banks, for either pairing of the groups.
-__device__ __forceinline__ int swz_k(int row) {
-  return BK == 32 ? (row >> 2) & 3 : (row >> 1) & 7;
-}
+__device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz_mn(int k) {
   return ((k & 3) << 1) | ((((k >> 3) ^ (k >> 4)) & 1) << 3);
 }
@@ -214,19 +210,6 @@ __device__ __forceinline__ F read_mnmajor(const char* tile, int c0, int kk, int 
   return __builtin_bit_cast(F, v);
 }
 
-// Waits until at most min(N, later) stages of LOADS_PER_STAGE loads per wave
-// are outstanding, where `later` stages were issued after the one needed now.
-template <int N>
-__device__ __forceinline__ void wait_stage(int later) {
-  static_assert(N * LOADS_PER_STAGE <= 63, "vmcnt holds at most 63");
-  if constexpr (N == 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  } else {
-    if (later >= N) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N * LOADS_PER_STAGE) : "memory");
-    else wait_stage<N - 1>(later);
-  }
-}
-
 // bf16 fragment bits -> fp16 fragment (operands of the fp16 gradient GEMMs).
 __device__ __forceinline__ f16x8 frag_to_f16(f16x8 v) {
   u32x4 u = __builtin_bit_cast(u32x4, v);
@@ -278,7 +261,7 @@ __device__ __forceinline__ void strip_out(const char* stg, int lane, int nrows, 
 // LDS of one workgroup tile: NS stages, then (with L2 prefetch) 256 bytes per
 // wave that the prefetch DMA writes and nothing reads, then (kDW) the ring of
 // gathered row indices.
-constexpr int kRingOff = NS * STAGE_BYTES + (PREFETCH ? NW * 256 : 0);
+constexpr int kRingOff = NS * STAGE_BYTES + NW * 256;
 template <int MODE>
 constexpr int tile_lds_bytes() { return kRingOff + (MODE == kDW ? RING_BYTES : 0); }
 
@@ -300,7 +283,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
   // L2 prefetch distance of this GEMM, and whether only the first tile of each
   // group sharing an operand slice touches it
   static_assert(!LEAD || kGateUp || MODE == kDown, "the lead policy is for gate/up and down");
-  constexpr bool kLead = PREFETCH > 0 && LEAD;
+  constexpr bool kLead = LEAD;
   constexpr int PF = kLead ? kGemmPrefetchLead : PREFETCH;
   // the index ring is loaded RA stages ahead of its first read (the touch of
   // stage kt + 1 + PF is read at stage kt)
@@ -421,16 +404,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
     rB = make_rsrc(p.B0 + kbase * p.ldb, bbytes);
     rB2 = make_rsrc((p.B_lo ? p.B_lo : p.B0) + kbase * p.ldb, bbytes);
     // a gathered operand is addressed from the start of its token-major rows
-    if (kGemmGatherDw && p.a_rowoff) rA = rA2 = make_rsrc(a, (size_t)p.a_rows * lda2);
-    if (kGemmGatherDw && p.b_rowoff) rB = rB2 = make_rsrc(p.B0, (size_t)p.b_rows * ldb2);
+    if (p.a_rowoff) rA = rA2 = make_rsrc(a, (size_t)p.a_rows * lda2);
+    if (p.b_rowoff) rB = rB2 = make_rsrc(p.B0, (size_t)p.b_rows * ldb2);
   }
 
   // ---------------------------------------------------------------- kDW gathered operand
   // ga / gb: A / B k-rows are gathered (wave-uniform).  gofs[i]: byte offset of
   // the token row behind this lane's k-row of load instruction i of the next
   // stage; gtouch: the same for the row this lane touches for the L2 prefetch.
-  const bool ga = kGemmGatherDw && !kRowGrouped && p.a_rowoff;
-  const bool gb = kGemmGatherDw && !kRowGrouped && p.b_rowoff;
+  const bool ga = !kRowGrouped && p.a_rowoff;
+  const bool gb = !kRowGrouped && p.b_rowoff;
   constexpr int QG = mnmajor_instrs<BM>();
   uint32_t gofs[QG] = {}, gtouch = 0;
   char* const ring = lds + kRingOff;
@@ -463,7 +446,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
     constexpr int KPI = 512 / BM, LPR = BM / 8;
 #pragma unroll
     for (int i = 0; i < QG; ++i) gofs[i] = gtok(kt_load, (wave + NW * i) * KPI + lane / LPR);
-    if (PF > 0) gtouch = gtok(min(kt_touch, nk - 1), ((wave % (NW / 2)) * 64 + lane) / (BM / 64));
+    gtouch = gtok(min(kt_touch, nk - 1), ((wave % (NW / 2)) * 64 + lane) / (BM / 64));
   };
 
   // Row-grouped A: the byte offset of each A row this lane loads (one row per
@@ -480,7 +463,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
     };
 #pragma unroll
     for (int i = 0; i < QA; ++i) aoff[i] = row_off(KRPI * (wave + NW * i) + lane / KCH);
-    if (PF > 0 && wave < NW / 2) atouch = row_off(wave * 64 + lane);
+    if (wave < NW / 2) atouch = row_off(wave * 64 + lane);
   }
 
   // Loads of stage kt, pieces [q0, q1) of LOADS_PER_STAGE (A first, then B).
@@ -601,14 +584,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
 
   // ---------------------------------------------------------------- main loop
   // The next stage's loads are spread over this stage's MFMAs: the FM * BK/32
-  // rows of MFMAs are slots, and every LOAD_STRIDE-th slot (the first
-  // LOAD_SLOTS of them) issues LOADS_PER_SLOT loads before its MFMAs, so no
-  // wave holds its MFMAs back behind a burst of memory instructions.
+  // rows of MFMAs are slots, and each of the first LOAD_SLOTS slots issues
+  // LOADS_PER_SLOT loads before its MFMAs, so no wave holds its MFMAs back
+  // behind a burst of memory instructions; the slot after them issues the
+  // L2 prefetch touch.
   constexpr int SLOTS = FM * (BK / 32);
-  constexpr int LOAD_SLOTS = MOE_GEMM_LOAD_SLOTS, LOAD_STRIDE = MOE_GEMM_LOAD_STRIDE;
+  constexpr int LOAD_SLOTS = kGemmLoadSlots;
   constexpr int LOADS_PER_SLOT = LOADS_PER_STAGE / LOAD_SLOTS;
-  static_assert(LOADS_PER_SLOT * LOAD_SLOTS == LOADS_PER_STAGE &&
-                    (LOAD_SLOTS - 1) * LOAD_STRIDE + (PF > 0 ? 1 : 0) < SLOTS,
+  static_assert(LOADS_PER_SLOT * LOAD_SLOTS == LOADS_PER_STAGE && LOAD_SLOTS + 1 <= SLOTS,
                 "load slots must split the stage's loads evenly and fit the MFMA rows");
   bool first_issued = false;  // stage 0's loads already issued by the gathered prologue
   if constexpr (!kRowGrouped) {
@@ -630,11 +613,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
       first_issued = true;
     }
   }
-  if constexpr (PF > 0) {
-    if (nk > 0) {
+  if (nk > 0) {
 #pragma unroll
-      for (int s = 1; s <= PF; ++s) touch(s);
-    }
+    for (int s = 1; s <= PF; ++s) touch(s);
   }
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
@@ -646,15 +627,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
   // kt + NS - 1 interleaved (kMore: that stage exists).
   auto stage = [&](int kt, auto more_tag) __attribute__((always_inline)) {
     constexpr bool kMore = decltype(more_tag)::value;
-    // stage kt has landed once only the stages issued after it (at most NS - 2)
-    // are still in flight
-    if constexpr (PF > 0) {
-      // only the prefetch issued last (after stage kt's loads) may be in flight
-      if (kt == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-    } else {
-      wait_stage<NS - 2>(nk - 1 - kt);
-    }
+    // stage kt has landed once only the prefetch touch issued after its loads
+    // may still be in flight
+    if (kt == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
     __builtin_amdgcn_s_barrier();  // every wave's part of stage kt is in LDS, and
     asm volatile("" ::: "memory");  // every wave is done reading stage kt - 1
     if constexpr (!kRowGrouped && kMore) {
@@ -670,7 +646,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
       // next stage (and the prefetch)
       if constexpr (kMore) {
         issue(kt + NS - 1, 0, LOADS_PER_STAGE);
-        if constexpr (PF > 0) touch(kt + NS - 1 + PF);
+        touch(kt + NS - 1 + PF);
       }
       return;
     }
@@ -703,9 +679,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int slot = (kk / 32) * FM + i;
-        const int t = slot / LOAD_STRIDE;
-        const bool loads_here = kMore && slot % LOAD_STRIDE == 0 && t < LOAD_SLOTS;
-        if (loads_here) issue(kt + NS - 1, t * LOADS_PER_SLOT, (t + 1) * LOADS_PER_SLOT);
+        const bool loads_here = kMore && slot < LOAD_SLOTS;
+        if (loads_here) issue(kt + NS - 1, slot * LOADS_PER_SLOT, (slot + 1) * LOADS_PER_SLOT);
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           if constexpr (kF16)
@@ -721,11 +696,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
         // (measured: -0.6% per step)
         if (i == FM - 1) __builtin_amdgcn_s_setprio(0);
         else __builtin_amdgcn_s_setprio(1);
-        if constexpr (PF > 0) {
-          if (kMore && slot == (LOAD_SLOTS - 1) * LOAD_STRIDE + 1) {
-            touch(kt + NS - 1 + PF);  // the stage's last memory instruction
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          }
+        if (kMore && slot == LOAD_SLOTS) {
+          touch(kt + NS - 1 + PF);  // the stage's last memory instruction
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
       }
     }
@@ -734,7 +707,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
   for (; kt + NS - 1 < nk; ++kt) stage(kt, std::true_type{});
   for (; kt < nk; ++kt) stage(kt, std::false_type{});
   // no prefetch DMA may still be writing this workgroup's LDS when it ends
-  if constexpr (PF > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---------------------------------------------------------------- epilogue
   // Lane holds, for fragment (i, j), row wm*WTM + i*16 + (lane % 16) and the 4

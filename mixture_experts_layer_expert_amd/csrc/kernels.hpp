@@ -8,8 +8,8 @@ namespace moe {
 
 // ---- per-kernel timing (prof.hip)
 enum KernelId : int {
-  kKRouteTopk, kKRouteHist, kKRouteScatter, kKTilemap, kKGather,
-  kKGemmGateUpH, kKGemmGateUpGU, kKGemmDown, kKGemmDA, kKCombine, kKReduceRows, kKReducePartials, kKGather2, kKRouterLogits,
+  kKRouteTopk, kKRouteHist, kKRouteScatter, kKTilemap,
+  kKGemmGateUpH, kKGemmGateUpGU, kKGemmDown, kKGemmDA, kKCombine, kKReduceRows, kKReducePartials, kKRouterLogits,
   kKRouterPrep, kKRouterDx, kKRouterDwr, kKRouterDwrSum, kKRowOffsets, kKDwChunkMap,
   kKDwReduce, kKBwdPrep, kKDyAmax, kKF16Operands, kKGemmBwdFused, kNumKernels
 };
@@ -39,8 +39,6 @@ hipError_t launch_tilemap(const int32_t* offsets, int E, int bm, int32_t* tstart
                           hipStream_t st);
 
 // ---- permutes (permute.hip)
-hipError_t launch_gather(const void* src0, const void* src1, void* dst0, void* dst1,
-                         const int32_t* s2f, int R, int K, int D, hipStream_t st);
 hipError_t launch_combine(const void* O, const float* w, const int32_t* f2s, void* y, int T,
                           int K, int D, hipStream_t st);
 hipError_t launch_reduce_rows(const void* dXs, void* dx, int T, int K, int D, hipStream_t st);
@@ -71,42 +69,17 @@ hipError_t launch_router_bwd(const void* x, const float* w_r, const int32_t* top
 
 // ---- grouped GEMMs (gemm.hip)
 // Workgroup tile geometry (shared by the kernels and the host-side tile
-// accounting).  The waves of a workgroup form a WM x WN grid.
-#ifndef MOE_GEMM_BM
-#define MOE_GEMM_BM 256
-#endif
-#ifndef MOE_GEMM_BN
-#define MOE_GEMM_BN 256
-#endif
-#ifndef MOE_GEMM_WM
-#define MOE_GEMM_WM 2
-#endif
-#ifndef MOE_GEMM_WN
-#define MOE_GEMM_WN 4
-#endif
-#ifndef MOE_GEMM_NS
-#define MOE_GEMM_NS 2
-#endif
-constexpr int kGemmBM = MOE_GEMM_BM;  // rows of a workgroup tile (routed rows or dW rows)
-constexpr int kGemmBN = MOE_GEMM_BN;  // columns of a tile (gate/up: BN/2 gate + BN/2 up)
-#ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 64
-#endif
-#ifndef MOE_GEMM_LOAD_SLOTS
-#define MOE_GEMM_LOAD_SLOTS 8
-#endif
-#ifndef MOE_GEMM_LOAD_STRIDE
-#define MOE_GEMM_LOAD_STRIDE 1
-#endif
-#ifndef MOE_GEMM_PREFETCH
-#define MOE_GEMM_PREFETCH 1
-#endif
-#ifndef MOE_DW_SPLIT_W2
-#define MOE_DW_SPLIT_W2 16.0f
-#endif
-#ifndef MOE_DW_SPLIT_ROWS
-#define MOE_DW_SPLIT_ROWS 100.0f
-#endif
+// accounting): 256 x 256 output tiles; 8 waves as 2 (rows) x 4 (columns), each
+// 128 x 64; 64-deep K stages, two resident in LDS.
+constexpr int kGemmBM = 256;  // rows of a workgroup tile (routed rows or dW rows)
+constexpr int kGemmBN = 256;  // columns of a tile (gate/up: BN/2 gate + BN/2 up)
+constexpr int kGemmBK = 64;   // reduction depth of one LDS stage
+constexpr int kGemmWM = 2;    // waves along the rows
+constexpr int kGemmWN = 4;    // waves along the columns
+constexpr int kGemmNS = 2;    // K stages resident in LDS
+// The next stage's loads are spread over the first kGemmLoadSlots rows of
+// MFMAs of the current stage.
+constexpr int kGemmLoadSlots = 8;
 // An expert with n rows whose router weights have squares summing to S gets
 // the fp16 hi + lo split of the rounded dW operand (two MFMA passes) when
 //   S * (1 + kDwSplitRows / n) * max(1, 3 D / (8 I)) > kDwSplitW2,
@@ -116,37 +89,25 @@ constexpr int kGemmBN = MOE_GEMM_BN;  // columns of a tile (gate/up: BN/2 gate +
 // give the per-entry sums of squares a heavier tail over the D x I entries,
 // and a wide D against I makes the gate/up gradient terms larger, hence the
 // two factors.
-constexpr float kDwSplitW2 = MOE_DW_SPLIT_W2;
-constexpr float kDwSplitRows = MOE_DW_SPLIT_ROWS;
-#ifndef MOE_DW_CHUNK_ROWS
-#define MOE_DW_CHUNK_ROWS 2048
-#endif
+constexpr float kDwSplitW2 = 16.0f;
+constexpr float kDwSplitRows = 100.0f;
 // The weight-gradient GEMMs process an expert's rows in chunks of at most this
 // many rows, one workgroup per (chunk, output tile), so that a hot expert's
 // tiles are spread over the GPU like everyone else's.  Chunk 0 writes (or
 // accumulates into) the output; chunks 1.. write partial tiles that a
 // reduction then adds in chunk order.
-constexpr int kDwChunkRows = MOE_DW_CHUNK_ROWS;
-constexpr int kGemmPrefetch = MOE_GEMM_PREFETCH;  // L2 prefetch distance in stages
-#ifndef MOE_GEMM_PREFETCH_LEAD
-#define MOE_GEMM_PREFETCH_LEAD 2
-#endif
+constexpr int kDwChunkRows = 2048;
+// L2 prefetch distance in stages: each stage touches the lines of the stage
+// kGemmPrefetch after the one it loads.
+constexpr int kGemmPrefetch = 1;
 // The "lead" prefetch policy of the gate/up and down GEMMs: only the first
 // tile of each group that shares an operand slice touches it, at distance
 // kGemmPrefetchLead.  The launch table (abi.hip) picks it when the experts
 // average at least kLeadMinRows routed rows (their tiles then run side by
 // side on an XCD); with fewer rows, and in the other GEMMs, every tile
 // touches its own lines at distance kGemmPrefetch, which measured faster.
-constexpr int kGemmPrefetchLead = MOE_GEMM_PREFETCH_LEAD;
+constexpr int kGemmPrefetchLead = 2;
 constexpr int kLeadMinRows = 256;
-constexpr int kGemmBK = MOE_GEMM_BK;  // reduction depth of one LDS stage (32 or 64)
-constexpr int kGemmWM = MOE_GEMM_WM;  // waves along the rows
-constexpr int kGemmWN = MOE_GEMM_WN;  // waves along the columns
-constexpr int kGemmNS = MOE_GEMM_NS;  // K stages resident in LDS
-// The weight-gradient GEMMs can gather a token-major operand inside their
-// loads (square tiles, double-buffered stages); otherwise the backward first
-// copies the routed rows into expert order.
-constexpr bool kGemmGatherDw = kGemmBM == kGemmBN && kGemmNS == 2;
 
 enum GemmMode : int {
   kGateUpH = 0,    // H  = silu(Xs Wg^T) * (Xs Wu^T)                       bf16 [R, I]

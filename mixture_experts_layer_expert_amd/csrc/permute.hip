@@ -1,13 +1,13 @@
-// Memory-bound kernels around the expert GEMMs (gfx950): gather into expert
-// order, router-weighted combine, the reduction of routed gradients back onto
+// Memory-bound kernels around the expert GEMMs (gfx950): router-weighted combine, the reduction of routed gradients back onto
 // tokens, and the backward's operand preparation (max|dy| for the gradient
 // scale; fp16 copies of x and s dy for the weight-gradient GEMMs).  Each
 // thread moves 16-byte chunks; rows are contiguous, so every wave reads and
 // writes whole 16-byte-aligned row segments.
 //
 // Method: LigerCute README (liger-cute-kernels 0.8.3), "LigerMoE design":
-//   - Forward pass: the sorted tokens are copied into the expert-ordered
-//     staging buffer before the expert loop; a final local combine applies the
+//   - Forward pass: the page copies the sorted tokens into an expert-ordered
+//     staging buffer before the expert loop (here the GEMMs gather the rows
+//     inside their operand loads instead); a final local combine applies the
 //     router weights once every expert result is there.
 //   - Backward pass: routed expert-output gradients are formed first; a final
 //     local step reduces the routed dX contributions back to the tokens.
@@ -17,28 +17,10 @@ namespace moe {
 
 constexpr int kPermuteThreads = 256;
 
-#ifndef MOE_PERMUTE_GRID_CAP
-#define MOE_PERMUTE_GRID_CAP (256 * 64)
-#endif
 static inline int grid_for(size_t work) {
   size_t b = (work + kPermuteThreads - 1) / kPermuteThreads;
-  const size_t cap = MOE_PERMUTE_GRID_CAP;  // enough resident waves to saturate HBM; rest loop
+  const size_t cap = 256 * 64;  // enough resident waves to saturate HBM; the rest loop
   return (int)(b < 1 ? 1 : (b > cap ? cap : b));
-}
-
-// dst0[p, :] = src0[sorted_to_flat[p] / K, :]  (and the same for src1/dst1 if given)
-__global__ __launch_bounds__(kPermuteThreads) void gather_rows_kernel(
-    const u32x4* __restrict__ src0, const u32x4* __restrict__ src1, u32x4* __restrict__ dst0,
-    u32x4* __restrict__ dst1, const int32_t* __restrict__ s2f, int R, int K, int cpr) {
-  const size_t total = (size_t)R * cpr;
-  for (size_t c = (size_t)blockIdx.x * kPermuteThreads + threadIdx.x; c < total;
-       c += (size_t)gridDim.x * kPermuteThreads) {
-    const size_t p = c / cpr;
-    const int j = (int)(c - p * cpr);
-    const size_t t = (size_t)(s2f[p] / K);
-    dst0[c] = src0[t * cpr + j];
-    if (src1) dst1[c] = src1[t * cpr + j];
-  }
 }
 
 // y[t, :] = sum_{k<K} w[t,k] * O[flat_to_sorted[t*K+k], :]   (fp32, k ascending)
@@ -202,16 +184,6 @@ hipError_t launch_f16_operands(const void* x, const void* dy, const float* gscal
   if (n == 0) return hipSuccess;
   MOE_LAUNCH(kKF16Operands, f16_operands_kernel, dim3(grid_for(n / 8)), dim3(kPermuteThreads), 0,
              st, (const u32x4*)x, (const u32x4*)dy, gscale, (u32x4*)x16, (u32x4*)dy16, n / 8);
-  return hipGetLastError();
-}
-
-hipError_t launch_gather(const void* src0, const void* src1, void* dst0, void* dst1,
-                         const int32_t* s2f, int R, int K, int D, hipStream_t st) {
-  const int cpr = D / 8;
-  if (R == 0) return hipSuccess;
-  MOE_LAUNCH(src1 ? kKGather2 : kKGather, gather_rows_kernel, dim3(grid_for((size_t)R * cpr)), dim3(kPermuteThreads),
-                     0, st, (const u32x4*)src0, (const u32x4*)src1, (u32x4*)dst0, (u32x4*)dst1,
-                     s2f, R, K, cpr);
   return hipGetLastError();
 }
 

@@ -36,9 +36,9 @@ bool capturing(hipStream_t st) {
 
 const char* const kNames[kNumKernels] = {
     "route_topk",   "route_hist",    "route_scatter", "tilemap",
-    "gather",       "gemm_gateup_h", "gemm_gateup_gu", "gemm_down",    "gemm_da",
+    "gemm_gateup_h", "gemm_gateup_gu", "gemm_down",    "gemm_da",
     "combine",      "reduce_rows",
-    "reduce_partials", "gather2",   "router_logits", "router_prep",  "router_dx",
+    "reduce_partials", "router_logits", "router_prep",  "router_dx",
     "router_dwr",   "router_dwr_sum", "row_offsets", "dw_chunkmap", "dw_reduce",
     "bwd_prep",     "dy_amax",       "f16_operands", "gemm_bwd_fused"};
 
