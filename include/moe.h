@@ -136,8 +136,12 @@ moe_status moe_route_sort_noalloc(const moe_dims *dims, const float *logits, int
  *   topk_w, offsets, sorted_to_flat, flat_to_sorted   as produced by moe_route_sort
  *   y               device bf16 [T, D]   out
  *   ws, ws_bytes    device workspace of at least moe_workspace_bytes(dims, MOE_PHASE_FWD)
- * Intermediates (SwiGLU activations, unweighted expert outputs) are stored as
- * bf16 in the workspace; all GEMMs accumulate in fp32. */
+ * Intermediates live in the workspace: the SwiGLU activations H as fp16 (the
+ * down GEMM multiplies fp16, its bf16 weights converted exactly where they are
+ * in fp16's normal range), the unweighted expert outputs as bf16; all GEMMs
+ * accumulate in fp32.  Range: |h| = |silu(g) u| <= 65504 (fp16); beyond it
+ * the affected outputs come out +-inf or NaN, never finite and wrong (the
+ * backward has the same limit on w h). */
 moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, const void *w_up,
                    const void *w_down, const float *topk_w, const int32_t *offsets,
                    const int32_t *sorted_to_flat, const int32_t *flat_to_sorted, void *y,
@@ -169,7 +173,14 @@ moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, cons
  * fp32 range): no loss scaling is needed.  x enters the weight gradients as
  * fp16 without a scale: |x| above 65504 saturates there, and values below
  * 2^-14 keep less relative precision (activations are far inside that
- * range).  Experts with no
+ * range).  Range of the fp16 gradient operands: with w the router weight,
+ * h = silu(g) u and dA = dOu W_down, the backward needs |w h| <= 65504 (the
+ * dW_down operand) and s |dG|, s |dU| <= 65504 (the dX and dW_gate/up
+ * operands); roughly, |g u| below ~6e4 for unit router weights.  Beyond it
+ * the gradients that pass through the overflowing operand come out +-inf or
+ * NaN (never finite and wrong), as in fp16 loss-scaled training: dW_down
+ * for Hw, dX, dW_gate and dW_up for dG and dU.  The forward output and
+ * d_topk_w (fp32 partials) are unaffected.  Experts with no
  * rows get exact zeros (or are left unchanged when accumulating).
  *   ws, ws_bytes   device workspace of at least moe_workspace_bytes(dims, MOE_PHASE_BWD) */
 moe_status moe_bwd(const moe_dims *dims, const void *x, const void *w_gate, const void *w_up,

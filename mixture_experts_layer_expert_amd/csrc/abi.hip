@@ -75,7 +75,8 @@ struct Carve {
 
 struct FwdWs {
   int32_t* tstart;
-  bf16_t *h, *o;
+  f16_t* h;   // SwiGLU activations H [R, I], fp16 (the down GEMM's operand)
+  bf16_t* o;  // unweighted expert outputs O [R, D]
 };
 struct BwdWs {
   int32_t* tstart;
@@ -126,7 +127,7 @@ size_t fwd_ws(const moe_dims& d, FwdWs* w, void* base) {
   Carve c{(char*)base};
   const size_t R = (size_t)d.T * d.K;
   w->tstart = c.take<int32_t>(d.E + 1);
-  w->h = c.take<bf16_t>(R * d.I);
+  w->h = c.take<f16_t>(R * d.I);
   w->o = c.take<bf16_t>(R * d.D);
   return c.used;
 }
@@ -368,11 +369,11 @@ MOE_EXPORT moe_status moe_fwd(const moe_dims* dims, const void* x, const void* w
   g.K = d.D;
   g.n_tiles = (int)gateup_tiles(d.I);
   g.lead = gemm_lead(d);
-  g.C0 = w.h;
+  g.C0 = (bf16_t*)w.h;  // fp16 bits
   g.ldc = d.I;
   MOE_TRY(launch_gemm(kGateUpH, g, rowgrouped_grid(d, g.n_tiles), st));
   // down: O[R, D] = H Wd^T
-  g.A = w.h;
+  g.A = (const bf16_t*)w.h;  // fp16 bits
   g.lda = d.I;
   g.B0 = (const bf16_t*)w_down;
   g.a_gather = nullptr;

@@ -33,8 +33,11 @@
 //   - the MFMA takes the B fragment as its first operand, so each lane ends
 //     with 4 consecutive output columns of one row (8-byte bf16 or 16-byte
 //     fp32 stores);
-//   - precision: every product accumulates in fp32.  The forward multiplies
-//     bf16 (H is stored as bf16 for the down GEMM).  The backward runs dA =
+//   - precision: every product accumulates in fp32.  The gate/up GEMM
+//     multiplies bf16; H is stored as fp16 (8 times finer than bf16: with bf16
+//     H the forward output of a dense top-1 layer reached 1.04 of the error
+//     bar where y cancels), so the down GEMM multiplies fp16, converting its
+//     bf16 weight fragments after the LDS read.  The backward runs dA =
 //     dOu Wd first and stores it fp32; the recompute GEMM then holds G and U
 //     in its fp32 accumulators and does the SwiGLU backward and the
 //     router-weight partials in its epilogue.  The per-row dX partials
@@ -277,7 +280,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
   const int wm = wave / WN, wn = wave % WN;
   constexpr bool kRowGrouped = MODE != kDW;
   constexpr bool kGateUp = MODE == kGateUpH || MODE == kGateUpBwd;
-  constexpr bool kF16 = MODE == kDXs || MODE == kDW;
+  constexpr bool kF16 = MODE == kDown || MODE == kDXs || MODE == kDW;
   constexpr bool kBmn = MODE == kDA || MODE == kDXs || MODE == kDW;  // B row-contiguous
   using frag_t = typename std::conditional<kF16, f16x8, bf16x8>::type;
   // L2 prefetch distance of this GEMM, and whether only the first tile of each
@@ -671,8 +674,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
           bfr[j] = read_kmajor<frag_t>(sb, wn * WTN + j * 16, kk, lane);
         }
       }
-      // dXs: the weights (B) are bf16; every other fp16 operand is stored as fp16
-      if constexpr (MODE == kDXs) {
+      // down, dXs: the weights (B) are bf16; every other fp16 operand is stored as fp16
+      if constexpr (MODE == kDown || MODE == kDXs) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) bfr[j] = frag_to_f16(bfr[j]);
       }
@@ -738,7 +741,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
         float h[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) h[q] = g[q] * sigmoidf_(g[q]) * u[q];
-        strip_put<S>(stg, frow, cl, u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])});
+        // H is the down GEMM's fp16 operand
+        strip_put<S>(stg, frow, cl, u32x2{pack_f16x2(h[0], h[1]), pack_f16x2(h[2], h[3])});
       }
       strip_out<S>(stg, lane, rows_valid - rb, p.N - col0, [&](int r, int) {
         return (char*)(p.C0 + (size_t)(m0 + rb + r) * p.ldc + col0); }, store16);

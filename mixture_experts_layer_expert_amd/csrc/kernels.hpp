@@ -110,10 +110,10 @@ constexpr int kGemmPrefetchLead = 2;
 constexpr int kLeadMinRows = 256;
 
 enum GemmMode : int {
-  kGateUpH = 0,    // H  = silu(Xs Wg^T) * (Xs Wu^T)                       bf16 [R, I]
+  kGateUpH = 0,    // H  = silu(Xs Wg^T) * (Xs Wu^T)                       fp16 [R, I]
   kGateUpBwd = 1,  // recompute G = Xs Wg^T, U = Xs Wu^T; the SwiGLU backward in the
                    // epilogue from dA: dG, dU, Hw (fp16) and router-weight partials
-  kDown = 2,       // O  = H Wd^T                                         bf16 [R, D]
+  kDown = 2,       // O  = H Wd^T (fp16 products)                         bf16 [R, D]
   kDA = 3,         // dA = dOu Wd                                         fp32 [R, I]
   kDXs = 4,        // dXs = dG Wg + dU Wu            fp32 [R, D], row f = flat slot of the routed row
   kDW = 5,         // dW[e] = A_e^T B_e over the expert's rows              fp32

@@ -97,6 +97,11 @@ SMALL = {
     # rule weighed the row count; now they take the two-pass split
     "few_rows_sigmoid": lambda: _custom(T=652, D=320, I=64, E=33, K=1, score=1, seed=512,
                                         dead=(22, 31)),
+    # dense top-1 layers (one expert, router weight 1) where y cancels: with
+    # H stored bf16 the forward reached 0.95 and 1.04 of the bar on these
+    # two (emulated); H is fp16 now, worst emulated 0.25-0.27
+    "dense_top1_cancel": lambda: _custom(T=787, D=64, I=192, E=1, K=1, score=0, seed=509),
+    "dense_top1_cancel2": lambda: _custom(T=8192, D=64, I=64, E=1, K=1, score=0, seed=67316),
     # one token
     "one_token": lambda: _custom(T=1, D=64, I=64, E=8, K=2, score=0, seed=107),
     # the maximum expert count: 1024 experts, most of them empty
@@ -110,6 +115,101 @@ SMALL = {
 def test_layer_parity_small(case):
     wl, data = SMALL[case]()
     _full_compare(wl, data)
+
+
+# ----------------------------------------------------------------------------- large activations
+
+def _pow2_scaled(wl, data, up=1.0, down=1.0):
+    """The workload with W_up multiplied by `up` and W_down by `down`, powers of
+    two (exact in bf16).  Then u, h, Hw, dG scale by `up`; dA by `down`; and
+    the outputs scale exactly: y, d_topk_w by up * down, dx and dw_gate by
+    up * down, dw_down by up, dw_up by down (dU = w dA silu(g) and x do not
+    see `up`)."""
+    out = dict(data)
+    f32, bf = synth.bf16_bits_to_f32, synth.f32_to_bf16_bits
+    out["w_up"] = bf(f32(data["w_up"]) * np.float32(up))
+    out["w_down"] = bf(f32(data["w_down"]) * np.float32(down))
+    return wl, out
+
+
+def _output_scales(up, down):
+    return {"y": up * down, "d_topk_w": up * down, "dx": up * down, "dw_gate": up * down,
+            "dw_up": down, "dw_down": up}
+
+
+def _refs(wl, data):
+    L, idx, w = G.oracle_layer(data, wl.K, wl.score)
+    dx, drw = oracle.backward_tokens(L, idx, w)
+    dwg, dwu, dwd = oracle.backward_dw(L, idx, w)
+    return L, idx, w, {"y": oracle.forward(L, idx, w), "dx": dx, "d_topk_w": drw,
+                       "dw_gate": dwg, "dw_up": dwu, "dw_down": dwd}
+
+
+def _gpu_outputs(y, grads):
+    return {"y": G.bf16_dev_to_f64(y), "dx": G.bf16_dev_to_f64(grads["dx"]),
+            "d_topk_w": G.host(grads["d_topk_w"]), "dw_gate": G.host(grads["dw_gate"]),
+            "dw_up": G.host(grads["dw_up"]), "dw_down": G.host(grads["dw_down"])}
+
+
+LARGE = {
+    # softmax top-8 of 16 (router weights near 1/8): every expert's dW
+    # operand takes the one-pass fp16 path
+    "onepass": lambda: _custom(T=512, D=256, I=128, E=16, K=8, score=0, seed=121),
+    # top-1 sigmoid (router weights 0.5..1): every expert takes the hi + lo split
+    "split": lambda: _custom(T=512, D=256, I=128, E=4, K=1, score=1, seed=122),
+}
+
+
+@pytest.mark.parametrize("case", list(LARGE))
+def test_layer_parity_large_activations(case):
+    """H and Hw = w h (fp16 operands of the down and dW_down GEMMs) and dG
+    (scaled fp16 operand of dX and dW_gate) reach the thousands: W_up times
+    2^10 makes |h| up to about 1.5e4.  Every output scales exactly with W_up, so
+    it must meet the bar scaled by its own factor (the unit-scale bar for
+    output / factor), on both dW paths."""
+    up = 1024.0
+    wl, data = _pow2_scaled(*LARGE[case](), up=up)
+    dev = G.DeviceInputs(data)
+    route, y, grads = G.run_gpu(dev, wl.K, wl.score, backward=True)
+    idx, w, _ = G.check_route_exact(route, data, wl.K, wl.score, wl.E)
+    L, _, _, ref = _refs(wl, data)
+    got = _gpu_outputs(y, grads)
+    for name, c in _output_scales(up, 1.0).items():
+        G.assert_close(got[name] / c, ref[name] / c, f"{name} (/{c:g})")
+    counts = np.bincount(idx.ravel(), minlength=wl.E)
+    w2 = np.bincount(idx.ravel(), weights=(w * w).ravel(), minlength=wl.E)
+    crit = w2 * (1 + 100.0 / np.maximum(counts, 1)) * max(1.0, 3 * wl.D / (8 * wl.I))
+    assert np.all((crit > 16) == (case == "split")), crit  # the case takes the path it names
+    g = np.einsum("td,eid->tei", L.x[::8], L.w_gate)
+    u = np.einsum("td,eid->tei", L.x[::8], L.w_up)
+    h_max = float(np.abs(g / (1 + np.exp(-g)) * u).max())
+    assert 3e3 < h_max < 65504, h_max
+
+
+@pytest.mark.parametrize("which", ["h", "dg"])
+def test_fp16_range_overflow_is_not_silent(which):
+    """Beyond fp16's range the outputs that went through the overflowing
+    operand come out non-finite, never finite and wrong; the others still meet
+    their scaled bar.  "h": W_up times 2^14 puts |h| far above 65504, so the
+    forward output (fp16 H) and dW_down (fp16 Hw) break; d_topk_w (fp32
+    partials) does not.  "dg": W_down times 2^16 makes dA, and with it s dG
+    and s dU, exceed 65504 (the gradient scale s follows dy, not dA), so dX
+    and dW_gate / dW_up break, while the forward and dW_down do not."""
+    up, down = (16384.0, 1.0) if which == "h" else (1.0, 65536.0)
+    wl, data = _pow2_scaled(*_custom(T=256, D=256, I=128, E=4, K=1, score=1, seed=123),
+                            up=up, down=down)
+    dev = G.DeviceInputs(data)
+    route, y, grads = G.run_gpu(dev, wl.K, wl.score, backward=True)
+    G.check_route_exact(route, data, wl.K, wl.score, wl.E)
+    _, _, _, ref = _refs(wl, data)
+    got = _gpu_outputs(y, grads)
+    sc = _output_scales(up, down)
+    broken = ("y", "dw_down") if which == "h" else ("dx", "dw_gate", "dw_up")
+    kept = ("d_topk_w",) if which == "h" else ("y", "d_topk_w", "dw_down")
+    for name in broken:
+        assert not np.all(np.isfinite(got[name])), f"{name}: the overflow must show"
+    for name in kept:
+        G.assert_close(got[name] / sc[name], ref[name] / sc[name], f"{name} (/{sc[name]:g})")
 
 
 # ----------------------------------------------------------------------------- random shapes
