@@ -166,6 +166,34 @@ def backward_dw(L: Layer, idx, w, tokens=None):
     return dwg, dwu, dwd
 
 
+def expert_dw(L: Layer, idx, w, e: int):
+    """(dW_gate[e] [I, D], dW_up[e] [I, D], dW_down[e] [D, I]) of one expert,
+    summed over all of its routed rows, as the page's backward accumulates an
+    expert's weight gradients over all of its token tiles (LigerCute README,
+    "LigerMoE design", Backward pass).  Each step is its plain formula, with
+    float64 matrix products (a library primitive) for the sums:
+      rows r = (t, k) with idx[t, k] = e, in ascending flat slot t*K + k;
+      g = x_t W_gate[e]^T,  u = x_t W_up[e]^T,  dA = dY_t W_down[e]   (per row);
+      h = silu(g) u;  dG = w dA u sigma(g) (1 + g (1 - sigma(g)));
+      dU = w dA silu(g);  Hw = w h   (w = the row's router weight);
+      dW_gate = dG^T X,  dW_up = dU^T X,  dW_down = dY^T Hw.
+    Needs the layer's dy."""
+    idx = np.asarray(idx)
+    w = np.asarray(w, dtype=np.float64)
+    t, k = np.nonzero(idx == e)  # row-major order: ascending flat slot
+    X, dY = L.x[t], L.dy[t]
+    wr = w[t, k][:, None]
+    g = X @ L.w_gate[e].T
+    u = X @ L.w_up[e].T
+    dA = dY @ L.w_down[e]
+    sg = 1.0 / (1.0 + np.exp(-g))
+    silu = g * sg
+    dG = wr * dA * u * sg * (1.0 + g * (1.0 - sg))
+    dU = wr * dA * silu
+    Hw = wr * silu * u
+    return dG.T @ X, dU.T @ X, dY.T @ Hw
+
+
 def dw_entries(L: Layer, idx, w, which, e, r, c):
     """Single weight-gradient entries: which 0 = dW_gate[e,r,c], 1 = dW_up, 2 = dW_down."""
     lib = _load()

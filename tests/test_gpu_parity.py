@@ -279,16 +279,24 @@ def test_route_empty_batch():
 
 # ----------------------------------------------------------------------------- full size: sampled
 
-def _sampled_compare(wl, n_tokens=24, n_entries=40, seed=0, full_hot=False):
+def _sampled_compare(wl, n_tokens=24, n_entries=40, seed=0, full_hot=False, all_tokens=False):
     """Sampled tokens and dW entries at full size; with full_hot, every entry of
     the hottest expert's three weight gradients as well (the oracle's dW over
-    the tokens routed to that expert, which is exact for it)."""
+    the tokens routed to that expert, which is exact for it); with all_tokens,
+    y and d_topk_w of every token (the oracle's forward with its expert
+    outputs o, and d_topk_w[t, k] = <dy[t], o[t, k]>, its definition)."""
     data = synth.generate(wl)
     dev = G.DeviceInputs(data)
     route, y, grads = G.run_gpu(dev, wl.K, wl.score, backward=True)
     idx, w, counts = G.check_route_exact(route, data, wl.K, wl.score, wl.E)
     L, _, _ = G.oracle_layer(data, wl.K, wl.score)
     tok = synth.sample_indices(wl.T, n_tokens, seed, must=(0, wl.T - 1))
+    if all_tokens:
+        y_ref, o_ref = oracle.forward(L, idx, w, want_o=True)
+        G.assert_close(G.bf16_dev_to_f64(y), y_ref, f"{wl.name} y (every token)")
+        drw_all = np.einsum("td,tkd->tk", L.dy, o_ref)
+        G.assert_close(G.host(grads["d_topk_w"]), drw_all, f"{wl.name} d_topk_w (every token)")
+        del y_ref, o_ref
     y_ref = oracle.forward(L, idx, w, tokens=tok)
     G.assert_close(G.bf16_dev_to_f64(y[tok]), y_ref, f"{wl.name} y")
     dx_ref, drw_ref = oracle.backward_tokens(L, idx, w, tokens=tok)
@@ -314,11 +322,8 @@ def _sampled_compare(wl, n_tokens=24, n_entries=40, seed=0, full_hot=False):
         for ee in np.flatnonzero(counts == 0):
             assert not G.host(grads[name][ee]).any(), f"{name}[{ee}] of an empty expert"
     if full_hot:
-        tok_hot = np.flatnonzero((idx == hot).any(1))
-        dwg, dwu, dwd = oracle.backward_dw(L, idx, w, tokens=tok_hot)
-        for name, ref in (("dw_gate", dwg), ("dw_up", dwu), ("dw_down", dwd)):
-            G.assert_close(G.host(grads[name][hot]), ref[hot], f"{wl.name} {name}[{hot}] (all entries)")
-        del dwg, dwu, dwd
+        for name, ref in zip(("dw_gate", "dw_up", "dw_down"), oracle.expert_dw(L, idx, w, hot)):
+            G.assert_close(G.host(grads[name][hot]), ref, f"{wl.name} {name}[{hot}] (all entries)")
     # whole-array property at full size: outputs finite everywhere
     torch = G.torch_mod()
     for t in (y, grads["dx"], grads["dw_gate"], grads["dw_up"], grads["dw_down"], grads["d_topk_w"]):
@@ -327,7 +332,9 @@ def _sampled_compare(wl, n_tokens=24, n_entries=40, seed=0, full_hot=False):
 
 @pytest.mark.slow
 def test_qwen3_30b_a3b_full_size():
-    _sampled_compare(synth.QWEN3_30B_A3B, full_hot=True)
+    """Every token's y and d_topk_w, dX of 512 tokens, sampled dW entries of
+    every matrix and all entries of the hottest expert's three dW."""
+    _sampled_compare(synth.QWEN3_30B_A3B, n_tokens=512, full_hot=True, all_tokens=True)
 
 
 @pytest.mark.slow
@@ -343,7 +350,10 @@ def test_qwen3_30b_a3b_max_tokens():
 
 @pytest.mark.slow
 def test_llama4_scout_full_size():
-    _sampled_compare(synth.LLAMA4_SCOUT, n_tokens=12, n_entries=512)
+    """Sampled tokens and dW entries, and every entry of the hottest expert's
+    three weight gradients (3 x 8192 x 5120 entries, each a sum over its ~540
+    rows; every Scout expert takes the split dW operand)."""
+    _sampled_compare(synth.LLAMA4_SCOUT, n_tokens=12, n_entries=512, full_hot=True)
 
 
 @pytest.mark.slow

@@ -319,6 +319,45 @@ def pin_backward_dw_token_subset():
         np.testing.assert_allclose(u, v, rtol=1e-13, atol=1e-15)
 
 
+def pin_expert_dw_finite_differences():
+    """One expert's weight gradients (the matrix-product form) against central
+    finite differences of L = <dY, y> in that expert's W_gate, W_up and W_down,
+    for every expert of a small layer (one of them receives no rows)."""
+    L, logits = _random_layer(T=9, D=5, I=4, E=4, K=2, score=synth.SOFTMAX_TOPK, seed=36)
+    logits[:, 3] = -50.0                                   # expert 3 never selected
+    idx, w = oracle.route(logits, 2, synth.SOFTMAX_TOPK)
+    h = 1e-5
+    for e in range(4):
+        grads = oracle.expert_dw(L, idx, w, e)
+        for name, grad in zip(("w_gate", "w_up", "w_down"), grads):
+            flat = getattr(L, name)[e].reshape(-1)         # a view: edits reach the oracle
+            num = np.empty(flat.size)
+            for j in range(flat.size):
+                keep = flat[j]
+                flat[j] = keep + h
+                lp = _loss(L, idx, w)
+                flat[j] = keep - h
+                lm = _loss(L, idx, w)
+                flat[j] = keep
+                num[j] = (lp - lm) / (2 * h)
+            np.testing.assert_allclose(grad.reshape(-1), num, rtol=1e-6, atol=1e-8,
+                                       err_msg=f"{name}[{e}]")
+        if e == 3:
+            assert not any(g.any() for g in grads)
+
+
+def pin_expert_dw_matches_row_loop():
+    """The matrix-product form equals the per-row loop of backward_dw for every
+    expert, with either score function."""
+    for score, seed in ((synth.SOFTMAX_TOPK, 37), (synth.SIGMOID, 38)):
+        L, logits = _random_layer(T=40, D=16, I=8, E=5, K=2, score=score, seed=seed)
+        idx, w = oracle.route(logits, 2, score)
+        full = oracle.backward_dw(L, idx, w)
+        for e in range(5):
+            for a, b in zip(oracle.expert_dw(L, idx, w, e), full):
+                np.testing.assert_allclose(a, b[e], rtol=1e-12, atol=1e-14)
+
+
 # --------------------------------------------------------------------------- router side
 
 def pin_router_logits_library():
@@ -447,6 +486,8 @@ PINS = [
     pin_backward_euler_identities,
     pin_backward_empty_expert_and_entries,
     pin_backward_dw_token_subset,
+    pin_expert_dw_finite_differences,
+    pin_expert_dw_matches_row_loop,
     pin_router_logits_library,
     pin_router_backward_finite_differences,
     pin_router_backward_invariants,
