@@ -102,6 +102,9 @@ SMALL = {
     # two (emulated); H is fp16 now, worst emulated 0.25-0.27
     "dense_top1_cancel": lambda: _custom(T=787, D=64, I=192, E=1, K=1, score=0, seed=509),
     "dense_top1_cancel2": lambda: _custom(T=8192, D=64, I=64, E=1, K=1, score=0, seed=67316),
+    # wide experts with few tokens (I = 1024: 32-stage reductions over 2I in the
+    # dXs GEMM, 16-stage ones in dA), every expert in one m-tile
+    "wide_experts": lambda: _custom(T=300, D=256, I=1024, E=4, K=2, score=0, seed=113),
     # one token
     "one_token": lambda: _custom(T=1, D=64, I=64, E=8, K=2, score=0, seed=107),
     # the maximum expert count: 1024 experts, most of them empty
