@@ -40,3 +40,18 @@ def test_step_stats_and_host_cpu():
     assert st["p10"] <= st["median"] <= st["p90"]
     h = bench.host_cpu()
     assert h["nproc"] >= 1 and h["cpus_on_host"] >= h["nproc"] and isinstance(h["cpu_model"], str)
+
+
+def test_gemm_min_bytes_and_ceilings():
+    """Every grouped GEMM kernel the library launches has its unavoidable bytes;
+    at the Qwen3-30B-A3B shape their arithmetic intensities put gate/up and dA
+    above the MFMA ridge (312 FLOP/B at 2.5 PFLOP/s and 8 TB/s) and the fused
+    dXs + dW launch below it."""
+    wl = synth.QWEN3_30B_A3B
+    mb = bench.gemm_min_bytes(wl)
+    work = bench.kernel_work(wl)
+    names = _kernel_names()
+    assert set(mb) == {n for n in names if n.startswith("gemm_")}
+    ai = {k: work[k][1] / v for k, v in mb.items()}
+    assert all(v > 0 for v in mb.values())
+    assert ai["gemm_gateup_h"] > 312 and ai["gemm_da"] > 312 and ai["gemm_bwd_fused"] < 312
