@@ -22,6 +22,13 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
 }
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+// the two fp16 halves of a 32-bit word as floats
+__device__ __forceinline__ float f16_lo(uint32_t pair) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(pair & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t pair) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(pair >> 16));
+}
 
 // float -> bf16 bits, round to nearest, ties to even (inputs are finite).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
@@ -54,7 +61,13 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(v), bf16_hi(v)));
 }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// sigma(z) = 1 / (1 + e^-z) with the hardware reciprocal (v_rcp_f32, about one
+// ulp) instead of an IEEE division (a ten-instruction sequence): the SwiGLU
+// epilogues evaluate it once per element, and its error stays far below the
+// fp16 / bf16 roundings of the values it feeds.
+__device__ __forceinline__ float sigmoidf_(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 template <typename T>
 __device__ __forceinline__ T ceil_div(T a, T b) { return (a + b - 1) / b; }
