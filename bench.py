@@ -58,8 +58,8 @@ def kernel_work(wl: synth.Workload) -> dict:
         "gemm_bwd_fused": ("mfma", 10 * dir_),
         # combine: read O (R*D*2), weights and indices (8R), write y (T*D*2)
         "combine": ("hbm", 2.0 * R * D + 8 * R + 2.0 * T * D),
-        # dX reduce: read the fp32 per-row partials (R*D*4) and indices, write dX (T*D*2)
-        "reduce_rows": ("hbm", 4.0 * R * D + 4 * R + 2.0 * T * D),
+        # dX reduce: read the fp16 per-row partials (R*D*2), write dX (T*D*2)
+        "reduce_rows": ("hbm", 2.0 * R * D + 2.0 * T * D),
         # dRouterWeights: read the per-row partials (one per gate/up column tile and wave
         # column, 4 * ceil(I / 128) per row) and the indices, write one value per row
         "reduce_partials": ("hbm", 4.0 * R * (4 * math.ceil(I / 128)) + 8 * R),
@@ -101,9 +101,9 @@ def gemm_min_bytes(wl: synth.Workload) -> dict:
         "gemm_down": 2.0 * R * I + w1 + 2.0 * R * D,
         # dy rows, W_down in; dA (fp32) out
         "gemm_da": 2.0 * T * D + w1 + 4.0 * R * I,
-        # dXs: dG | dU, W_gate + W_up in, fp32 dX rows out; dW_down: s dy (fp16), Hw in,
+        # dXs: dG | dU, W_gate + W_up in, fp16 dX rows out; dW_down: s dy (fp16), Hw in,
         # fp32 dW_down out; dW_gate / dW_up: x (fp16) in, fp32 dW_gate, dW_up out
-        "gemm_bwd_fused": 4.0 * R * I + 2 * w1 + 4.0 * R * D + 2.0 * T * D + 2.0 * R * I
+        "gemm_bwd_fused": 4.0 * R * I + 2 * w1 + 2.0 * R * D + 2.0 * T * D + 2.0 * R * I
                           + 2 * w1 + 2.0 * T * D + 4 * w1,
     }
 

@@ -91,7 +91,9 @@ struct BwdWs {
   // partial dW tiles of chunks 1.. of the chunked experts: dW_gate | dW_up, and
   // dW_down apart (the two dW GEMMs run in one launch)
   float *dw_part, *dw_part_down;
-  float *da, *dxs, *part;  // dA [R, I], dX rows [R, D] (flat order), dRW partials
+  float* da;     // dA [R, I]
+  f16_t* dxs;    // s dXs rows [R, D] fp16, flat slot order
+  float* part;   // dRW partials
 };
 
 // dW row chunks: experts with more than kDwChunkRows rows (at most R / (chunk + 1)
@@ -152,7 +154,7 @@ size_t bwd_ws(const moe_dims& d, BwdWs* w, void* base) {
   w->hw = c.take<f16_t>(R * d.I);
   w->dgu_lo = c.take<f16_t>(R * 2 * d.I);
   w->hw_lo = c.take<f16_t>(R * d.I);
-  w->dxs = c.take<float>(R * d.D);
+  w->dxs = c.take<f16_t>(R * d.D);
   w->part = c.take<float>(R * partials_per_row(d));
   return c.used;
 }
@@ -493,7 +495,7 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   gx.N = d.D;
   gx.K = 2 * d.I;
   gx.n_tiles = (d.D + kGemmBN - 1) / kGemmBN;
-  gx.Cf = w.dxs;  // rows in flat slot order (t*K + k)
+  gx.C0 = (bf16_t*)w.dxs;  // fp16 bits; rows in flat slot order (t*K + k)
   gx.ldc = d.D;
   gx.s2f = sorted_to_flat;
   gx.gscale = w.gscale;
@@ -552,7 +554,7 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
                            d.E, max_chunked, st));
 
   if (R > 0) {
-    MOE_TRY(launch_reduce_rows(w.dxs, dx, d.T, d.K, d.D, st));
+    MOE_TRY(launch_reduce_rows(w.dxs, w.gscale, dx, d.T, d.K, d.D, st));
     MOE_TRY(launch_reduce_partials(w.part, flat_to_sorted, d_topk_w, (int)R,
                                    partials_per_row(d), st));
   }

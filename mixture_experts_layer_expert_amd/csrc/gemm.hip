@@ -40,17 +40,19 @@
 //     bf16 weight fragments after the LDS read.  The backward runs dA =
 //     dOu Wd first and stores it fp32; the recompute GEMM then holds G and U
 //     in its fp32 accumulators and does the SwiGLU backward and the
-//     router-weight partials in its epilogue.  The per-row dX partials
-//     (summed over the K routed copies) stay fp32.  The gradient
+//     router-weight partials in its epilogue.  The per-row dX partials s dXs
+//     (summed over the K routed copies by the dX reduction, which removes s)
+//     are stored fp16: that rounding (2^-12 of the row) is small against the
+//     fp16 roundings of dG and dU the row already carries.  The gradient
 //     GEMMs (dXs, dW) multiply fp16: dG/dU/Hw are rounded to fp16 (3 more
 //     mantissa bits than bf16, at the same matrix-core rate); dXs converts
 //     its bf16 weight fragments after the LDS read, and the dW GEMMs read fp16
 //     copies of x and s dy written once per backward (exact for |v| in fp16's
 //     normal range).  s, a power of two with s max|dy| in [1, 2), keeps the
 //     gradient operands (s dy, s dG, s dU) clear of fp16's subnormal range
-//     and of its overflow whatever the loss scale; dXs and dW multiply their
-//     fp32 results by 1/s, so at any scale the results equal those of unit-
-//     scale gradients times the scale, bit for bit.  The dW GEMMs sum over
+//     and of its overflow whatever the loss scale; the dW epilogue and the dX
+//     reduction multiply their fp32 results by 1/s, so at any scale the
+//     results equal those of unit-scale gradients times the scale, bit for bit.  The dW GEMMs sum over
 //     all of an expert's rows, where the rounding error grows like the
 //     root-sum-square of the terms while the
 //     result can cancel to ~0.  Each term carries one factor of its row's
@@ -863,7 +865,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
       if (row_ok && lane < 16) p.part[(size_t)(m0 + r) * p.np + nt_idx * WN + wn] = dot;
     }
   } else if constexpr (MODE == kDown || MODE == kDXs || MODE == kDA) {
-    using S = Strip<WTN, MODE == kDown ? 2 : 4>;
+    // O (bf16) and s dXs (fp16) leave as 2-byte elements, dA as fp32
+    using S = Strip<WTN, MODE == kDA ? 4 : 2>;
     static_assert(NW * S::BYTES <= NS * STAGE_BYTES, "staging fits the stage buffers");
     char* const stg = lds + wave * S::BYTES;
     const int col0 = n0 + wn * WTN;
@@ -889,16 +892,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
       for (int j = 0; j < FN; ++j) {
         const int cl = j * 16 + cq;
         const f32x4 v = acc[i][j];
-        if constexpr (MODE == kDXs) strip_put<S>(stg, frow, cl, v * ginv);
+        // dXs rows keep the gradient scale s (fp16, away from its subnormal
+        // range); the dX reduction removes it after the sum
+        if constexpr (MODE == kDXs)
+          strip_put<S>(stg, frow, cl, u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])});
         else if constexpr (MODE == kDA) strip_put<S>(stg, frow, cl, v);
         else strip_put<S>(stg, frow, cl, u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
       }
       const int nrows = rows_valid - rb, ncols = p.N - col0;
       if constexpr (MODE == kDXs) {
-        // fp32 rows at their flat slot t*K + k: the K copies of a token sit
+        // rows at their flat slot t*K + k: the K copies of a token sit
         // together for the reduction
         strip_out<S>(stg, lane, nrows, ncols, [&](int, int h) {
-          return (char*)(p.Cf + (size_t)flat[i][h] * p.ldc + col0); }, store16);
+          return (char*)(p.C0 + (size_t)flat[i][h] * p.ldc + col0); }, store16);
       } else if constexpr (MODE == kDA) {
         strip_out<S>(stg, lane, nrows, ncols, [&](int r, int) {
           return (char*)(p.Cf + (size_t)(m0 + rb + r) * p.ldc + col0); }, store16);

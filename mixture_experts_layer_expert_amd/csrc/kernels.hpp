@@ -41,7 +41,10 @@ hipError_t launch_tilemap(const int32_t* offsets, int E, int bm, int32_t* tstart
 // ---- permutes (permute.hip)
 hipError_t launch_combine(const void* O, const float* w, const int32_t* f2s, void* y, int T,
                           int K, int D, hipStream_t st);
-hipError_t launch_reduce_rows(const void* dXs, void* dx, int T, int K, int D, hipStream_t st);
+// dx[t] = (1/s) sum_k dXs[t*K + k] with dXs the fp16 rows of s dXs and 1/s =
+// gscale[1] (fp32 sum, k ascending, one bf16 rounding).
+hipError_t launch_reduce_rows(const void* dXs, const float* gscale, void* dx, int T, int K, int D,
+                              hipStream_t st);
 hipError_t launch_reduce_partials(const float* part, const int32_t* f2s, float* out, int R,
                                   int np, hipStream_t st);
 // rowoff[p] = (sorted_to_flat[p] / K) * row_bytes: byte offset of routed row p's token row
@@ -115,7 +118,7 @@ enum GemmMode : int {
                    // epilogue from dA: dG, dU, Hw (fp16) and router-weight partials
   kDown = 2,       // O  = H Wd^T (fp16 products)                         bf16 [R, D]
   kDA = 3,         // dA = dOu Wd                                         fp32 [R, I]
-  kDXs = 4,        // dXs = dG Wg + dU Wu            fp32 [R, D], row f = flat slot of the routed row
+  kDXs = 4,        // s dXs = s (dG Wg + dU Wu)      fp16 [R, D], row f = flat slot of the routed row
   kDW = 5,         // dW[e] = A_e^T B_e over the expert's rows              fp32
 };
 
@@ -138,7 +141,8 @@ struct GemmArgs {
   float* dw_part;
   const int32_t* dw_split;  // [E] 1: the expert's dW operand is split hi + lo
   // backward gradient scale {s, 1/s} (see launch_bwd_prep), or null (s = 1):
-  // kGateUpBwd scales dG and dU by s; kDXs and kDW multiply their results by 1/s
+  // kGateUpBwd scales dG and dU by s; kDW multiplies its results by 1/s (kDXs
+  // keeps s in its fp16 rows; the dX reduction removes it)
   const float* gscale;
   const bf16_t* A2;  // kDW second matrix's A (dW_up), else unused
   const bf16_t* B0;  // weights (row-grouped) or token-major activations (kDW)

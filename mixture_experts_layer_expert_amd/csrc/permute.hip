@@ -69,32 +69,45 @@ __global__ __launch_bounds__(kPermuteThreads) void combine_kernel(
   }
 }
 
-// dX[t, :] = sum_{k<K} dXs[t*K + k, :]  (fp32 rows in flat slot order, fp32 sum,
-// k ascending).  The K rows of a token are contiguous, so the reads stream;
-// they are read once (non-temporal loads).
-// Each thread produces 4 outputs from one 16-byte read per routed copy; with
-// KT > 0 all K reads are in flight together.  cpr4 = D / 4.
+// dX[t, :] = (1/s) sum_{k<K} dXs[t*K + k, :]: fp16 rows of s dXs in flat slot
+// order, fp32 sum, k ascending, then the power-of-two 1/s (exact) and one
+// bf16 rounding.  The K rows of a token are contiguous, so the reads stream;
+// they are read once (non-temporal loads).  Each thread produces 8 outputs
+// from one 16-byte read per routed copy; with KT > 0 all K reads are in
+// flight together.  cpr8 = D / 8.
 template <int KT>
 __global__ __launch_bounds__(kPermuteThreads) void reduce_rows_kernel(
-    const f32x4* __restrict__ dXs, u32x2* __restrict__ dx, int T, int K_, int cpr4) {
+    const u32x4* __restrict__ dXs, const float* __restrict__ gscale, u32x4* __restrict__ dx,
+    int T, int K_, int cpr8) {
   const int K = KT > 0 ? KT : K_;
-  const size_t total = (size_t)T * cpr4;
+  const float inv = gscale[1];
+  const size_t total = (size_t)T * cpr8;
   for (size_t c = (size_t)blockIdx.x * kPermuteThreads + threadIdx.x; c < total;
        c += (size_t)gridDim.x * kPermuteThreads) {
-    const size_t t = c / cpr4;
-    const int j = (int)(c - t * cpr4);
-    const f32x4* rows = dXs + t * K * cpr4 + j;
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    const size_t t = c / cpr8;
+    const int j = (int)(c - t * cpr8);
+    const u32x4* rows = dXs + t * K * cpr8 + j;
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto add = [&](u32x4 v) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a[2 * q] += f16_lo(v[q]);
+        a[2 * q + 1] += f16_hi(v[q]);
+      }
+    };
     if constexpr (KT > 0) {
-      f32x4 v[KT];
+      u32x4 v[KT];
 #pragma unroll
-      for (int k = 0; k < KT; ++k) v[k] = __builtin_nontemporal_load(rows + (size_t)k * cpr4);
+      for (int k = 0; k < KT; ++k) v[k] = __builtin_nontemporal_load(rows + (size_t)k * cpr8);
 #pragma unroll
-      for (int k = 0; k < KT; ++k) a += v[k];
+      for (int k = 0; k < KT; ++k) add(v[k]);
     } else {
-      for (int k = 0; k < K; ++k) a += __builtin_nontemporal_load(rows + (size_t)k * cpr4);
+      for (int k = 0; k < K; ++k) add(__builtin_nontemporal_load(rows + (size_t)k * cpr8));
     }
-    dx[c] = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+    u32x4 out;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) out[q] = pack_bf16x2(a[2 * q] * inv, a[2 * q + 1] * inv);
+    dx[c] = out;
   }
 }
 
@@ -206,13 +219,14 @@ hipError_t launch_combine(const void* O, const float* w, const int32_t* f2s, voi
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_rows(const void* dXs, void* dx, int T, int K, int D, hipStream_t st) {
-  const int cpr4 = D / 4;
+hipError_t launch_reduce_rows(const void* dXs, const float* gscale, void* dx, int T, int K, int D,
+                              hipStream_t st) {
+  const int cpr8 = D / 8;
   if (T == 0) return hipSuccess;
-  const dim3 grid(grid_for((size_t)T * cpr4)), block(kPermuteThreads);
+  const dim3 grid(grid_for((size_t)T * cpr8)), block(kPermuteThreads);
 #define MOE_REDUCE(KT)                                                                     \
-  MOE_LAUNCH(kKReduceRows, reduce_rows_kernel<KT>, grid, block, 0, st, (const f32x4*)dXs, \
-             (u32x2*)dx, T, K, cpr4)
+  MOE_LAUNCH(kKReduceRows, reduce_rows_kernel<KT>, grid, block, 0, st, (const u32x4*)dXs, \
+             gscale, (u32x4*)dx, T, K, cpr8)
   switch (K) {
     case 1: MOE_REDUCE(1); break;
     case 2: MOE_REDUCE(2); break;
