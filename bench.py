@@ -68,9 +68,10 @@ def kernel_work(wl: synth.Workload) -> dict:
         # scatter: read the ids (4R) and the histogram table once, write both permutations (8R)
         "route_scatter": ("hbm", 12.0 * R + 4.0 * E * math.ceil(R / route_chunk(R))),
         "tilemap": ("hbm", 8.0 * E),
-        "row_offsets": ("hbm", 8.0 * R),
-        # split flags: the sorted-row indices and their router weights (8R), offsets, flags
-        "bwd_prep": ("hbm", 8.0 * R + 8.0 * E),
+        # backward set-up: split flags from the sorted-row indices and their router
+        # weights (8R), the row offsets (write 4R; the indices again from L2),
+        # offsets, flags, tile starts and chunk map
+        "bwd_setup": ("hbm", 12.0 * R + 24.0 * E),
         # max |dy| for the gradient scale: read dy once
         "dy_amax": ("hbm", 2.0 * T * D + 4.0 * 1024),
         # fp16 copies of x and s dy for the dW GEMMs: read both, write both

@@ -415,19 +415,31 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   hipStream_t st = (hipStream_t)stream;
   clear_stale_error();
 
-  // which experts' dW operands are split hi + lo (read by the recompute
-  // GEMM's epilogue and the dW GEMMs), and the gradient scale from max|dy|
+  // max|dy|, then one set-up launch: which experts' dW operands are split
+  // hi + lo (read by the recompute GEMM's epilogue and the dW GEMMs), the
+  // gradient scale, the row-tile starts, the dW row-chunk map and the
+  // token-row byte offsets of the routed rows (the dW GEMMs gather the rows of
+  // the fp16 x and s dy through them inside their loads)
   MOE_TRY(launch_amax_bf16(dy, TD, w.amax_part, st));
-  const float dim_factor = std::max(1.0f, 3.0f * (float)d.D / (8.0f * (float)d.I));
-  MOE_TRY(launch_bwd_prep(offsets, sorted_to_flat, topk_w, d.E, dim_factor, w.amax_part,
-                          w.dw_split, w.gscale, st));
+  BwdSetupArgs sa{};
+  sa.offsets = offsets;
+  sa.s2f = sorted_to_flat;
+  sa.topk_w = topk_w;
+  sa.amax_part = w.amax_part;
+  sa.split = w.dw_split;
+  sa.gscale = w.gscale;
+  sa.tstart = w.tstart;
+  sa.cstart = w.cstart;
+  sa.pstart = w.pstart;
+  sa.slist = w.slist;
+  sa.rowoff = w.rowoff;
+  sa.dim_factor = std::max(1.0f, 3.0f * (float)d.D / (8.0f * (float)d.I));
+  sa.E = d.E;
+  sa.R = (int)R;
+  sa.K = d.K;
+  sa.row_bytes = (uint32_t)d.D * 2u;
+  MOE_TRY(launch_bwd_setup(sa, st));
   MOE_TRY(launch_f16_operands(x, dy, w.gscale, w.x16, w.dy16, TD, st));
-  if (R > 0) {
-    // token-row byte offsets of the routed rows: the dW GEMMs gather the rows
-    // of the fp16 x and s dy through them inside their loads
-    MOE_TRY(launch_row_offsets(sorted_to_flat, (int)R, d.K, (uint32_t)d.D * 2u, w.rowoff, st));
-    MOE_TRY(launch_tilemap(offsets, d.E, kGemmBM, w.tstart, st));
-  }
   GemmArgs g{};
   g.offsets = offsets;
   g.tstart = w.tstart;
@@ -542,16 +554,13 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   gg.Cf = dw_gate;
   gg.Cf2 = dw_up;
   // the three read only the recompute GEMM's outputs: one launch (no tail
-  // between them); the chunk map first, the chunk partials after
-  MOE_TRY(launch_dw_chunkmap(offsets, d.E, w.cstart, w.pstart, w.slist, st));
+  // between them); then the chunk partials
   MOE_TRY(launch_bwd_fused(gx, R > 0 ? rowgrouped_grid(d, gx.n_tiles) : 0, gd,
                            dw_grid(1, dw_chunks_bound(d), d.D, d.I), gg,
                            dw_grid(2, dw_chunks_bound(d), d.I, d.D), st));
-  const int max_chunked = (int)dw_max_chunked(d);
-  MOE_TRY(launch_dw_reduce(w.dw_part_down, w.slist, w.pstart, w.cstart, dw_down, nullptr, 1, d.D, d.I,
-                           d.E, max_chunked, st));
-  MOE_TRY(launch_dw_reduce(w.dw_part, w.slist, w.pstart, w.cstart, dw_gate, dw_up, 2, d.I, d.D,
-                           d.E, max_chunked, st));
+  MOE_TRY(launch_dw_reduce(DwReduceArgs{w.dw_part_down, dw_down, nullptr, 1, d.D, d.I},
+                           DwReduceArgs{w.dw_part, dw_gate, dw_up, 2, d.I, d.D}, w.slist,
+                           w.pstart, w.cstart, d.E, (int)dw_max_chunked(d), st));
 
   if (R > 0) {
     MOE_TRY(launch_reduce_rows(w.dxs, w.gscale, dx, d.T, d.K, d.D, st));

@@ -72,4 +72,44 @@ __device__ __forceinline__ float sigmoidf_(float z) {
 template <typename T>
 __device__ __forceinline__ T ceil_div(T a, T b) { return (a + b - 1) / b; }
 
+// Block-wide exclusive scan of one int per thread (1024 threads), returns the
+// exclusive prefix; *total receives the sum.  Deterministic (integers).
+__device__ inline int block_exclusive_scan_1024(int v, int* total) {
+  __shared__ int wsum[16];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int i = 0; i < 16; ++i) {
+    if (i < wv) before += wsum[i];
+    all += wsum[i];
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+// tstart[e] = exclusive prefix over the experts of ceil(rows_e / bm), the first
+// row tile of expert e in a row-grouped GEMM's tile list; tstart[E] = the
+// number of row tiles.  One workgroup of 1024 threads.
+__device__ inline void tile_starts_block(const int32_t* __restrict__ offsets, int E, int bm,
+                                         int32_t* __restrict__ tstart) {
+  int carry = 0;
+  for (int e0 = 0; e0 < E; e0 += 1024) {
+    const int e = e0 + threadIdx.x;
+    const int c = e < E ? (offsets[e + 1] - offsets[e] + bm - 1) / bm : 0;
+    int total;
+    const int ex = block_exclusive_scan_1024(c, &total);
+    if (e < E) tstart[e] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) tstart[E] = carry;
+}
+
 }  // namespace moe

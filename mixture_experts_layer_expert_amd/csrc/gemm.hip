@@ -77,6 +77,7 @@
 //     lines one stage ahead, or, for gate/up and down when the launch asks
 //     for the lead policy, only the first tile of each group sharing an
 //     operand slice, two stages ahead.
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -964,15 +965,24 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void b
   else gemm_tile<kDW>(dw_gateup, b - g1 - g2, lds);
 }
 // ---------------------------------------------------------------------------
-// dW row chunks.  One workgroup of 1024 threads: nch_e = max(1, ceil(rows_e /
-// kDwChunkRows)); cstart = exclusive prefix of nch (cstart[E] = total);
-// pstart = exclusive prefix of (nch_e - 1) (the partial slots of chunks 1..);
-// slist = the experts with nch_e > 1 in ascending order, their number in
-// slist[E].  Deterministic (integer scans).
-__global__ __launch_bounds__(1024) void dw_chunkmap_kernel(const int32_t* __restrict__ offsets,
-                                                           int E, int32_t* __restrict__ cstart,
-                                                           int32_t* __restrict__ pstart,
-                                                           int32_t* __restrict__ slist) {
+// Backward set-up.  Everything the backward GEMMs need from the routing and
+// from max|dy| comes from one launch of 1024-thread workgroups with one role
+// each (they share nothing, so any order of the workgroups gives the same
+// result):
+//   workgroups [0, E)   expert e's dW split flag; workgroup 0 also the
+//                       gradient scale;
+//   workgroup E         the tile starts of the row-grouped GEMMs;
+//   workgroup E + 1     the dW row-chunk map;
+//   workgroups E + 2..  the token-row byte offsets of the routed rows.
+
+// dW row chunks: nch_e = max(1, ceil(rows_e / kDwChunkRows)); cstart =
+// exclusive prefix of nch (cstart[E] = total); pstart = exclusive prefix of
+// (nch_e - 1) (the partial slots of chunks 1..); slist = the experts with
+// nch_e > 1 in ascending order, their number in slist[E].  Deterministic
+// (integer scans).
+__device__ void dw_chunkmap_block(const int32_t* __restrict__ offsets, int E,
+                                  int32_t* __restrict__ cstart, int32_t* __restrict__ pstart,
+                                  int32_t* __restrict__ slist) {
   __shared__ int wsum[3][16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int carry[3] = {0, 0, 0};
@@ -1017,37 +1027,36 @@ __global__ __launch_bounds__(1024) void dw_chunkmap_kernel(const int32_t* __rest
   }
 }
 
-// Workgroup e: S = sum of topk_w[s2f[r]]^2 over the expert's n rows r, each
-// thread summing a fixed stride of rows, then a fixed tree, and
+// Expert e: S = sum of topk_w[s2f[r]]^2 over the expert's n rows r, threads
+// 0..255 each summing a fixed stride of rows, then a fixed tree, and
 // split[e] = S * (1 + kDwSplitRows / n) * dim_factor > kDwSplitW2.
 // Workgroup 0 also turns the kAmaxBlocks partial maxima of |dy| into the
 // gradient scale {s, 1/s}: s = 2^(1 - x) for max|dy| = m 2^x, m in [0.5, 1),
 // with x clamped to [-64, 64]; s = 1 when dy is all zero or not finite.
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const int32_t* __restrict__ offsets,
-                                                       const int32_t* __restrict__ s2f,
-                                                       const float* __restrict__ topk_w,
-                                                       float dim_factor,
-                                                       const uint32_t* __restrict__ amax_part,
-                                                       int32_t* __restrict__ split,
-                                                       float* __restrict__ gscale) {
+__device__ void bwd_prep_block(int e, const int32_t* __restrict__ offsets,
+                               const int32_t* __restrict__ s2f, const float* __restrict__ topk_w,
+                               float dim_factor, const uint32_t* __restrict__ amax_part,
+                               int32_t* __restrict__ split, float* __restrict__ gscale) {
   __shared__ float wsum[4];
   __shared__ uint32_t wmax[4];
-  const int e = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int r0 = offsets[e], r1 = offsets[e + 1];
-  float s = 0.0f;
-  for (int r = r0 + tid; r < r1; r += 256) {
-    const float w = topk_w[s2f[r]];
-    s += w * w;
-  }
+  if (tid < 256) {
+    float s = 0.0f;
+    for (int r = r0 + tid; r < r1; r += 256) {
+      const float w = topk_w[s2f[r]];
+      s += w * w;
+    }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if ((tid & 63) == 0) wsum[tid >> 6] = s;
-  if (e == 0) {
-    uint32_t m = 0;
-    for (int b = tid; b < kAmaxBlocks; b += 256) m = max(m, amax_part[b]);
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if ((tid & 63) == 0) wsum[tid >> 6] = s;
+    if (e == 0) {
+      uint32_t m = 0;
+      for (int b = tid; b < kAmaxBlocks; b += 256) m = max(m, amax_part[b]);
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-    if ((tid & 63) == 0) wmax[tid >> 6] = m;
+      for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+      if ((tid & 63) == 0) wmax[tid >> 6] = m;
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -1069,55 +1078,65 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const int32_t* __restrict
   }
 }
 
-hipError_t launch_bwd_prep(const int32_t* offsets, const int32_t* s2f, const float* topk_w, int E,
-                           float dim_factor, const uint32_t* amax_part, int32_t* split,
-                           float* gscale, hipStream_t st) {
-  if (E <= 0) return hipSuccess;
-  MOE_LAUNCH(kKBwdPrep, bwd_prep_kernel, dim3(E), dim3(256), 0, st, offsets, s2f, topk_w,
-             dim_factor, amax_part, split, gscale);
+__global__ __launch_bounds__(1024) void bwd_setup_kernel(BwdSetupArgs a) {
+  const int b = blockIdx.x;
+  if (b < a.E) {
+    bwd_prep_block(b, a.offsets, a.s2f, a.topk_w, a.dim_factor, a.amax_part, a.split, a.gscale);
+  } else if (b == a.E) {
+    tile_starts_block(a.offsets, a.E, kGemmBM, a.tstart);
+  } else if (b == a.E + 1) {
+    dw_chunkmap_block(a.offsets, a.E, a.cstart, a.pstart, a.slist);
+  } else {
+    // rowoff[p] = (s2f[p] / K) * row_bytes
+    const int nb = gridDim.x - (a.E + 2);
+    for (int p = (b - a.E - 2) * 1024 + threadIdx.x; p < a.R; p += nb * 1024)
+      a.rowoff[p] = (uint32_t)(a.s2f[p] / a.K) * a.row_bytes;
+  }
+}
+
+hipError_t launch_bwd_setup(const BwdSetupArgs& a, hipStream_t st) {
+  if (a.E <= 0 || a.R < 0) return hipErrorInvalidValue;
+  const int nro = a.R > 0 ? std::min((a.R + 1023) / 1024, 256) : 0;
+  MOE_LAUNCH(kKBwdSetup, bwd_setup_kernel, dim3(a.E + 2 + nro), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 
-// out_mat[e] += sum_{c >= 1} part[pstart[e] + c - 1][mat]  (c ascending) for
-// the chunked experts e = slist[i]; workgroup (i, stripe) strides over the
-// expert's nmat * M * N elements, 4 per thread.
-__global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict__ part,
+// The chunked experts' weight gradients, both reductions in one launch:
+// workgroup (i, stripe, z) adds, for the chunked expert e = slist[i] and the
+// reduction z (0: dW_down from part_down, 1: dW_gate and dW_up from part),
+// out_mat[e] += sum_{c >= 1} part[pstart[e] + c - 1][mat]  (c ascending),
+// striding over the expert's nmat * M * N elements, 4 per thread.
+__global__ __launch_bounds__(256) void dw_reduce_kernel(DwReduceArgs a0, DwReduceArgs a1,
                                                         const int32_t* __restrict__ slist,
                                                         const int32_t* __restrict__ pstart,
                                                         const int32_t* __restrict__ cstart,
-                                                        float* __restrict__ out0,
-                                                        float* __restrict__ out1, int nmat, int M,
-                                                        int N, int E) {
+                                                        int E) {
   const int i = blockIdx.x;
   if (i >= slist[E]) return;
+  const DwReduceArgs& a = blockIdx.z == 0 ? a0 : a1;
   const int e = slist[i];
   const int nch = cstart[e + 1] - cstart[e];
-  const size_t mn = (size_t)M * N;  // a multiple of 4 (N is a multiple of 64)
+  const int nmat = a.nmat;
+  const size_t mn = (size_t)a.M * a.N;  // a multiple of 4 (N is a multiple of 64)
   const size_t slot0 = (size_t)pstart[e];
   for (size_t q = ((size_t)blockIdx.y * 256 + threadIdx.x) * 4; q < nmat * mn;
        q += (size_t)gridDim.y * 256 * 4) {
     const int mat = q >= mn ? 1 : 0;
     const size_t idx = q - mat * mn;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 1; c < nch; ++c) s += *(const f32x4*)(part + ((slot0 + c - 1) * nmat + mat) * mn + idx);
-    float* o = (mat == 0 ? out0 : out1) + (size_t)e * mn + idx;
+    for (int c = 1; c < nch; ++c)
+      s += *(const f32x4*)(a.part + ((slot0 + c - 1) * nmat + mat) * mn + idx);
+    float* o = (mat == 0 ? a.out0 : a.out1) + (size_t)e * mn + idx;
     *(f32x4*)o = *(const f32x4*)o + s;
   }
 }
 
-hipError_t launch_dw_chunkmap(const int32_t* offsets, int E, int32_t* cstart, int32_t* pstart,
-                              int32_t* slist, hipStream_t st) {
-  MOE_LAUNCH(kKDwChunkMap, dw_chunkmap_kernel, dim3(1), dim3(1024), 0, st, offsets, E, cstart,
-             pstart, slist);
-  return hipGetLastError();
-}
-
-hipError_t launch_dw_reduce(const float* part, const int32_t* slist, const int32_t* pstart,
-                            const int32_t* cstart, float* out0, float* out1, int nmat, int M,
-                            int N, int E, int max_chunked, hipStream_t st) {
+hipError_t launch_dw_reduce(const DwReduceArgs& down, const DwReduceArgs& gateup,
+                            const int32_t* slist, const int32_t* pstart, const int32_t* cstart,
+                            int E, int max_chunked, hipStream_t st) {
   if (max_chunked <= 0) return hipSuccess;
-  MOE_LAUNCH(kKDwReduce, dw_reduce_kernel, dim3(max_chunked, 64), dim3(256), 0, st, part, slist,
-             pstart, cstart, out0, out1, nmat, M, N, E);
+  MOE_LAUNCH(kKDwReduce, dw_reduce_kernel, dim3(max_chunked, 64, 2), dim3(256), 0, st, down,
+             gateup, slist, pstart, cstart, E);
   return hipGetLastError();
 }
 

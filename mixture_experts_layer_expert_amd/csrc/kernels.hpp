@@ -10,8 +10,8 @@ namespace moe {
 enum KernelId : int {
   kKRouteTopk, kKRouteHist, kKRouteScatter, kKTilemap,
   kKGemmGateUpH, kKGemmGateUpGU, kKGemmDown, kKGemmDA, kKCombine, kKReduceRows, kKReducePartials, kKRouterLogits,
-  kKRouterPrep, kKRouterDx, kKRouterDwr, kKRouterDwrSum, kKRowOffsets, kKDwChunkMap,
-  kKDwReduce, kKBwdPrep, kKDyAmax, kKF16Operands, kKGemmBwdFused, kNumKernels
+  kKRouterPrep, kKRouterDx, kKRouterDwr, kKRouterDwrSum, kKDwReduce, kKBwdSetup, kKDyAmax,
+  kKF16Operands, kKGemmBwdFused, kNumKernels
 };
 namespace prof {
 void begin(int kid, hipStream_t st);  // no-ops unless timing is enabled
@@ -47,9 +47,6 @@ hipError_t launch_reduce_rows(const void* dXs, const float* gscale, void* dx, in
                               hipStream_t st);
 hipError_t launch_reduce_partials(const float* part, const int32_t* f2s, float* out, int R,
                                   int np, hipStream_t st);
-// rowoff[p] = (sorted_to_flat[p] / K) * row_bytes: byte offset of routed row p's token row
-hipError_t launch_row_offsets(const int32_t* s2f, int R, int K, uint32_t row_bytes,
-                              uint32_t* rowoff, hipStream_t st);
 // Largest |v| over the n bf16 values of src (n a multiple of 8): kAmaxBlocks
 // workgroup maxima (bit patterns of |v|, ordered like the values) into part.
 constexpr int kAmaxBlocks = 1024;
@@ -140,7 +137,7 @@ struct GemmArgs {
   const int32_t* pstart;
   float* dw_part;
   const int32_t* dw_split;  // [E] 1: the expert's dW operand is split hi + lo
-  // backward gradient scale {s, 1/s} (see launch_bwd_prep), or null (s = 1):
+  // backward gradient scale {s, 1/s} (see launch_bwd_setup), or null (s = 1):
   // kGateUpBwd scales dG and dU by s; kDW multiplies its results by 1/s (kDXs
   // keeps s in its fp16 rows; the dX reduction removes it)
   const float* gscale;
@@ -183,29 +180,54 @@ hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st);
 hipError_t launch_bwd_fused(const GemmArgs& dxs, int g1, const GemmArgs& dw_down, int g2,
                             const GemmArgs& dw_gateup, int g3, hipStream_t st);
 
-// Backward preparation, one workgroup per expert:
+// Backward set-up, one launch (its workgroups each take one role):
 //   split[e] = 1 when S, the sum of the squared router weights
 //     topk_w[s2f[r]]^2 over expert e's n rows r, has
 //     S * (1 + kDwSplitRows / n) * dim_factor > kDwSplitW2, where the caller
 //     passes dim_factor = max(1, 3 D / (8 I)) (fixed summation order, so the
 //     decision repeats bit for bit): its dW operand is split hi + lo;
-//   gscale = {s, 1/s} (workgroup 0), the power of two s with s * max|dy| in
-//     [1, 2) (s = 1 for an all-zero or non-finite dy), from the kAmaxBlocks
-//     maxima that launch_amax_bf16 left in amax_part.  The gradient GEMMs
-//     carry s * dy, s * dG, s * dU in fp16, away from its subnormal range, and
-//     multiply their fp32 results by 1/s (all exact).
-hipError_t launch_bwd_prep(const int32_t* offsets, const int32_t* s2f, const float* topk_w, int E,
-                           float dim_factor, const uint32_t* amax_part, int32_t* split,
-                           float* gscale, hipStream_t st);
+//   gscale = {s, 1/s}, the power of two s with s * max|dy| in [1, 2) (s = 1
+//     for an all-zero or non-finite dy), from the kAmaxBlocks maxima that
+//     launch_amax_bf16 left in amax_part.  The gradient GEMMs carry s * dy,
+//     s * dG, s * dU in fp16, away from its subnormal range, and multiply
+//     their fp32 results by 1/s (all exact);
+//   tstart [E+1]: the row-tile starts of the row-grouped GEMMs (as
+//     launch_tilemap);
+//   the dW row-chunk map: cstart [E+1] (chunk prefix), pstart [E] (first
+//     partial slot of each expert's chunks 1..), slist [E+1] (the chunked
+//     experts ascending, their number in slist[E]);
+//   rowoff [R]: rowoff[p] = (s2f[p] / K) * row_bytes, the byte offset of
+//     routed row p's token row in x16 and dy16.
+struct BwdSetupArgs {
+  const int32_t* offsets;
+  const int32_t* s2f;
+  const float* topk_w;
+  const uint32_t* amax_part;
+  int32_t* split;
+  float* gscale;
+  int32_t* tstart;
+  int32_t* cstart;
+  int32_t* pstart;
+  int32_t* slist;
+  uint32_t* rowoff;
+  float dim_factor;
+  int E, R, K;
+  uint32_t row_bytes;
+};
+hipError_t launch_bwd_setup(const BwdSetupArgs& a, hipStream_t st);
 
-// dW row-chunk map from the expert offsets: cstart [E+1], pstart [E], and the
-// list of chunked experts slist [E] with its length in slist[E].
-hipError_t launch_dw_chunkmap(const int32_t* offsets, int E, int32_t* cstart, int32_t* pstart,
-                              int32_t* slist, hipStream_t st);
 // Chunked experts' weight gradients: out[e] += sum over chunks 1.. of the
-// partial tiles (chunk order); max_chunked bounds the number of chunked experts.
-hipError_t launch_dw_reduce(const float* part, const int32_t* slist, const int32_t* pstart,
-                            const int32_t* cstart, float* out0, float* out1, int nmat, int M,
-                            int N, int E, int max_chunked, hipStream_t st);
+// partial tiles (chunk order), for the nmat (1 or 2) M x N matrices of one
+// reduction; one launch takes dW_down's and dW_gate/up's.  max_chunked bounds
+// the number of chunked experts.
+struct DwReduceArgs {
+  const float* part;
+  float* out0;
+  float* out1;
+  int nmat, M, N;
+};
+hipError_t launch_dw_reduce(const DwReduceArgs& down, const DwReduceArgs& gateup,
+                            const int32_t* slist, const int32_t* pstart, const int32_t* cstart,
+                            int E, int max_chunked, hipStream_t st);
 
 }  // namespace moe

@@ -124,22 +124,6 @@ __global__ __launch_bounds__(kPermuteThreads) void reduce_partials_kernel(
   }
 }
 
-// rowoff[p] = (s2f[p] / K) * row_bytes
-__global__ __launch_bounds__(kPermuteThreads) void row_offsets_kernel(
-    const int32_t* __restrict__ s2f, int R, int K, uint32_t row_bytes, uint32_t* __restrict__ out) {
-  for (int p = blockIdx.x * kPermuteThreads + threadIdx.x; p < R;
-       p += gridDim.x * kPermuteThreads)
-    out[p] = (uint32_t)(s2f[p] / K) * row_bytes;
-}
-
-hipError_t launch_row_offsets(const int32_t* s2f, int R, int K, uint32_t row_bytes,
-                              uint32_t* rowoff, hipStream_t st) {
-  if (R == 0) return hipSuccess;
-  MOE_LAUNCH(kKRowOffsets, row_offsets_kernel, dim3(grid_for((size_t)R)), dim3(kPermuteThreads), 0,
-             st, s2f, R, K, row_bytes, rowoff);
-  return hipGetLastError();
-}
-
 // part[b] = max over workgroup b's grid-stride share of |src| (bf16 values as
 // their 15-bit magnitude patterns, which order like the values; NaN patterns
 // sort above infinity).  Integer max: the result does not depend on order.

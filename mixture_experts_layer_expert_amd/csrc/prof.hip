@@ -39,8 +39,8 @@ const char* const kNames[kNumKernels] = {
     "gemm_gateup_h", "gemm_gateup_gu", "gemm_down",    "gemm_da",
     "combine",      "reduce_rows",
     "reduce_partials", "router_logits", "router_prep",  "router_dx",
-    "router_dwr",   "router_dwr_sum", "row_offsets", "dw_chunkmap", "dw_reduce",
-    "bwd_prep",     "dy_amax",       "f16_operands", "gemm_bwd_fused"};
+    "router_dwr",   "router_dwr_sum", "dw_reduce",   "bwd_setup",    "dy_amax",
+    "f16_operands", "gemm_bwd_fused"};
 
 hipEvent_t take() {
   if (!pool.empty()) {

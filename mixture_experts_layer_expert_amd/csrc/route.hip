@@ -99,29 +99,6 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)e * nblk + blockIdx.x] = cnt[e];
 }
 
-// Block-wide exclusive scan of one int per thread (1024 threads), returns the
-// exclusive prefix; *total receives the sum.  Deterministic (integers).
-__device__ int block_exclusive_scan_1024(int v, int* total) {
-  __shared__ int wsum[16];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
-  if (lane == 63) wsum[wv] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-  for (int i = 0; i < 16; ++i) {
-    if (i < wv) before += wsum[i];
-    all += wsum[i];
-  }
-  __syncthreads();
-  *total = all;
-  return before + incl - v;
-}
-
 // Stable scatter, one wave per block (block b owns flat slots of chunk b and
 // walks them in order, 64 at a time).  The block first derives its own first
 // output row per expert from the per-block histograms: base(e, b) = (rows of
@@ -220,16 +197,7 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
 // Tile map for the row-grouped GEMMs: tstart[e] = sum_{e'<e} ceil(count/BM).
 __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t* __restrict__ offsets, int E,
                                                        int bm, int32_t* __restrict__ tstart) {
-  int carry = 0;
-  for (int e0 = 0; e0 < E; e0 += 1024) {
-    const int e = e0 + threadIdx.x;
-    const int c = e < E ? (offsets[e + 1] - offsets[e] + bm - 1) / bm : 0;
-    int total;
-    const int ex = block_exclusive_scan_1024(c, &total);
-    if (e < E) tstart[e] = carry + ex;
-    carry += total;
-  }
-  if (threadIdx.x == 0) tstart[E] = carry;
+  tile_starts_block(offsets, E, bm, tstart);
 }
 
 // ---------------------------------------------------------------------------
