@@ -472,13 +472,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
     if (wave < NW / 2) atouch = row_off(wave * 64 + lane);
   }
 
-  // Loads of stage kt, pieces [q0, q1) of LOADS_PER_STAGE (A first, then B).
-  auto issue = [&](int kt, int q0, int q1) __attribute__((always_inline)) {
+  // Row-grouped tiles with fewer than BM rows (an expert's last row tile):
+  // the A pieces (64 rows each) from a_end on hold padding rows only and are
+  // not loaded, and this wave's fragment rows from fm_valid on are padding
+  // and take no fragment reads or MFMAs.  Every fragment row that is
+  // multiplied lies in a loaded piece (zeros past the expert's end), so the
+  // accumulators are exactly those of the zero-padded tile.  Wave-uniform.
+  const int a_end = kRowGrouped ? min(QA, ceil_div(rows_valid, KRPI * NW)) : QA;
+  const int fm_valid = kRowGrouped ? max(0, min(FM, ceil_div(rows_valid - wm * WTM, 16))) : FM;
+
+  // Loads of stage kt, pieces [q0, q1) of LOADS_PER_STAGE (A first, then B);
+  // A pieces only below a_end_.
+  auto issue = [&](int kt, int q0, int q1, int a_end_) __attribute__((always_inline)) {
     char* sa = lds + (kt % NS) * STAGE_BYTES;
     char* sb = sa + A_BYTES;
     if constexpr (kRowGrouped) {
       const uint32_t k0b = (uint32_t)kt * BK * 2u;
-      issue_kmajor<BM>(sa, wave, lane, k0b, [&](int i, int) { return aoff[i]; }, rA, 0, q0, q1);
+      issue_kmajor<BM>(sa, wave, lane, k0b, [&](int i, int) { return aoff[i]; }, rA, 0, q0,
+                       min(q1, a_end_));
       if constexpr (kGateUp) {
         // B rows 0..BN/2-1: gate rows, BN/2..BN-1: the matching up rows
         constexpr int QG = kmajor_instrs<BN / 2>();
@@ -608,14 +619,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
       static_assert(QA == LOADS_PER_STAGE - QA, "gathered kDW tiles: equal A and B pieces");
       for (int s = 0; s < RA && s < nk; ++s)
         if (s == 0 || chunk_q(s) != chunk_q(s - 1)) ring_load(chunk_q(s));
-      if (ga) issue(0, QA, LOADS_PER_STAGE);
-      else issue(0, 0, QA);
+      if (ga) issue(0, QA, LOADS_PER_STAGE, QA);
+      else issue(0, 0, QA, QA);
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QA) : "memory");
       __builtin_amdgcn_s_barrier();  // everyone's index chunks are in LDS
       asm volatile("" ::: "memory");
       gather_offsets(0, PF);
-      if (ga) issue(0, 0, QA);
-      else issue(0, QA, LOADS_PER_STAGE);
+      if (ga) issue(0, 0, QA, QA);
+      else issue(0, QA, LOADS_PER_STAGE, QA);
       first_issued = true;
     }
   }
@@ -625,14 +636,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
   }
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < nk && !(s == 0 && first_issued)) issue(s, 0, LOADS_PER_STAGE);
+    if (s < nk && !(s == 0 && first_issued)) issue(s, 0, LOADS_PER_STAGE, a_end);
   // Waves whose rows all lie past a ragged expert's end (row-grouped tiles)
   // skip the fragment reads and MFMAs; wave-uniform.
   const bool wave_rows = !kRowGrouped || wm * WTM < rows_valid;
   // One stage: wait for it, then MFMAs over it with the loads of stage
-  // kt + NS - 1 interleaved (kMore: that stage exists).
-  auto stage = [&](int kt, auto more_tag) __attribute__((always_inline)) {
+  // kt + NS - 1 interleaved (kMore: that stage exists; kPart: a row tile with
+  // padding rows, see a_end and fm_valid).
+  auto stage = [&](int kt, auto more_tag, auto part_tag) __attribute__((always_inline)) {
     constexpr bool kMore = decltype(more_tag)::value;
+    constexpr bool kPart = decltype(part_tag)::value;
+    const int a_lim = kPart ? a_end : QA;
     // stage kt has landed once only the prefetch touch issued after its loads
     // may still be in flight
     if (kt == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -651,7 +665,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
       // all of this wave's rows are padding: it only moves its share of the
       // next stage (and the prefetch)
       if constexpr (kMore) {
-        issue(kt + NS - 1, 0, LOADS_PER_STAGE);
+        issue(kt + NS - 1, 0, LOADS_PER_STAGE, a_lim);
         touch(kt + NS - 1 + PF);
       }
       return;
@@ -663,6 +677,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
       frag_t af[FM], bfr[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
+        if (kPart && i >= fm_valid) continue;
         if constexpr (kRowGrouped) af[i] = read_kmajor<frag_t>(sa, wm * WTM + i * 16, kk, lane);
         else af[i] = read_mnmajor<BM, frag_t>(sa, wm * WTM + i * 16, kk, lane);
       }
@@ -686,17 +701,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
       for (int i = 0; i < FM; ++i) {
         const int slot = (kk / 32) * FM + i;
         const bool loads_here = kMore && slot < LOAD_SLOTS;
-        if (loads_here) issue(kt + NS - 1, slot * LOADS_PER_SLOT, (slot + 1) * LOADS_PER_SLOT);
+        if (loads_here)
+          issue(kt + NS - 1, slot * LOADS_PER_SLOT, (slot + 1) * LOADS_PER_SLOT, a_lim);
+        if (!kPart || i < fm_valid) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          if constexpr (kF16)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < FN; ++j) {
+            if constexpr (kF16)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+          }
         }
         // keep the order: this slot's loads, then its row of MFMAs
-        if (loads_here) __builtin_amdgcn_sched_group_barrier(0x020, LOADS_PER_SLOT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);
+        if constexpr (!kPart) {
+          if (loads_here) __builtin_amdgcn_sched_group_barrier(0x020, LOADS_PER_SLOT, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);
+        }
         // raised issue priority between MFMA rows, normal after the stage's last
         // row, so the other wave on the SIMD reads its fragments meanwhile
         // (measured: -0.6% per step)
@@ -709,9 +729,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
       }
     }
   };
+  // the padding-aware stages where at least one A piece is padding only (with
+  // more valid rows the full tile's schedule measured faster)
   int kt = 0;
-  for (; kt + NS - 1 < nk; ++kt) stage(kt, std::true_type{});
-  for (; kt < nk; ++kt) stage(kt, std::false_type{});
+  bool part = false;
+  if constexpr (kRowGrouped) part = a_end < QA;
+  if (part) {
+    if constexpr (kRowGrouped) {
+      for (; kt + NS - 1 < nk; ++kt) stage(kt, std::true_type{}, std::true_type{});
+      for (; kt < nk; ++kt) stage(kt, std::false_type{}, std::true_type{});
+    }
+  } else {
+    for (; kt + NS - 1 < nk; ++kt) stage(kt, std::true_type{}, std::false_type{});
+    for (; kt < nk; ++kt) stage(kt, std::false_type{}, std::false_type{});
+  }
   // no prefetch DMA may still be writing this workgroup's LDS when it ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -786,7 +817,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
     int src_next = src_of(0);
     float wr_next = p.topk_w[src_next];
     if (FM > 1) src_next = src_of(1);
-    f32x4 dbuf[2][FJ];
+    // dA blocks in flight ahead of their use
+    constexpr int DA_AHEAD = 4;
+    constexpr int NB = DA_AHEAD + 1 < FM ? DA_AHEAD + 1 : FM;
+    f32x4 dbuf[NB][FJ];
     auto load_da = [&](int i, f32x4 (&dv)[FJ]) {
       const int r = wm * WTM + i * 16 + frow;
       const size_t m = (size_t)(m0 + (r < rows_valid ? r : 0));
@@ -796,13 +830,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
         dv[j] = *(const f32x4*)(p.DA + m * (size_t)I + (col < I ? col : 0));
       }
     };
-    load_da(0, dbuf[0]);
+#pragma unroll
+    for (int a = 0; a < DA_AHEAD && a < FM; ++a) load_da(a, dbuf[a % NB]);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      // block i + 1's dA, its router weight, and block i + 2's source row
+      // block i + DA_AHEAD's dA, block i + 1's router weight, and block
+      // i + 2's source row
       const float wr_i = wr_next;
+      if (i + DA_AHEAD < FM) load_da(i + DA_AHEAD, dbuf[(i + DA_AHEAD) % NB]);
       if (i + 1 < FM) {
-        load_da(i + 1, dbuf[(i + 1) & 1]);
         wr_next = p.topk_w[src_next];
         if (i + 2 < FM) src_next = src_of(i + 2);
       }
@@ -817,7 +853,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
         const int cl = j * 16 + cq;  // column within the wave's CW
         const bool ok = row_ok && col0 + cl < I;
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 dav = ok ? dbuf[i & 1][j] : zero;
+        const f32x4 dav = ok ? dbuf[i % NB][j] : zero;
         const f32x4 gv = acc[i][j], uv = acc[i][j + FJ];
         float dg[4], du[4], hw[4];
 #pragma unroll
