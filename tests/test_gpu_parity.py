@@ -105,6 +105,10 @@ SMALL = {
     # wide experts with few tokens (I = 1024: 32-stage reductions over 2I in the
     # dXs GEMM, 16-stage ones in dA), every expert in one m-tile
     "wide_experts": lambda: _custom(T=300, D=256, I=1024, E=4, K=2, score=0, seed=113),
+    # three experts at router weight 1 (K = 1), all with the two-pass dW split:
+    # a hot one of about 5,900 rows (three dW row chunks) beside two of about
+    # 1,500, every element compared
+    "split_chunks_k1": lambda: _custom(T=9000, D=64, I=64, E=3, K=1, score=0, seed=130, hot=0),
     # one token
     "one_token": lambda: _custom(T=1, D=64, I=64, E=8, K=2, score=0, seed=107),
     # the maximum expert count: 1024 experts, most of them empty
