@@ -171,9 +171,10 @@ moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, cons
  * scale s with s * max|dy| in [1, 2), removed from the fp32 results, so the
  * gradients of 2^c dy are exactly 2^c times those of dy whatever c (within
  * fp32 range): no loss scaling is needed.  x enters the weight gradients as
- * fp16 without a scale: |x| above 65504 saturates there, and values below
- * 2^-14 keep less relative precision (activations are far inside that
- * range).  Range of the fp16 gradient operands: with w the router weight,
+ * fp16 without a scale (rounded to nearest): |x| from 65520 on becomes
+ * infinite there, so dW_gate and dW_up of the experts such a token reaches
+ * come out non-finite (never finite and wrong), and values below 2^-14 keep
+ * less relative precision (activations are far inside that range).  Range of the fp16 gradient operands: with w the router weight,
  * h = silu(g) u and dA = dOu W_down, the backward needs |w h| <= 65504 (the
  * dW_down operand) and s |dG|, s |dU| <= 65504 (the dX and dW_gate/up
  * operands); roughly, |g u| below ~6e4 for unit router weights.  Beyond it

@@ -52,8 +52,9 @@ hipError_t launch_reduce_partials(const float* part, const int32_t* f2s, float* 
 constexpr int kAmaxBlocks = 1024;
 hipError_t launch_amax_bf16(const void* src, size_t n, uint32_t* part, hipStream_t st);
 // fp16 operands of the weight-gradient GEMMs from the bf16 inputs (n values
-// each, a multiple of 8): x16 = x, dy16 = s dy with s = gscale[0] (exact in
-// fp16's normal range; rounded toward zero below it).
+// each, a multiple of 8): x16 = x (exact in fp16's normal range, rounded to
+// nearest below it, infinite from 65520 on), dy16 = s dy with s = gscale[0]
+// (exact in fp16's normal range; rounded toward zero below it).
 hipError_t launch_f16_operands(const void* x, const void* dy, const float* gscale, void* x16,
                                void* dy16, size_t n, hipStream_t st);
 

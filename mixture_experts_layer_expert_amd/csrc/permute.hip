@@ -155,7 +155,9 @@ hipError_t launch_amax_bf16(const void* src, size_t n, uint32_t* part, hipStream
   return hipGetLastError();
 }
 
-// x16 = fp16(x), dy16 = fp16(s dy), 8 values per thread and tensor.
+// x16 = fp16(x) (round to nearest: exact in fp16's normal range, infinite
+// above it), dy16 = fp16(s dy) (toward zero; s |dy| < 2), 8 values per thread
+// and tensor.
 __global__ __launch_bounds__(kPermuteThreads) void f16_operands_kernel(
     const u32x4* __restrict__ x, const u32x4* __restrict__ dy, const float* __restrict__ gscale,
     u32x4* __restrict__ x16, u32x4* __restrict__ dy16, size_t n16) {
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(kPermuteThreads) void f16_operands_kernel(
     u32x4 ao, bo;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      ao[q] = bf16x2_to_f16x2(a[q]);
+      ao[q] = pack_f16x2(bf16_lo(a[q]), bf16_hi(a[q]));  // nearest: |x| >= 65520 -> inf
       bo[q] = __builtin_bit_cast(uint32_t,
                                  __builtin_amdgcn_cvt_pkrtz(bf16_lo(b[q]) * sc, bf16_hi(b[q]) * sc));
     }

@@ -219,6 +219,32 @@ def test_fp16_range_overflow_is_not_silent(which):
         G.assert_close(got[name] / sc[name], ref[name] / sc[name], f"{name} (/{sc[name]:g})")
 
 
+def test_fp16_range_x_overflow_is_not_silent():
+    """x enters the weight gradients as fp16: x times 2^17 (with W_gate and
+    W_up times 2^-17, so g, u and every other operand are unchanged) puts
+    |x| above 65504, so dW_gate and dW_up come out non-finite, never finite
+    and wrong; y, d_topk_w and dW_down are unchanged and meet the bar (dX
+    scales by 2^-17, into fp16's subnormal range in the dX GEMM's weight
+    operand, so it is not compared here)."""
+    wl, data = _custom(T=256, D=256, I=128, E=4, K=1, score=1, seed=124)
+    f32, bf = synth.bf16_bits_to_f32, synth.f32_to_bf16_bits
+    c = np.float32(2.0 ** 17)
+    data = dict(data)
+    data["x"] = bf(f32(data["x"]) * c)
+    data["w_gate"] = bf(f32(data["w_gate"]) / c)
+    data["w_up"] = bf(f32(data["w_up"]) / c)
+    assert float(np.abs(f32(data["x"])).max()) > 65520
+    dev = G.DeviceInputs(data)
+    route, y, grads = G.run_gpu(dev, wl.K, wl.score, backward=True)
+    G.check_route_exact(route, data, wl.K, wl.score, wl.E)
+    _, _, _, ref = _refs(wl, data)
+    got = _gpu_outputs(y, grads)
+    for name in ("dw_gate", "dw_up"):
+        assert not np.all(np.isfinite(got[name])), f"{name}: the overflow must show"
+    for name in ("y", "d_topk_w", "dw_down"):
+        G.assert_close(got[name], ref[name], name)
+
+
 # ----------------------------------------------------------------------------- random shapes
 
 def _random_cases(n=10, seed=2024):
