@@ -40,6 +40,20 @@ def _custom(T, D, I, E, K, score, seed, hot=None, dead=(), scale=1.0):
     return wl, data
 
 
+def _exact_counts(ns, D, I, seed):
+    """Top-1 routing (router weight 1) with exactly ns[e] tokens on expert e:
+    each token's logit for its expert is raised far above the others."""
+    T = int(sum(ns))
+    wl = synth.Workload(f"counts_{T}_{D}_{I}", T=T, D=D, I=I, E=len(ns), K=1, score=0, seed=seed)
+    data = synth.generate(wl)
+    owner = np.repeat(np.arange(len(ns)), ns)
+    np.random.Generator(np.random.PCG64(seed)).shuffle(owner)
+    lg = data["logits"].astype(np.float64)
+    lg[np.arange(T), owner] += 20.0
+    data["logits"] = lg.astype(np.float32)
+    return wl, data
+
+
 def _full_compare(wl, data, backward=True):
     dev = G.DeviceInputs(data)
     route, y, grads = G.run_gpu(dev, wl.K, wl.score, backward=backward)
@@ -109,6 +123,11 @@ SMALL = {
     # a hot one of about 5,900 rows (three dW row chunks) beside two of about
     # 1,500, every element compared
     "split_chunks_k1": lambda: _custom(T=9000, D=64, I=64, E=3, K=1, score=0, seed=130, hot=0),
+    # last row tiles at every boundary of the padding-aware stages (64-row A
+    # pieces, 16-row fragments): experts of exactly 1, 63, 64, 65, 192, 193,
+    # 256, 257, 448 and 449 rows
+    "tile_boundaries": lambda: _exact_counts([1, 63, 64, 65, 192, 193, 256, 257, 448, 449],
+                                             D=128, I=64, seed=131),
     # one token
     "one_token": lambda: _custom(T=1, D=64, I=64, E=8, K=2, score=0, seed=107),
     # the maximum expert count: 1024 experts, most of them empty
