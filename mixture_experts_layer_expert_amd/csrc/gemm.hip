@@ -63,7 +63,9 @@
 //     (error about 2^-22 sum |terms|); the others take one pass over hi
 //     (error about 2^-12 times the root-sum-square of the terms);
 //   - ragged expert segments: the tile list is built on the device from the
-//     expert offsets (no host read-back, graph-capturable);
+//     expert offsets (no host read-back, graph-capturable); an expert's last
+//     row tile with a padding-only 64-row piece of A loads only the pieces
+//     that hold rows and multiplies only its 16-row fragments that do;
 //   - weight gradients: one workgroup owns one output tile of one row chunk
 //     (at most kDwChunkRows of its expert's rows); chunk 0 writes the tile,
 //     later chunks write partial tiles that dw_reduce_kernel adds in chunk
