@@ -128,6 +128,13 @@ SMALL = {
     # 256, 257, 448 and 449 rows
     "tile_boundaries": lambda: _exact_counts([1, 63, 64, 65, 192, 193, 256, 257, 448, 449],
                                              D=128, I=64, seed=131),
+    # the skewed-sweep routing (a Zipf(1.2) log-prior over the experts) at a
+    # small size, every element compared: two hot experts above 2048 rows (two
+    # dW row chunks each), 8 experts with the split dW operand and 24 with one
+    # pass, the coldest with 2 rows
+    "zipf_small": lambda: (lambda wl: (wl, synth.generate(wl)))(
+        synth.Workload("zipf_small", T=3000, D=128, I=64, E=32, K=4, score=0, seed=132,
+                       zipf_s=1.2)),
     # one token
     "one_token": lambda: _custom(T=1, D=64, I=64, E=8, K=2, score=0, seed=107),
     # the maximum expert count: 1024 experts, most of them empty
