@@ -56,6 +56,8 @@ def kernel_work(wl: synth.Workload) -> dict:
         "gemm_down": ("mfma", 2 * dir_), "gemm_da": ("mfma", 2 * dir_),
         # dXs (4 D I R), dW_down (2 D I R) and dW_gate + dW_up (4 D I R) in one launch
         "gemm_bwd_fused": ("mfma", 10 * dir_),
+        # chained launches (many m-tiles): gate/up + down, dA + the recompute
+        "gemm_fwd_chain": ("mfma", 6 * dir_), "gemm_da_recompute": ("mfma", 6 * dir_),
         # combine: read O (R*D*2), weights and indices (8R), write y (T*D*2)
         "combine": ("hbm", 2.0 * R * D + 8 * R + 2.0 * T * D),
         # dX reduce: read the fp16 per-row partials (R*D*2), write dX (T*D*2)
@@ -92,7 +94,7 @@ def gemm_min_bytes(wl: synth.Workload) -> dict:
     arithmetic intensity and its attainable roof min(MFMA peak, AI x HBM)."""
     T, D, I, E, R = wl.T, wl.D, wl.I, wl.E, wl.R
     w1 = 2.0 * E * I * D  # one expert weight set, bf16
-    return {
+    b = {
         # x rows, W_gate + W_up, H (fp16)
         "gemm_gateup_h": 2.0 * T * D + 2 * w1 + 2.0 * R * I,
         # x rows, W_gate + W_up, dA (fp32) in; dG | dU, Hw (fp16) and the dRW partials out
@@ -107,6 +109,10 @@ def gemm_min_bytes(wl: synth.Workload) -> dict:
         "gemm_bwd_fused": 4.0 * R * I + 2 * w1 + 2.0 * R * D + 2.0 * T * D + 2.0 * R * I
                           + 2 * w1 + 2.0 * T * D + 4 * w1,
     }
+    # the chained launches move what their two GEMMs move
+    b["gemm_fwd_chain"] = b["gemm_gateup_h"] + b["gemm_down"]
+    b["gemm_da_recompute"] = b["gemm_da"] + b["gemm_gateup_gu"]
+    return b
 
 
 def route_chunk(R: int) -> int:

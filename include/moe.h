@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* Router score functions. */
 #define MOE_SCORE_SOFTMAX_TOPK 0 /* softmax over E, keep top K, renormalise over the K */
@@ -141,7 +141,16 @@ moe_status moe_route_sort_noalloc(const moe_dims *dims, const float *logits, int
  * in fp16's normal range), the unweighted expert outputs as bf16; all GEMMs
  * accumulate in fp32.  Range: |h| = |silu(g) u| <= 65504 (fp16); beyond it
  * the affected outputs come out +-inf or NaN, never finite and wrong (the
- * backward has the same limit on w h). */
+ * backward has the same limit on w h).
+ * With 16 to 64 row tiles of 256 routed rows per XCD (at most
+ * (T K + 255 E) / 256 row tiles over 8 XCDs) the two GEMMs run as one launch:
+ * each XCD takes a range of row tiles, and a down tile starts once the
+ * gate/up tiles of its rows, on the same XCD, have stored H.  The first 4
+ * bytes of the workspace then hold the call's status word once the call has
+ * run on the stream: 0, or nonzero if a wait of that launch gave up after
+ * about a second (bit 0) or the GPU dealt workgroups to its XCDs other than
+ * round-robin (bit 1); the outputs of such a call are not valid.  Concurrent
+ * calls need separate workspaces. */
 moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, const void *w_up,
                    const void *w_down, const float *topk_w, const int32_t *offsets,
                    const int32_t *sorted_to_flat, const int32_t *flat_to_sorted, void *y,
@@ -183,6 +192,10 @@ moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, cons
  * for Hw, dX, dW_gate and dW_up for dG and dU.  The forward output and
  * d_topk_w (fp32 partials) are unaffected.  Experts with no
  * rows get exact zeros (or are left unchanged when accumulating).
+ * dA and the recompute GEMM run as one launch under the same rule as the
+ * forward's gate/up and down GEMMs (a recompute tile reads dA in its
+ * epilogue, once the dA tiles of its rows have stored it), with the same
+ * status word in the first 4 bytes of the workspace.
  *   ws, ws_bytes   device workspace of at least moe_workspace_bytes(dims, MOE_PHASE_BWD) */
 moe_status moe_bwd(const moe_dims *dims, const void *x, const void *w_gate, const void *w_up,
                    const void *w_down, const float *topk_w, const int32_t *offsets,

@@ -39,8 +39,13 @@ moe_status check_dims(const moe_dims* d) {
   // tile counts of the grouped GEMMs must fit in 32-bit grids
   const int64_t R = (int64_t)d->T * d->K;
   const int64_t mt = (R + (int64_t)d->E * (kGemmBM - 1)) / kGemmBM;
-  const int64_t nt = std::max<int64_t>(gateup_tiles(d->I), (d->D + kGemmBN - 1) / kGemmBN);
-  if (mt * nt >= (int64_t(1) << 31) - 8) return MOE_ERR_UNSUPPORTED;
+  // the chained launches (gate/up + down, dA + recompute): kNumXcd ranges of
+  // at most ceil(mt / kNumXcd) + 2 kChainSlack m-tiles, each with both GEMMs'
+  // column tiles (the tile indices of an XCD's range)
+  const int64_t mtx = ((mt + kNumXcd - 1) / kNumXcd + 2 * kChainSlack) * kNumXcd;
+  const int64_t ntd = (d->D + kGemmBN - 1) / kGemmBN, nti = (d->I + kGemmBN - 1) / kGemmBN;
+  if (mtx * (gateup_tiles(d->I) + std::max(ntd, nti)) >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
   // the dW grids as launched (dw_grid below: the (matrix, row chunk) groups
   // rounded up to a multiple of the XCD count)
   const int64_t per_c = ((d->I + kGemmBM - 1) / kGemmBM) * ((d->D + kGemmBN - 1) / kGemmBN);
@@ -48,11 +53,10 @@ moe_status check_dims(const moe_dims* d) {
   if ((groups + kNumXcd - 1) / kNumXcd * kNumXcd * per_c >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
   // the fused backward launch: the dXs grid and both dW grids in one
-  const int64_t ntd = (d->D + kGemmBN - 1) / kGemmBN;
   const int64_t chunks = d->E + (R + kDwChunkRows - 1) / kDwChunkRows;
   const int64_t per_d = ((d->D + kGemmBM - 1) / kGemmBM) * ((d->I + kGemmBN - 1) / kGemmBN);
   const int64_t per_g = ((d->I + kGemmBM - 1) / kGemmBM) * ((d->D + kGemmBN - 1) / kGemmBN);
-  const int64_t fused = (mt * ntd + kNumXcd) + (chunks + kNumXcd) * per_d +
+  const int64_t fused = mtx * ntd + (chunks + kNumXcd) * per_d +
                         (2 * chunks + kNumXcd) * per_g;
   if (fused >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   // the GEMMs address token-major operands with 32-bit buffer offsets
@@ -74,11 +78,17 @@ struct Carve {
 };
 
 struct FwdWs {
+  // chain[0]: status word of the call (nonzero: a chained launch's wait gave
+  // up, or a workgroup ran on an unexpected XCD); chain[1 .. kNumXcd + 1]: the
+  // XCDs' m-tile ranges; then the per-m-tile counters of the chained launch.
+  // Set by the call's first kernel.
+  int32_t* chain;
   int32_t* tstart;
   f16_t* h;   // SwiGLU activations H [R, I], fp16 (the down GEMM's operand)
   bf16_t* o;  // unweighted expert outputs O [R, D]
 };
 struct BwdWs {
+  int32_t* chain;  // as FwdWs::chain
   int32_t* tstart;
   f16_t *dgu, *hw;        // fp16 operands of the gradient GEMMs (rounded values)
   f16_t *dgu_lo, *hw_lo;  // their low parts (value - rounded value), for the dW GEMMs
@@ -125,9 +135,33 @@ size_t route_ws(const moe_dims& d, int32_t** hist, void* base) {
   return c.used;
 }
 
+// m-tiles of the row-grouped GEMMs: at most this many over all experts
+int64_t mt_bound(const moe_dims& d) {
+  return ((int64_t)d.T * d.K + (int64_t)d.E * (kGemmBM - 1)) / kGemmBM;
+}
+int chain_grid(const moe_dims& d, int n_tiles) {
+  return kNumXcd * chain_slots(mt_bound(d), n_tiles);
+}
+// the larger of the two chained launches' grids
+int chain_grid_max(const moe_dims& d) {
+  const int ntd = (d.D + kGemmBN - 1) / kGemmBN, nti = (d.I + kGemmBN - 1) / kGemmBN;
+  return chain_grid(d, (int)gateup_tiles(d.I) + std::max(ntd, nti));
+}
+// the layout of FwdWs::chain / BwdWs::chain: status, XCD ranges, per-m-tile
+// counters, (XCD, slot) claims
+constexpr int kChainXcd = 1, kChainCnt = 2 + kNumXcd;
+size_t chain_claim_off(const moe_dims& d) { return kChainCnt + (size_t)mt_bound(d); }
+size_t chain_ints(const moe_dims& d) { return chain_claim_off(d) + (size_t)chain_grid_max(d); }
+// gate/up + down and dA + recompute as chained launches (else four launches)
+bool use_chain(const moe_dims& d) {
+  return mt_bound(d) >= (int64_t)kNumXcd * kChainMinMtPerXcd &&
+         mt_bound(d) <= (int64_t)kNumXcd * kChainMaxMtPerXcd;
+}
+
 size_t fwd_ws(const moe_dims& d, FwdWs* w, void* base) {
   Carve c{(char*)base};
   const size_t R = (size_t)d.T * d.K;
+  w->chain = c.take<int32_t>(chain_ints(d));
   w->tstart = c.take<int32_t>(d.E + 1);
   w->h = c.take<f16_t>(R * d.I);
   w->o = c.take<bf16_t>(R * d.D);
@@ -137,6 +171,7 @@ size_t fwd_ws(const moe_dims& d, FwdWs* w, void* base) {
 size_t bwd_ws(const moe_dims& d, BwdWs* w, void* base) {
   Carve c{(char*)base};
   const size_t R = (size_t)d.T * d.K;
+  w->chain = c.take<int32_t>(chain_ints(d));
   w->tstart = c.take<int32_t>(d.E + 1);
   w->rowoff = c.take<uint32_t>(std::max<size_t>(1, R));
   w->cstart = c.take<int32_t>(d.E + 1);
@@ -174,10 +209,7 @@ size_t router_bwd_ws(const moe_dims& d, RouterBwdWs* w, void* base) {
 }
 
 int rowgrouped_grid(const moe_dims& d, int n_tiles) {
-  const int64_t R = (int64_t)d.T * d.K;
-  const int64_t mt = (R + (int64_t)d.E * (kGemmBM - 1)) / kGemmBM;
-  const int64_t tiles = mt * n_tiles;
-  return (int)((tiles + kNumXcd - 1) / kNumXcd * kNumXcd);
+  return kNumXcd * rowgrouped_slots(mt_bound(d), n_tiles);
 }
 
 // dW grid: (matrix, row chunk) groups of m-tiles x n-tiles, dealt round-robin
@@ -351,7 +383,9 @@ MOE_EXPORT moe_status moe_fwd(const moe_dims* dims, const void* x, const void* w
   hipStream_t st = (hipStream_t)stream;
   clear_stale_error();
 
-  MOE_TRY(launch_tilemap(offsets, d.E, kGemmBM, w.tstart, st));
+  const bool chain = use_chain(d);
+  MOE_TRY(launch_tilemap(offsets, d.E, kGemmBM, w.tstart, w.chain, (int)chain_ints(d),
+                         chain ? w.chain + kChainXcd : nullptr, st));
 
   GemmArgs g{};
   g.offsets = offsets;
@@ -373,20 +407,32 @@ MOE_EXPORT moe_status moe_fwd(const moe_dims* dims, const void* x, const void* w
   g.lead = gemm_lead(d);
   g.C0 = (bf16_t*)w.h;  // fp16 bits
   g.ldc = d.I;
-  MOE_TRY(launch_gemm(kGateUpH, g, rowgrouped_grid(d, g.n_tiles), st));
-  // down: O[R, D] = H Wd^T
-  g.A = (const bf16_t*)w.h;  // fp16 bits
-  g.lda = d.I;
-  g.B0 = (const bf16_t*)w_down;
-  g.a_gather = nullptr;
-  g.B1 = nullptr;
-  g.ldb = d.I;
-  g.N = d.D;
-  g.K = d.I;
-  g.n_tiles = (d.D + kGemmBN - 1) / kGemmBN;
-  g.C0 = w.o;
-  g.ldc = d.D;
-  MOE_TRY(launch_gemm(kDown, g, rowgrouped_grid(d, g.n_tiles), st));
+  // down: O[R, D] = H Wd^T; chained, a down tile starts reading H once the
+  // gate/up tiles of its m-tile have stored theirs
+  GemmArgs g2 = g;
+  g2.A = (const bf16_t*)w.h;  // fp16 bits
+  g2.lda = d.I;
+  g2.B0 = (const bf16_t*)w_down;
+  g2.a_gather = nullptr;
+  g2.B1 = nullptr;
+  g2.ldb = d.I;
+  g2.N = d.D;
+  g2.K = d.I;
+  g2.n_tiles = (d.D + kGemmBN - 1) / kGemmBN;
+  g2.C0 = w.o;
+  g2.ldc = d.D;
+  if (chain) {
+    g.xcd_mt = g2.xcd_mt = w.chain + kChainXcd;
+    g.xcd_claim = w.chain + chain_claim_off(d);
+    g.mt_signal = w.chain + kChainCnt;
+    g2.mt_wait = w.chain + kChainCnt;
+    g2.mt_need = g.n_tiles;
+    g2.chain_err = w.chain;
+    MOE_TRY(launch_gemm_chain(kGateUpH, g, kDown, g2, chain_grid(d, g.n_tiles + g2.n_tiles), st));
+  } else {
+    MOE_TRY(launch_gemm(kGateUpH, g, rowgrouped_grid(d, g.n_tiles), st));
+    MOE_TRY(launch_gemm(kDown, g2, rowgrouped_grid(d, g2.n_tiles), st));
+  }
 
   MOE_TRY(launch_combine(w.o, topk_w, flat_to_sorted, y, d.T, d.K, d.D, st));
   return MOE_OK;
@@ -433,6 +479,10 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   sa.pstart = w.pstart;
   sa.slist = w.slist;
   sa.rowoff = w.rowoff;
+  const bool chain = use_chain(d);
+  sa.zero = w.chain;
+  sa.nzero = (int)chain_ints(d);
+  sa.xcd_mt = chain ? w.chain + kChainXcd : nullptr;
   sa.dim_factor = std::max(1.0f, 3.0f * (float)d.D / (8.0f * (float)d.I));
   sa.E = d.E;
   sa.R = (int)R;
@@ -458,10 +508,11 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
     g.n_tiles = (d.I + kGemmBN - 1) / kGemmBN;
     g.Cf = w.da;
     g.ldc = d.I;
-    MOE_TRY(launch_gemm(kDA, g, rowgrouped_grid(d, g.n_tiles), st));
+    GemmArgs gda = g;
     // recompute G, U from the routed rows of x (gathered in the loads) and,
     // in the epilogue, the SwiGLU backward from dA: dG | dU, Hw (fp16 hi and,
-    // for split experts, lo) and the router-weight partials
+    // for split experts, lo) and the router-weight partials.  Chained to dA:
+    // a recompute tile's epilogue waits for the dA tiles of its m-tile.
     g = GemmArgs{};
     g.offsets = offsets;
     g.tstart = w.tstart;
@@ -492,7 +543,18 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
     g.np = partials_per_row(d);
     g.dw_split = w.dw_split;
     g.gscale = w.gscale;
-    MOE_TRY(launch_gemm(kGateUpBwd, g, rowgrouped_grid(d, g.n_tiles), st));
+    if (chain) {
+      gda.xcd_mt = g.xcd_mt = w.chain + kChainXcd;
+      gda.xcd_claim = w.chain + chain_claim_off(d);
+      gda.mt_signal = w.chain + kChainCnt;
+      g.mt_wait = w.chain + kChainCnt;
+      g.mt_need = gda.n_tiles;
+      g.chain_err = w.chain;
+      MOE_TRY(launch_gemm_chain(kDA, gda, kGateUpBwd, g, chain_grid(d, gda.n_tiles + g.n_tiles), st));
+    } else {
+      MOE_TRY(launch_gemm(kDA, gda, rowgrouped_grid(d, gda.n_tiles), st));
+      MOE_TRY(launch_gemm(kGateUpBwd, g, rowgrouped_grid(d, g.n_tiles), st));
+    }
   }
   // dXs = dG Wg + dU Wu   (reduction over 2I)
   GemmArgs gx{};

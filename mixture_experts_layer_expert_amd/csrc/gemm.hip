@@ -120,6 +120,12 @@ constexpr int RING_STAGES = RING_ROWS / BK;  // row blocks per chunk
 static_assert(NS * STAGE_BYTES + NW * 256 + RING_BYTES <= 160 * 1024,
               "LDS budget with the index ring");
 
+// Chained launches: polls of a wait before it gives up (each poll is a
+// device-coherent load and an s_sleep: well over a second in all), and the
+// hardware register that names the XCD a wave runs on.
+constexpr int kChainSpinLimit = 1 << 20;
+constexpr int kHwRegXccId = (3 << 11) | 20;  // bits [3:0] of HW_REG_XCC_ID
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -273,13 +279,14 @@ constexpr int kRingOff = NS * STAGE_BYTES + NW * 256;
 template <int MODE>
 constexpr int tile_lds_bytes() { return kRingOff + (MODE == kDW ? RING_BYTES : 0); }
 
-// One workgroup tile of a grouped GEMM: `block` plays the role of the block
-// index in the GEMM's own grid (tile decode and XCD order); lds holds at
-// least tile_lds_bytes<MODE>() bytes, 1024-byte aligned.
+// One workgroup tile of a grouped GEMM: the workgroup runs on XCD `xcd` and is
+// that XCD's `slot`-th workgroup of this GEMM (tile decode and order); lds
+// holds at least tile_lds_bytes<MODE>() bytes, 1024-byte aligned.
 // LEAD: the L2 prefetch policy of the gate/up and down GEMMs (see kLead); the
 // host picks it per launch from the shape (GemmArgs::lead).
 template <int MODE, bool LEAD = false>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, char* const lds) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int xcd, const int slot,
+                                          char* const lds) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
@@ -299,72 +306,85 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
   static_assert(PF <= 1 || RING_STAGES >= PF, "index chunks must span the prefetch distance");
 
   // ---------------------------------------------------------------- tile decode
-  int e, m0, n0, nk, rows_valid, mat = 0, k_count = 0, nk_pass = 0, nt_idx = 0, mt_idx = 0;
+  // The number of experts i < E with f(starts[i]) <= key, less one, for a
+  // nondecreasing f(starts[]): the expert whose range holds key.  All lanes
+  // read 64 starts each round (one round of loads for E <= 256) instead of a
+  // binary search's chain of dependent loads.
+  auto expert_of = [&](const int32_t* starts, auto f, int key) {
+    int cnt = 0;
+    for (int c = 0; c < p.E; c += 256) {
+      int v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = c + 64 * q + lane;
+        v[q] = i < p.E ? starts[i] : 0;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        cnt += (int)__popcll(__ballot(c + 64 * q + lane < p.E && f(v[q]) <= key));
+    }
+    return cnt - 1;
+  };
+  int e, m0, n0, nk, rows_valid, mat = 0, k_count = 0, nk_pass = 0, nt_idx = 0;
   int dw_chunk = 0, dw_slot = -1;  // kDW: row chunk of the expert; partial slot (chunks 1..)
+  int gmt = 0, mt_first = 0;  // row-grouped: global m-tile; first of the expert's m-tiles on this XCD
   size_t kbase = 0;
   {
-    int total;
     if constexpr (kRowGrouped) {
-      total = p.tstart[p.E] * p.n_tiles;
-    } else {
-      total = p.nmat * p.cstart[p.E] * ceil_div(p.M, BM) * ceil_div(p.N, BN);
-    }
-    int tile;
-    if constexpr (kRowGrouped) {
-      // XCD x takes the x-th contiguous range of tiles (an expert's tiles share
-      // an L2); row-grouped tiles all carry about the same work
-      const int per = ceil_div(total, kNumXcd);
-      const int slot = block / kNumXcd;
-      tile = (block % kNumXcd) * per + slot;
-      if (slot >= per || tile >= total) return;
-    } else {
-      // dW: the tm x tn tiles of one (matrix, row chunk) group stay on one XCD
-      // (they share the chunk's operands in L2), and the groups are dealt to
-      // the XCDs round-robin, so the heavy chunks of a hot expert spread
-      const int per_c = ceil_div(p.M, BM) * ceil_div(p.N, BN);
-      const int slot = block / kNumXcd;
-      const int grp = (slot / per_c) * kNumXcd + block % kNumXcd;
-      tile = grp * per_c + slot % per_c;
-      if (tile >= total) return;
-    }
-    if constexpr (kRowGrouped) {
-      int lo = 0, hi = p.E;  // tstart[lo]*nt <= tile < tstart[hi]*nt
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.tstart[mid] * p.n_tiles <= tile) lo = mid;
-        else hi = mid;
+      // XCD x takes a contiguous range of the tile list (expert by expert,
+      // column tile by column tile, m-tile by m-tile), so an expert's tiles
+      // share one L2: with xcd_mt, every column tile of a range of m-tiles
+      // (both GEMMs of a chained launch then put an m-tile on the same XCD),
+      // else an equal share of the tiles.
+      const int nt = p.n_tiles;
+      int lo, hi, key;
+      if (p.xcd_mt) {
+        lo = p.xcd_mt[xcd];
+        hi = p.xcd_mt[xcd + 1];
+        if (slot >= (hi - lo) * nt) return;
+        key = lo * nt + slot;
+      } else {
+        // every XCD the same number of tiles (column tiles of one m-tile may
+        // then sit on two XCDs)
+        lo = 0;
+        hi = p.tstart[p.E];
+        const int per = ceil_div(hi * nt, kNumXcd);
+        key = xcd * per + slot;
+        if (slot >= per || key >= hi * nt) return;
       }
-      e = lo;
-      const int local = tile - p.tstart[e] * p.n_tiles;
-      const int mcnt = p.tstart[e + 1] - p.tstart[e];
+      auto clip = [lo, hi](int v) { return min(max(v, lo), hi); };
+      e = expert_of(p.tstart, [&](int v) { return clip(v) * nt; }, key);
+      const int ts0 = p.tstart[e];
+      const int cs = clip(ts0), mcnt = clip(p.tstart[e + 1]) - cs;
+      const int local = key - cs * nt;
       nt_idx = local / mcnt;
-      const int mt = local - nt_idx * mcnt;
-      mt_idx = mt;
+      const int mloc = local - nt_idx * mcnt;
+      gmt = cs + mloc;
+      mt_first = mloc == 0;
+      const int mt = gmt - ts0;
       m0 = p.offsets[e] + mt * BM;
       rows_valid = min(BM, p.offsets[e + 1] - m0);
       n0 = nt_idx * (kGateUp ? BN / 2 : BN);  // gate/up tiles: BN/2 gate + BN/2 up rows
       nk = p.K / BK;
     } else {
-      // tiles: (matrix, row chunk, m-tile, n-tile); the chunks of expert e are
+      // dW: the tm x tn tiles of one (matrix, row chunk) group stay on one XCD
+      // (they share the chunk's operands in L2), and the groups are dealt to
+      // the XCDs round-robin, so the heavy chunks of a hot expert spread.
+      // Tiles: (matrix, row chunk, m-tile, n-tile); the chunks of expert e are
       // cstart[e] .. cstart[e+1]-1
       const int tm = ceil_div(p.M, BM), tn = ceil_div(p.N, BN);
       const int per_c = tm * tn;
       const int nchunk = p.cstart[p.E];
+      const int tile = ((slot / per_c) * kNumXcd + xcd) * per_c + slot % per_c;
+      if (tile >= p.nmat * nchunk * per_c) return;
       mat = tile / (nchunk * per_c);
       const int rem = tile - mat * nchunk * per_c;
       const int gc = rem / per_c;
       const int r2 = rem - gc * per_c;
-      int lo = 0, hi = p.E;  // cstart[lo] <= gc < cstart[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.cstart[mid] <= gc) lo = mid;
-        else hi = mid;
-      }
-      e = lo;
+      e = expert_of(p.cstart, [](int v) { return v; }, gc);  // cstart[e] <= gc < cstart[e+1]
       dw_chunk = gc - p.cstart[e];
       if (dw_chunk > 0) dw_slot = p.pstart[e] + dw_chunk - 1;
       const int mt = r2 / tn;
-      mt_idx = mt;
       nt_idx = r2 - mt * tn;
       m0 = mt * BM;
       n0 = nt_idx * BN;
@@ -377,6 +397,33 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
       rows_valid = p.M - m0;
     }
   }
+
+  // Chained launches: wait until the first GEMM's tiles of this m-tile have
+  // stored their results.  The producers run on this XCD and share its L2;
+  // each adds to the counter there once its stores are acknowledged.  Every
+  // wave observes the counter itself before it reads the results, so no
+  // barrier is needed; the first read is issued here, at decode, and is
+  // usually already satisfied when the wave gets to the wait.  Device-scope
+  // atomic loads: a plain load could keep hitting a stale line in the CU's
+  // L1.  Bounded.
+  int chain_seen = 0;
+  if constexpr (kRowGrouped) {
+    if (p.mt_wait)
+      chain_seen = __hip_atomic_load(p.mt_wait + gmt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  auto chain_wait = [&]() {
+    int v = __builtin_amdgcn_readfirstlane(chain_seen);
+    int n = 0;
+    while (v < p.mt_need) {
+      if (++n > kChainSpinLimit) {
+        if (lane == 0) __hip_atomic_fetch_or(p.chain_err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+      v = __builtin_amdgcn_readfirstlane(
+          __hip_atomic_load(p.mt_wait + gmt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    }
+  };
 
   // ---------------------------------------------------------------- operand sources
   const uint32_t lda2 = (uint32_t)p.lda * 2u, ldb2 = (uint32_t)p.ldb * 2u;
@@ -585,7 +632,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
   // The tiles that share an operand slice (an A slice: the tiles of one row
   // tile; a B slice: those of one column tile) run side by side on one XCD;
   // with kLead only the first of them touches its lines.
-  const bool touch_lead = !kLead || (wave < NW / 2 ? nt_idx == 0 : mt_idx == 0);
+  const bool touch_lead = !kLead || (wave < NW / 2 ? nt_idx == 0 : mt_first != 0);
   char* const touch_dst = lds + NS * STAGE_BYTES + wave * 256;
   auto touch = [&](int kt) __attribute__((always_inline)) {
     touch_stage(kt, nk, il, touch_lead, touch_dst, wave, lane, rA, rA2, rB, rB2, lda2, ldb2, m0, n0, p.K,
@@ -632,13 +679,26 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
       first_issued = true;
     }
   }
-  if (nk > 0) {
+  static_assert(NS == 2, "the prologue issues one stage");
+  if constexpr (kRowGrouped) {
+    // stage 0's weight pieces first: they need no row index (and, in a
+    // chained down GEMM, nothing from the first GEMM), then the A pieces
+    if (nk > 0) issue(0, QA, LOADS_PER_STAGE, a_end);
+    if constexpr (MODE == kDown) {
+      if (p.mt_wait) chain_wait();  // H rows of this m-tile stored
+    }
+    if (nk > 0) {
 #pragma unroll
-    for (int s = 1; s <= PF; ++s) touch(s);
+      for (int s = 1; s <= PF; ++s) touch(s);
+      issue(0, 0, QA, a_end);
+    }
+  } else {
+    if (nk > 0) {
+#pragma unroll
+      for (int s = 1; s <= PF; ++s) touch(s);
+      if (!first_issued) issue(0, 0, LOADS_PER_STAGE, a_end);
+    }
   }
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk && !(s == 0 && first_issued)) issue(s, 0, LOADS_PER_STAGE, a_end);
   // Waves whose rows all lie past a ragged expert's end (row-grouped tiles)
   // skip the fragment reads and MFMAs; wave-uniform.
   const bool wave_rows = !kRowGrouped || wm * WTM < rows_valid;
@@ -796,6 +856,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
     constexpr int FJ = FN / 2;   // gate fragments of this wave
     using S = Strip<CW, 2>;
     static_assert(NW * 6 * S::BYTES <= NS * STAGE_BYTES, "staging fits the stage buffers");
+    if (p.mt_wait) chain_wait();  // chained after dA: dA rows of this m-tile stored
     char* const stg = lds + wave * 6 * S::BYTES;
     const int I = p.N;
     const int col0 = n0 + wn * CW;  // the wave's first i column
@@ -976,6 +1037,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int block, ch
         });
     }
   }
+  // Chained launches: once every wave's results are stored (acknowledged),
+  // count this tile done for its m-tile.
+  if constexpr (kRowGrouped) {
+    if (p.mt_signal) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_fetch_add(p.mt_signal + gmt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 
@@ -983,7 +1054,32 @@ template <int MODE, bool LEAD = false>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void grouped_gemm_kernel(
     GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) char lds[tile_lds_bytes<MODE>()];
-  gemm_tile<MODE, LEAD>(p, blockIdx.x, lds);
+  gemm_tile<MODE, LEAD>(p, blockIdx.x % kNumXcd, blockIdx.x / kNumXcd, lds);
+}
+
+// Two row-grouped GEMMs in one launch (see launch_gemm_chain).  A workgroup
+// takes its XCD from the hardware, not from its index: workgroup b is the
+// XCD's (b / kNumXcd)-th, since the dispatcher deals consecutive workgroups
+// to the XCDs round-robin (starting at any XCD).  It claims that (XCD, slot)
+// pair, so a dispatch that broke the pattern (two workgroups on one pair, and
+// so a pair left out) is reported; then it runs the slot-th tile of its XCD:
+// the first GEMM's tiles of the XCD's m-tile range, then the second's.
+template <int M1, int M2, bool LEAD>
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void gemm_chain_kernel(
+    GemmArgs a1, GemmArgs a2) {
+  constexpr int kLds = std::max(tile_lds_bytes<M1>(), tile_lds_bytes<M2>());
+  __shared__ __attribute__((aligned(1024))) char lds[kLds];
+  const int xcd = (int)(__builtin_amdgcn_s_getreg(kHwRegXccId) & 0xf) % kNumXcd;
+  const int slot = blockIdx.x / kNumXcd;
+  int claimed = 0;
+  if (threadIdx.x == 0)
+    claimed = __hip_atomic_exchange(a1.xcd_claim + (size_t)xcd * (gridDim.x / kNumXcd) + slot, 1,
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int n1 = (a1.xcd_mt[xcd + 1] - a1.xcd_mt[xcd]) * a1.n_tiles;
+  if (slot < n1) gemm_tile<M1, LEAD && M1 != kDA>(a1, xcd, slot, lds);
+  else gemm_tile<M2, LEAD && M2 != kDA>(a2, xcd, slot - n1, lds);
+  if (threadIdx.x == 0 && claimed != 0)
+    __hip_atomic_fetch_or(a2.chain_err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The three backward GEMMs that read only the recompute GEMM's outputs (dXs,
@@ -998,9 +1094,10 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void b
   __shared__ __attribute__((aligned(1024))) char lds[tile_lds_bytes<kDW>()];
   static_assert(tile_lds_bytes<kDW>() >= tile_lds_bytes<kDXs>(), "one LDS size serves both");
   const int b = blockIdx.x;
-  if (b < g1) gemm_tile<kDXs>(dxs, b, lds);
-  else if (b < g1 + g2) gemm_tile<kDW>(dw_down, b - g1, lds);
-  else gemm_tile<kDW>(dw_gateup, b - g1 - g2, lds);
+  const int xcd = b % kNumXcd;  // g1, g2: multiples of kNumXcd
+  if (b < g1) gemm_tile<kDXs>(dxs, xcd, b / kNumXcd, lds);
+  else if (b < g1 + g2) gemm_tile<kDW>(dw_down, xcd, (b - g1) / kNumXcd, lds);
+  else gemm_tile<kDW>(dw_gateup, xcd, (b - g1 - g2) / kNumXcd, lds);
 }
 // ---------------------------------------------------------------------------
 // Backward set-up.  Everything the backward GEMMs need from the routing and
@@ -1121,7 +1218,12 @@ __global__ __launch_bounds__(1024) void bwd_setup_kernel(BwdSetupArgs a) {
   if (b < a.E) {
     bwd_prep_block(b, a.offsets, a.s2f, a.topk_w, a.dim_factor, a.amax_part, a.split, a.gscale);
   } else if (b == a.E) {
+    for (int i = threadIdx.x; i < a.nzero; i += 1024) a.zero[i] = 0;
     tile_starts_block(a.offsets, a.E, kGemmBM, a.tstart);
+    if (a.xcd_mt) {
+      __syncthreads();
+      chain_bounds_block(a.offsets, a.tstart, a.E, a.xcd_mt);
+    }
   } else if (b == a.E + 1) {
     dw_chunkmap_block(a.offsets, a.E, a.cstart, a.pstart, a.slist);
   } else {
@@ -1216,6 +1318,34 @@ hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st) {
       break;
     default:
       return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_chain(int mode1, const GemmArgs& a1, int mode2, const GemmArgs& a2,
+                             int grid, hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  if (!a1.mt_signal || a2.mt_wait != a1.mt_signal || !a2.chain_err || a2.mt_need != a1.n_tiles ||
+      a1.tstart != a2.tstart || a1.E != a2.E || !a1.xcd_mt || a2.xcd_mt != a1.xcd_mt ||
+      !a1.xcd_claim || a1.mt_wait || a2.mt_signal || grid % kNumXcd)
+    return hipErrorInvalidValue;
+  if (mode1 == kGateUpH && mode2 == kDown) {
+    if (a1.lead != a2.lead) return hipErrorInvalidValue;
+    if (a1.lead)
+      MOE_LAUNCH(kKGemmFwdChain, (gemm_chain_kernel<kGateUpH, kDown, true>), dim3(grid), dim3(NTH),
+                 0, st, a1, a2);
+    else
+      MOE_LAUNCH(kKGemmFwdChain, (gemm_chain_kernel<kGateUpH, kDown, false>), dim3(grid), dim3(NTH),
+                 0, st, a1, a2);
+  } else if (mode1 == kDA && mode2 == kGateUpBwd) {
+    if (a2.lead)
+      MOE_LAUNCH(kKGemmBwdChain, (gemm_chain_kernel<kDA, kGateUpBwd, true>), dim3(grid), dim3(NTH),
+                 0, st, a1, a2);
+    else
+      MOE_LAUNCH(kKGemmBwdChain, (gemm_chain_kernel<kDA, kGateUpBwd, false>), dim3(grid),
+                 dim3(NTH), 0, st, a1, a2);
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -11,7 +11,7 @@ enum KernelId : int {
   kKRouteTopk, kKRouteHist, kKRouteScatter, kKTilemap,
   kKGemmGateUpH, kKGemmGateUpGU, kKGemmDown, kKGemmDA, kKCombine, kKReduceRows, kKReducePartials, kKRouterLogits,
   kKRouterPrep, kKRouterDx, kKRouterDwr, kKRouterDwrSum, kKDwReduce, kKBwdSetup, kKDyAmax,
-  kKF16Operands, kKGemmBwdFused, kNumKernels
+  kKF16Operands, kKGemmBwdFused, kKGemmFwdChain, kKGemmBwdChain, kNumKernels
 };
 namespace prof {
 void begin(int kid, hipStream_t st);  // no-ops unless timing is enabled
@@ -35,8 +35,11 @@ int route_chunk(int R);
 hipError_t launch_route_sort(const moe_dims& d, const float* logits, int32_t* idx, float* w,
                              int32_t* counts, int32_t* offsets, int32_t* s2f, int32_t* f2s,
                              int32_t* hist, hipStream_t st);
-hipError_t launch_tilemap(const int32_t* offsets, int E, int bm, int32_t* tstart,
-                          hipStream_t st);
+// tstart [E+1] (the row-grouped GEMMs' m-tile starts, bm = kGemmBM); also
+// zero[0 .. nzero) = 0 and, if xcd_mt is not null, the chained launches' XCD
+// ranges xcd_mt[0 .. kNumXcd] (chain_bounds_block)
+hipError_t launch_tilemap(const int32_t* offsets, int E, int bm, int32_t* tstart, int32_t* zero,
+                          int nzero, int32_t* xcd_mt, hipStream_t st);
 
 // ---- permutes (permute.hip)
 hipError_t launch_combine(const void* O, const float* w, const int32_t* f2s, void* y, int T,
@@ -172,10 +175,92 @@ struct GemmArgs {
   const int32_t* s2f;
   float* part;  // kGateUpBwd: router-weight-gradient partials [R, np]
   int np;
+  // Two row-grouped GEMMs in one launch, the second reading the first's
+  // results (launch_gemm_chain): the first GEMM's tile of m-tile g adds 1 to
+  // mt_signal[g] once its results are stored; a tile of the second waits until
+  // mt_wait[g] >= mt_need before it reads them.  Null when not chained.
+  int32_t* mt_signal;
+  const int32_t* mt_wait;
+  int mt_need;
+  int32_t* chain_err;  // nonzero after a wait gave up (see launch_gemm_chain)
+  // Row-grouped modes: null, or the XCDs' m-tile ranges [xcd_mt[x], xcd_mt[x+1])
+  // (chain_bounds_block): XCD x then takes every column tile of its m-tiles.
+  // With null, XCD x takes the x-th of kNumXcd equal ranges of the tile list.
+  const int32_t* xcd_mt;
+  int32_t* xcd_claim;  // chained launches: one flag per (XCD, slot), zero at launch
 };
 
 // One grouped GEMM of the row-grouped modes (kGateUpH, kGateUpBwd, kDown, kDA).
+// Grid: kNumXcd * rowgrouped_slots(m-tile bound, n_tiles), with a.xcd_mt
+// null; kNumXcd * chain_slots(m-tile bound, n_tiles) with the XCD ranges.
 hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st);
+// Workgroups per XCD of a row-grouped GEMM: the XCD's share of at most
+// mt_bound m-tiles of n_tiles tiles each.
+inline int rowgrouped_slots(int64_t mt_bound, int n_tiles) {
+  return (int)((mt_bound * n_tiles + kNumXcd - 1) / kNumXcd);
+}
+// The chained launches' XCD ranges put an m-tile boundary near every
+// kNumXcd-th of the routed rows, at most kChainSlack m-tiles away from an equal
+// split of the m-tiles.  The row-grouped GEMMs are chained when the m-tile
+// bound per XCD lies in [kChainMinMtPerXcd, kChainMaxMtPerXcd]: with fewer, one
+// m-tile more or less unbalances the XCDs; with more, the last tile wave that
+// chaining fills is a small share of the launch, while the per-tile waits and
+// signals and the coarser XCD split grow with the tile count (measured at the
+// Qwen shape with Zipf-skewed routing over 16384 tokens: +1.1% per step).
+constexpr int kChainSlack = 3;
+constexpr int kChainMinMtPerXcd = 16;
+constexpr int kChainMaxMtPerXcd = 64;
+inline int chain_slots(int64_t mt_bound, int n_tiles) {
+  return (int)(((mt_bound + kNumXcd - 1) / kNumXcd + 2 * kChainSlack) * n_tiles);
+}
+// xcd_mt[0 .. kNumXcd] (see GemmArgs::xcd_mt) from the expert row offsets and
+// the m-tile starts (threads 0 .. kNumXcd of the calling block; tstart must be
+// visible to them): xcd_mt[x] is the m-tile boundary nearest to row
+// x R / kNumXcd, clamped to within kChainSlack of x M / kNumXcd (M = tstart[E]),
+// so the ranges are nondecreasing, hold about equal rows, and none holds more
+// than ceil(M / kNumXcd) + 2 kChainSlack m-tiles.
+__device__ inline void chain_bounds_block(const int32_t* __restrict__ offsets,
+                                          const int32_t* __restrict__ tstart, int E,
+                                          int32_t* __restrict__ xcd_mt) {
+  const int x = threadIdx.x;
+  if (x > kNumXcd) return;
+  const int R = offsets[E], M = tstart[E];
+  int v = x == 0 ? 0 : M;
+  if (x > 0 && x < kNumXcd) {
+    const int64_t t = (int64_t)x * R / kNumXcd;
+    int lo = 0, hi = E;  // offsets[lo] <= t < offsets[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (offsets[mid] <= t) lo = mid;
+      else hi = mid;
+    }
+    const int mc = tstart[lo + 1] - tstart[lo];
+    const int j = (int)((t - offsets[lo] + kGemmBM / 2) / kGemmBM);
+    v = tstart[lo] + min(j, mc);
+    const int base = (int)((int64_t)x * M / kNumXcd);
+    v = min(max(v, base - kChainSlack), base + kChainSlack);
+    v = min(max(v, 0), M);
+  }
+  xcd_mt[x] = v;
+}
+// Two row-grouped GEMMs as one launch, the second reading the first's results
+// (gate/up then down: a1 kGateUpH, a2 kDown; dA then the recompute: a1 kDA,
+// a2 kGateUpBwd).  Each XCD takes the same range of m-tiles in both (xcd_mt,
+// the same array in a1 and a2) and runs the first GEMM's tiles of its range
+// before the second's; a tile of the second waits for the a1.n_tiles tiles of
+// its m-tile (a2.mt_wait, filled through a1.mt_signal, which must hold zeros
+// for every m-tile at launch), before its first read of A (down) or of dA (the
+// recompute's epilogue).  Grid: kNumXcd * chain_slots(bound, a1.n_tiles +
+// a2.n_tiles).  A workgroup takes the tiles of the XCD it runs on (read from
+// the hardware), as that XCD's (b / kNumXcd)-th workgroup: the dispatcher deals
+// consecutive workgroups to the XCDs round-robin, and in index order within an
+// XCD, so a wait is always for a tile of the same XCD (same L2) that an
+// earlier workgroup of that XCD holds.  a1.xcd_claim (grid ints, zero at
+// launch) records the (XCD, slot) pairs taken: a pair taken twice sets bit 2
+// of *chain_err, a wait that exceeds its spin limit bit 1 (the results are
+// then not valid); every wait is bounded, so the launch always completes.
+hipError_t launch_gemm_chain(int mode1, const GemmArgs& a1, int mode2, const GemmArgs& a2,
+                             int grid, hipStream_t st);
 // dXs (grid g1), dW_down (grid g2) and dW_gate/up (grid g3) as one launch; the
 // grids are those launch_gemm would take (g1, g2 multiples of kNumXcd).
 hipError_t launch_bwd_fused(const GemmArgs& dxs, int g1, const GemmArgs& dw_down, int g2,
@@ -211,6 +296,9 @@ struct BwdSetupArgs {
   int32_t* pstart;
   int32_t* slist;
   uint32_t* rowoff;
+  int32_t* zero;  // zero[0 .. nzero) = 0: the chained launch's status word and counters
+  int nzero;
+  int32_t* xcd_mt;  // null, or the chained launch's XCD ranges (chain_bounds_block)
   float dim_factor;
   int E, R, K;
   uint32_t row_bytes;

@@ -40,7 +40,7 @@ const char* const kNames[kNumKernels] = {
     "combine",      "reduce_rows",
     "reduce_partials", "router_logits", "router_prep",  "router_dx",
     "router_dwr",   "router_dwr_sum", "dw_reduce",   "bwd_setup",    "dy_amax",
-    "f16_operands", "gemm_bwd_fused"};
+    "f16_operands", "gemm_bwd_fused", "gemm_fwd_chain", "gemm_da_recompute"};
 
 hipEvent_t take() {
   if (!pool.empty()) {

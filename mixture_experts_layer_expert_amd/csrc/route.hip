@@ -194,10 +194,18 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Tile map for the row-grouped GEMMs: tstart[e] = sum_{e'<e} ceil(count/BM).
+// Tile map for the row-grouped GEMMs: tstart[e] = sum_{e'<e} ceil(count/BM);
+// zero[0 .. nzero) = 0 (the chained launch's status word and counters).
 __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t* __restrict__ offsets, int E,
-                                                       int bm, int32_t* __restrict__ tstart) {
+                                                       int bm, int32_t* __restrict__ tstart,
+                                                       int32_t* __restrict__ zero, int nzero,
+                                                       int32_t* __restrict__ xcd_mt) {
+  for (int i = threadIdx.x; i < nzero; i += 1024) zero[i] = 0;
   tile_starts_block(offsets, E, bm, tstart);
+  if (xcd_mt) {
+    __syncthreads();
+    chain_bounds_block(offsets, tstart, E, xcd_mt);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -249,9 +257,11 @@ hipError_t launch_route_sort(const moe_dims& d, const float* logits, int32_t* id
   return hipGetLastError();
 }
 
-hipError_t launch_tilemap(const int32_t* offsets, int E, int bm, int32_t* tstart,
-                          hipStream_t st) {
-  MOE_LAUNCH(kKTilemap, tilemap_kernel, dim3(1), dim3(1024), 0, st, offsets, E, bm, tstart);
+hipError_t launch_tilemap(const int32_t* offsets, int E, int bm, int32_t* tstart, int32_t* zero,
+                          int nzero, int32_t* xcd_mt, hipStream_t st) {
+  if (bm != kGemmBM) return hipErrorInvalidValue;
+  MOE_LAUNCH(kKTilemap, tilemap_kernel, dim3(1), dim3(1024), 0, st, offsets, E, bm, tstart, zero,
+             nzero, xcd_mt);
   return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ def test_no_torch_dependency(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
     for code in range(6):
         assert moe.status_string(code)
 

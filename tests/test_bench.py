@@ -26,11 +26,15 @@ def test_work_table_names_library_kernels():
 
 def test_gemm_flops_add_up_to_the_counted_step():
     """The seven grouped GEMMs' algorithmic FLOPs are the step's counted 18 D I
-    per routed row plus the recompute's 4 D I."""
+    per routed row plus the recompute's 4 D I, whether gate/up + down and dA +
+    the recompute run as four launches or as two chained ones."""
     wl = synth.QWEN3_30B_A3B
     work = bench.kernel_work(wl)
-    total = sum(a for n, (b, a) in work.items() if b == "mfma")
-    assert total == (18 + 4) * wl.D * wl.I * wl.R
+    separate = ["gemm_gateup_h", "gemm_down", "gemm_da", "gemm_gateup_gu", "gemm_bwd_fused"]
+    chained = ["gemm_fwd_chain", "gemm_da_recompute", "gemm_bwd_fused"]
+    assert sorted(n for n, (b, _) in work.items() if b == "mfma") == sorted(set(separate + chained))
+    for names in (separate, chained):
+        assert sum(work[n][1] for n in names) == (18 + 4) * wl.D * wl.I * wl.R
     assert wl.flops_fwd() + wl.flops_bwd() == 18 * wl.D * wl.I * wl.R
 
 

@@ -135,6 +135,14 @@ SMALL = {
     "zipf_small": lambda: (lambda wl: (wl, synth.generate(wl)))(
         synth.Workload("zipf_small", T=3000, D=128, I=64, E=32, K=4, score=0, seed=132,
                        zipf_s=1.2)),
+    # enough m-tiles (16 to 64 per XCD) for the chained launches (gate/up with
+    # down, dA with the recompute; waits on per-m-tile counters): uniform
+    # routing over 16 experts of about 2048 rows, and the skewed-sweep routing
+    # over 64 experts (hot experts of many m-tiles next to experts of a few rows)
+    "chained_uniform": lambda: _custom(T=4096, D=128, I=128, E=16, K=8, score=0, seed=133),
+    "chained_zipf": lambda: (lambda wl: (wl, synth.generate(wl)))(
+        synth.Workload("chained_zipf", T=3000, D=128, I=64, E=64, K=8, score=0, seed=134,
+                       zipf_s=1.2)),
     # one token
     "one_token": lambda: _custom(T=1, D=64, I=64, E=8, K=2, score=0, seed=107),
     # the maximum expert count: 1024 experts, most of them empty
@@ -562,3 +570,46 @@ def test_empty_batch_layer():
     torch.cuda.synchronize()
     for k in ("dw_gate", "dw_up", "dw_down"):
         assert bool((out2[k] == 1.5).all()), f"{k} changed by an empty accumulating backward"
+
+
+# ----------------------------------------------------------------------------- chained launches
+
+def _m_tile_bound(wl):
+    return (wl.T * wl.K + wl.E * 255) // 256
+
+
+@pytest.mark.parametrize("name", ["chained_uniform", "qwen3_30b_a3b", "llama4_scout"])
+def test_chained_launches_status(name):
+    """The chained GEMM launches run where the m-tile count calls for them
+    (16 to 64 m-tiles per XCD) and not elsewhere, and leave the call's status
+    word (the first 4 bytes of the forward and backward workspaces) at 0: no
+    wait gave up and every workgroup ran on the XCD the partition assumes."""
+    import mixture_experts_layer_expert_amd as moe
+    torch = G.torch_mod()
+    if name == "chained_uniform":
+        wl, data = SMALL[name]()
+    else:
+        wl = {"qwen3_30b_a3b": synth.QWEN3_30B_A3B, "llama4_scout": synth.LLAMA4_SCOUT}[name]
+        data = synth.generate(wl)
+    chained = 128 <= _m_tile_bound(wl) <= 512
+    dev = G.DeviceInputs(data)
+    route = moe.moe_route_sort(dev.logits, wl.K, wl.score)
+    d = moe.binding.dims(wl.T, wl.D, wl.I, wl.E, wl.K, wl.score)
+    wf = torch.full((moe.moe_workspace_bytes(d, moe.MOE_PHASE_FWD),), 0x5A, dtype=torch.uint8,
+                    device="cuda")
+    wb = torch.full((moe.moe_workspace_bytes(d, moe.MOE_PHASE_BWD),), 0x5A, dtype=torch.uint8,
+                    device="cuda")
+    moe.moe_prof_enable(True)
+    try:
+        moe.moe_fwd(dev.x, dev.w_gate, dev.w_up, dev.w_down, route, wl.K, wl.score, ws=wf)
+        moe.moe_bwd(dev.x, dev.w_gate, dev.w_up, dev.w_down, route, dev.dy, wl.K, wl.score, ws=wb)
+        torch.cuda.synchronize()
+        ran = moe.moe_prof_read()
+    finally:
+        moe.moe_prof_enable(False)
+    assert int(wf[:4].view(torch.int32).item()) == 0
+    assert int(wb[:4].view(torch.int32).item()) == 0
+    for k in ("gemm_fwd_chain", "gemm_da_recompute"):
+        assert (k in ran) == chained, (k, sorted(ran))
+    for k in ("gemm_gateup_h", "gemm_down", "gemm_da", "gemm_gateup_gu"):
+        assert (k in ran) != chained, (k, sorted(ran))
