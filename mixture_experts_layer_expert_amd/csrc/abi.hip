@@ -44,7 +44,9 @@ moe_status check_dims(const moe_dims* d) {
   // column tiles (the tile indices of an XCD's range)
   const int64_t mtx = ((mt + kNumXcd - 1) / kNumXcd + 2 * kChainSlack) * kNumXcd;
   const int64_t ntd = (d->D + kGemmBN - 1) / kGemmBN, nti = (d->I + kGemmBN - 1) / kGemmBN;
-  if (mtx * (gateup_tiles(d->I) + std::max(ntd, nti)) >= (int64_t(1) << 31))
+  if (mtx * (gateup_tiles(d->I) + std::max(ntd, nti)) >= (int64_t(1) << 31) ||
+      kNumXcd * (2 * ((mt * (gateup_tiles(d->I) + ntd) + kNumXcd - 1) / kNumXcd) + 2) >=
+          (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
   // the dW grids as launched (dw_grid below: the (matrix, row chunk) groups
   // rounded up to a multiple of the XCD count)
@@ -56,7 +58,7 @@ moe_status check_dims(const moe_dims* d) {
   const int64_t chunks = d->E + (R + kDwChunkRows - 1) / kDwChunkRows;
   const int64_t per_d = ((d->D + kGemmBM - 1) / kGemmBM) * ((d->I + kGemmBN - 1) / kGemmBN);
   const int64_t per_g = ((d->I + kGemmBM - 1) / kGemmBM) * ((d->D + kGemmBN - 1) / kGemmBN);
-  const int64_t fused = mtx * ntd + (chunks + kNumXcd) * per_d +
+  const int64_t fused = kNumXcd * (2 * ((mt * ntd + kNumXcd - 1) / kNumXcd) + 2) + (chunks + kNumXcd) * per_d +
                         (2 * chunks + kNumXcd) * per_g;
   if (fused >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   // the GEMMs address token-major operands with 32-bit buffer offsets
@@ -162,7 +164,7 @@ size_t fwd_ws(const moe_dims& d, FwdWs* w, void* base) {
   Carve c{(char*)base};
   const size_t R = (size_t)d.T * d.K;
   w->chain = c.take<int32_t>(chain_ints(d));
-  w->tstart = c.take<int32_t>(d.E + 1);
+  w->tstart = c.take<int32_t>(2 * (size_t)d.E + 2);
   w->h = c.take<f16_t>(R * d.I);
   w->o = c.take<bf16_t>(R * d.D);
   return c.used;
@@ -172,7 +174,7 @@ size_t bwd_ws(const moe_dims& d, BwdWs* w, void* base) {
   Carve c{(char*)base};
   const size_t R = (size_t)d.T * d.K;
   w->chain = c.take<int32_t>(chain_ints(d));
-  w->tstart = c.take<int32_t>(d.E + 1);
+  w->tstart = c.take<int32_t>(2 * (size_t)d.E + 2);
   w->rowoff = c.take<uint32_t>(std::max<size_t>(1, R));
   w->cstart = c.take<int32_t>(d.E + 1);
   w->pstart = c.take<int32_t>(d.E);
@@ -573,6 +575,7 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   gx.ldc = d.D;
   gx.s2f = sorted_to_flat;
   gx.gscale = w.gscale;
+  gx.even_split = 1;
   // dW_down[e] = dOu_e^T Hw_e   ([D, I], reduction over the expert's rows, in
   // row chunks of at most kDwChunkRows); dOu from the fp16 s dy, the result
   // times 1/s

@@ -95,21 +95,46 @@ __device__ inline int block_exclusive_scan_1024(int v, int* total) {
   return before + incl - v;
 }
 
-// tstart[e] = exclusive prefix over the experts of ceil(rows_e / bm), the first
-// row tile of expert e in a row-grouped GEMM's tile list; tstart[E] = the
-// number of row tiles.  One workgroup of 1024 threads.
+// Cost of one row tile of a row-grouped GEMM with `rows` valid rows, in
+// eighths of a full tile, as the tiles run: with more than 192 rows the full
+// tile's schedule (8); otherwise the weights' half of each stage plus one
+// eighth per 64-row A piece that holds rows (5, 6 or 7).  Experts of 513-541
+// rows, for instance, end in a tile of at most 29 rows that costs 5.
+__device__ __forceinline__ int tile_cost8(int rows) {
+  return rows > 192 ? 8 : 4 + (rows + 63) / 64;
+}
+
+// The tile map of the row-grouped GEMMs, [2 (E + 1)] ints:
+//   tstart[e] = exclusive prefix over the experts of ceil(rows_e / bm), the
+//     first row tile of expert e in a GEMM's tile list (tstart[E] = the
+//     number of row tiles);
+//   tstart[E + 1 + e] = exclusive prefix of the experts' row-tile costs
+//     (tile_cost8 summed over each expert's row tiles): the cost of a column
+//     tile's pass over the experts before e.
+// One workgroup of 1024 threads.
 __device__ inline void tile_starts_block(const int32_t* __restrict__ offsets, int E, int bm,
                                          int32_t* __restrict__ tstart) {
-  int carry = 0;
+  int carry = 0, ccarry = 0;
+  int32_t* const cpre = tstart + E + 1;
   for (int e0 = 0; e0 < E; e0 += 1024) {
     const int e = e0 + threadIdx.x;
-    const int c = e < E ? (offsets[e + 1] - offsets[e] + bm - 1) / bm : 0;
-    int total;
+    const int rows = e < E ? offsets[e + 1] - offsets[e] : 0;
+    const int c = (rows + bm - 1) / bm;
+    const int cost = c > 0 ? 8 * (c - 1) + tile_cost8(rows - bm * (c - 1)) : 0;
+    int total, ctotal;
     const int ex = block_exclusive_scan_1024(c, &total);
-    if (e < E) tstart[e] = carry + ex;
+    const int cex = block_exclusive_scan_1024(cost, &ctotal);
+    if (e < E) {
+      tstart[e] = carry + ex;
+      cpre[e] = ccarry + cex;
+    }
     carry += total;
+    ccarry += ctotal;
   }
-  if (threadIdx.x == 0) tstart[E] = carry;
+  if (threadIdx.x == 0) {
+    tstart[E] = carry;
+    cpre[E] = ccarry;
+  }
 }
 
 }  // namespace moe

@@ -344,13 +344,38 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int xcd, cons
         if (slot >= (hi - lo) * nt) return;
         key = lo * nt + slot;
       } else {
-        // every XCD the same number of tiles (column tiles of one m-tile may
-        // then sit on two XCDs)
+        // every XCD about the same tile cost (tile_cost8), or with even_split
+        // the same tile count (column tiles of one m-tile may then sit on two
+        // XCDs): XCD x starts at the tile where the list's cumulative cost
+        // reaches x / kNumXcd of the total
         lo = 0;
         hi = p.tstart[p.E];
-        const int per = ceil_div(hi * nt, kNumXcd);
-        key = xcd * per + slot;
-        if (slot >= per || key >= hi * nt) return;
+        const int32_t* const cpre = p.tstart + p.E + 1;
+        const int64_t ctot = cpre[p.E];
+        auto first_tile = [&](int x) -> int {
+          if (x == 0) return 0;
+          if (x == kNumXcd) return hi * nt;
+          // the cost target in passes over the expert list, its expert, and
+          // the tile within the expert's (column tile, m-tile) order
+          const int64_t t = (int64_t)x * ctot / kNumXcd;
+          const int ex = expert_of(cpre, [](int v) { return v; }, (int)t);
+          const int c0 = cpre[ex], ce = cpre[ex + 1] - c0;
+          const int t0 = p.tstart[ex], mc = p.tstart[ex + 1] - t0;
+          if (ce == 0) return t0 * nt;
+          const int64_t rem = (t - c0) * nt;  // eighths of a tile into the expert
+          const int q = (int)(rem / ce);      // whole column tiles
+          const int r = min((int)((rem - (int64_t)q * ce + 4) / 8), mc - 1);
+          return t0 * nt + q * mc + r;
+        };
+        if (p.even_split) {
+          const int per = ceil_div(hi * nt, kNumXcd);
+          key = xcd * per + slot;
+          if (slot >= per || key >= hi * nt) return;
+        } else {
+          const int k0 = first_tile(xcd), k1 = first_tile(xcd + 1);
+          key = k0 + slot;
+          if (key >= k1) return;
+        }
       }
       auto clip = [lo, hi](int v) { return min(max(v, lo), hi); };
       e = expert_of(p.tstart, [&](int v) { return clip(v) * nt; }, key);
@@ -1222,7 +1247,7 @@ __global__ __launch_bounds__(1024) void bwd_setup_kernel(BwdSetupArgs a) {
     tile_starts_block(a.offsets, a.E, kGemmBM, a.tstart);
     if (a.xcd_mt) {
       __syncthreads();
-      chain_bounds_block(a.offsets, a.tstart, a.E, a.xcd_mt);
+      chain_bounds_block(a.tstart, a.E, a.xcd_mt);
     }
   } else if (b == a.E + 1) {
     dw_chunkmap_block(a.offsets, a.E, a.cstart, a.pstart, a.slist);

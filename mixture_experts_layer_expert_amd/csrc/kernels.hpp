@@ -149,7 +149,7 @@ struct GemmArgs {
   const bf16_t* B0;  // weights (row-grouped) or token-major activations (kDW)
   const bf16_t* B1;  // up weights (kGateUp*, kDXs)
   const int32_t* offsets;  // [E+1] expert row offsets
-  const int32_t* tstart;   // [E+1] per-expert m-tile prefix (row-grouped modes)
+  const int32_t* tstart;   // [2 (E+1)] the tile map (tile_starts_block; row-grouped modes)
   int E;
   int M, N, K;  // kDW: output M x N per expert.  Row-grouped: N output cols, K reduction
   int lda, ldb;
@@ -188,16 +188,22 @@ struct GemmArgs {
   // With null, XCD x takes the x-th of kNumXcd equal ranges of the tile list.
   const int32_t* xcd_mt;
   int32_t* xcd_claim;  // chained launches: one flag per (XCD, slot), zero at launch
+  // Row-grouped modes without xcd_mt: 1 = the XCDs take equal tile counts, 0 =
+  // equal tile costs (tile_cost8).  The dXs GEMM, whose last tile wave the
+  // fused launch's dW tiles fill, measured faster with equal counts; the
+  // others with equal costs.
+  int even_split;
 };
 
 // One grouped GEMM of the row-grouped modes (kGateUpH, kGateUpBwd, kDown, kDA).
 // Grid: kNumXcd * rowgrouped_slots(m-tile bound, n_tiles), with a.xcd_mt
 // null; kNumXcd * chain_slots(m-tile bound, n_tiles) with the XCD ranges.
 hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st);
-// Workgroups per XCD of a row-grouped GEMM: the XCD's share of at most
-// mt_bound m-tiles of n_tiles tiles each.
+// Workgroups per XCD of a row-grouped GEMM (the XCDs take equal tile costs,
+// see the tile decode): at most twice an equal share of mt_bound m-tiles of
+// n_tiles tiles each, plus two (no tile costs less than 5/8 of another).
 inline int rowgrouped_slots(int64_t mt_bound, int n_tiles) {
-  return (int)((mt_bound * n_tiles + kNumXcd - 1) / kNumXcd);
+  return (int)(2 * ((mt_bound * n_tiles + kNumXcd - 1) / kNumXcd) + 2);
 }
 // The chained launches' XCD ranges put an m-tile boundary near every
 // kNumXcd-th of the routed rows, at most kChainSlack m-tiles away from an equal
@@ -213,29 +219,30 @@ constexpr int kChainMaxMtPerXcd = 64;
 inline int chain_slots(int64_t mt_bound, int n_tiles) {
   return (int)(((mt_bound + kNumXcd - 1) / kNumXcd + 2 * kChainSlack) * n_tiles);
 }
-// xcd_mt[0 .. kNumXcd] (see GemmArgs::xcd_mt) from the expert row offsets and
-// the m-tile starts (threads 0 .. kNumXcd of the calling block; tstart must be
-// visible to them): xcd_mt[x] is the m-tile boundary nearest to row
-// x R / kNumXcd, clamped to within kChainSlack of x M / kNumXcd (M = tstart[E]),
-// so the ranges are nondecreasing, hold about equal rows, and none holds more
-// than ceil(M / kNumXcd) + 2 kChainSlack m-tiles.
-__device__ inline void chain_bounds_block(const int32_t* __restrict__ offsets,
-                                          const int32_t* __restrict__ tstart, int E,
+// xcd_mt[0 .. kNumXcd] (see GemmArgs::xcd_mt) from the tile map (threads
+// 0 .. kNumXcd of the calling block; tstart, with its cost prefix, must be
+// visible to them): xcd_mt[x] is the m-tile boundary nearest to x / kNumXcd
+// of the m-tiles' total cost (tile_cost8), clamped to within kChainSlack of
+// x M / kNumXcd (M = tstart[E]), so the ranges are nondecreasing, cost about
+// the same, and none holds more than ceil(M / kNumXcd) + 2 kChainSlack m-tiles.
+__device__ inline void chain_bounds_block(const int32_t* __restrict__ tstart, int E,
                                           int32_t* __restrict__ xcd_mt) {
   const int x = threadIdx.x;
   if (x > kNumXcd) return;
-  const int R = offsets[E], M = tstart[E];
+  const int32_t* const cpre = tstart + E + 1;
+  const int M = tstart[E];
   int v = x == 0 ? 0 : M;
   if (x > 0 && x < kNumXcd) {
-    const int64_t t = (int64_t)x * R / kNumXcd;
-    int lo = 0, hi = E;  // offsets[lo] <= t < offsets[hi]
+    const int64_t t = (int64_t)x * cpre[E] / kNumXcd;
+    int lo = 0, hi = E;  // cpre[lo] <= t < cpre[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (offsets[mid] <= t) lo = mid;
+      if (cpre[mid] <= t) lo = mid;
       else hi = mid;
     }
+    // the expert's m-tiles cost 8 each but the last one
     const int mc = tstart[lo + 1] - tstart[lo];
-    const int j = (int)((t - offsets[lo] + kGemmBM / 2) / kGemmBM);
+    const int j = (int)((t - cpre[lo] + 4) / 8);
     v = tstart[lo] + min(j, mc);
     const int base = (int)((int64_t)x * M / kNumXcd);
     v = min(max(v, base - kChainSlack), base + kChainSlack);

@@ -204,7 +204,7 @@ __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t* __restrict
   tile_starts_block(offsets, E, bm, tstart);
   if (xcd_mt) {
     __syncthreads();
-    chain_bounds_block(offsets, tstart, E, xcd_mt);
+    chain_bounds_block(tstart, E, xcd_mt);
   }
 }
 
