@@ -143,6 +143,13 @@ SMALL = {
     "chained_zipf": lambda: (lambda wl: (wl, synth.generate(wl)))(
         synth.Workload("chained_zipf", T=3000, D=128, I=64, E=64, K=8, score=0, seed=134,
                        zipf_s=1.2)),
+    # chained, one expert of 40,000 rows: its m-tiles span every XCD's range
+    # (20 dW row chunks, the two-pass split: router weight 1)
+    "chained_one_expert": lambda: _custom(T=40000, D=64, I=64, E=1, K=1, score=0, seed=135),
+    # chained, 256 experts of which 128 are never chosen: the XCD ranges and the
+    # tile-cost prefix step over runs of empty experts
+    "chained_sparse": lambda: _custom(T=4096, D=64, I=64, E=256, K=8, score=0, seed=136,
+                                      dead=tuple(range(1, 256, 2))),
     # one token
     "one_token": lambda: _custom(T=1, D=64, I=64, E=8, K=2, score=0, seed=107),
     # the maximum expert count: 1024 experts, most of them empty
