@@ -95,13 +95,18 @@ __device__ inline int block_exclusive_scan_1024(int v, int* total) {
   return before + incl - v;
 }
 
-// Cost of one row tile of a row-grouped GEMM with `rows` valid rows, in
-// eighths of a full tile, as the tiles run: with more than 192 rows the full
-// tile's schedule (8); otherwise the weights' half of each stage plus one
-// eighth per 64-row A piece that holds rows (5, 6 or 7).  Experts of 513-541
-// rows, for instance, end in a tile of at most 29 rows that costs 5.
-__device__ __forceinline__ int tile_cost8(int rows) {
-  return rows > 192 ? 8 : 4 + (rows + 63) / 64;
+// Cost of an expert's last row tile in a row-grouped GEMM, in eighths of a
+// full tile, as the tiles run (every other row tile costs 8): with more than
+// 192 rows the full tile's schedule (8).  With fewer, the tile loads only the
+// 64-row A pieces that hold rows; when the expert has other row tiles, which
+// run beside it over the same weight slices (in L2), it costs the weights'
+// half of each stage plus an eighth per piece (5, 6 or 7: experts of 513-541
+// rows end in a tile of at most 29 rows that costs 5).  An expert's only row
+// tile streams its weight slices from memory alone and costs a full tile
+// whatever its rows (measured: weighing those tiles by their rows left the
+// XCD holding the coldest experts of a Zipf routing 30% behind).
+__device__ __forceinline__ int last_tile_cost8(int rows, int tiles) {
+  return rows > 192 || tiles < 2 ? 8 : 4 + (rows + 63) / 64;
 }
 
 // The tile map of the row-grouped GEMMs, [2 (E + 1)] ints:
@@ -109,8 +114,8 @@ __device__ __forceinline__ int tile_cost8(int rows) {
 //     first row tile of expert e in a GEMM's tile list (tstart[E] = the
 //     number of row tiles);
 //   tstart[E + 1 + e] = exclusive prefix of the experts' row-tile costs
-//     (tile_cost8 summed over each expert's row tiles): the cost of a column
-//     tile's pass over the experts before e.
+//     (8 per row tile, last_tile_cost8 for each expert's last): the cost of
+//     a column tile's pass over the experts before e.
 // One workgroup of 1024 threads.
 __device__ inline void tile_starts_block(const int32_t* __restrict__ offsets, int E, int bm,
                                          int32_t* __restrict__ tstart) {
@@ -120,7 +125,7 @@ __device__ inline void tile_starts_block(const int32_t* __restrict__ offsets, in
     const int e = e0 + threadIdx.x;
     const int rows = e < E ? offsets[e + 1] - offsets[e] : 0;
     const int c = (rows + bm - 1) / bm;
-    const int cost = c > 0 ? 8 * (c - 1) + tile_cost8(rows - bm * (c - 1)) : 0;
+    const int cost = c > 0 ? 8 * (c - 1) + last_tile_cost8(rows - bm * (c - 1), c) : 0;
     int total, ctotal;
     const int ex = block_exclusive_scan_1024(c, &total);
     const int cex = block_exclusive_scan_1024(cost, &ctotal);

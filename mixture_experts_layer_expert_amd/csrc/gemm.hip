@@ -344,7 +344,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int xcd, cons
         if (slot >= (hi - lo) * nt) return;
         key = lo * nt + slot;
       } else {
-        // every XCD about the same tile cost (tile_cost8), or with even_split
+        // every XCD about the same tile cost (last_tile_cost8), or with even_split
         // the same tile count (column tiles of one m-tile may then sit on two
         // XCDs): XCD x starts at the tile where the list's cumulative cost
         // reaches x / kNumXcd of the total

@@ -189,7 +189,7 @@ struct GemmArgs {
   const int32_t* xcd_mt;
   int32_t* xcd_claim;  // chained launches: one flag per (XCD, slot), zero at launch
   // Row-grouped modes without xcd_mt: 1 = the XCDs take equal tile counts, 0 =
-  // equal tile costs (tile_cost8).  The dXs GEMM, whose last tile wave the
+  // equal tile costs (last_tile_cost8).  The dXs GEMM, whose last tile wave the
   // fused launch's dW tiles fill, measured faster with equal counts; the
   // others with equal costs.
   int even_split;
@@ -222,7 +222,7 @@ inline int chain_slots(int64_t mt_bound, int n_tiles) {
 // xcd_mt[0 .. kNumXcd] (see GemmArgs::xcd_mt) from the tile map (threads
 // 0 .. kNumXcd of the calling block; tstart, with its cost prefix, must be
 // visible to them): xcd_mt[x] is the m-tile boundary nearest to x / kNumXcd
-// of the m-tiles' total cost (tile_cost8), clamped to within kChainSlack of
+// of the m-tiles' total cost (last_tile_cost8), clamped to within kChainSlack of
 // x M / kNumXcd (M = tstart[E]), so the ranges are nondecreasing, cost about
 // the same, and none holds more than ceil(M / kNumXcd) + 2 kChainSlack m-tiles.
 __device__ inline void chain_bounds_block(const int32_t* __restrict__ tstart, int E,
