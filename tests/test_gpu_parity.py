@@ -497,20 +497,24 @@ def test_gradient_scale_invariance(log2c):
         assert not zero[k].float().any(), k
 
 
-@pytest.mark.parametrize("shape", ["small", "chunked"])
+@pytest.mark.parametrize("shape", ["small", "chunked", "chained"])
 def test_stream_and_graph_capture(shape):
     """Calls run on the caller's stream and can be captured into a graph; replays
     (with eager work in between) reproduce the eager results bit for bit.  The
     chunked case has experts of two and three dW row chunks, all with the split
-    operand.  A last replay after dy is scaled in place by 2^-10 gives the
-    gradients times 2^-10 exactly: the gradient scale is taken anew on every
-    replay."""
+    operand; the chained case runs the chained GEMM launches, whose counters
+    and status word each replay sets anew (the status word stays 0).  A last
+    replay after dy is scaled in place by 2^-10 gives the gradients times 2^-10
+    exactly: the gradient scale is taken anew on every replay."""
     import mixture_experts_layer_expert_amd as moe
     torch = G.torch_mod()
     if shape == "small":
         wl, data = _custom(T=384, D=128, I=128, E=8, K=2, score=0, seed=202)
-    else:
+    elif shape == "chunked":
         wl, data = _custom(T=6000, D=128, I=64, E=4, K=2, score=0, seed=112, hot=0)
+    else:
+        wl, data = SMALL["chained_uniform"]()
+        assert 128 <= _m_tile_bound(wl) <= 512
     dev = G.DeviceInputs(data)
     r_ref, y_ref, g_ref = G.run_gpu(dev, wl.K, wl.score)
     s = torch.cuda.Stream()
@@ -547,6 +551,8 @@ def test_stream_and_graph_capture(shape):
             if a.dtype == torch.bfloat16:
                 a, b = a.view(torch.int16), b.view(torch.int16)
             assert torch.equal(a, b), (rep, k)
+        assert int(ws[1][:4].view(torch.int32).item()) == 0, rep
+        assert int(ws[2][:4].view(torch.int32).item()) == 0, rep
     dev.dy.mul_(2.0 ** -10)
     torch.cuda.synchronize()
     graph.replay()
