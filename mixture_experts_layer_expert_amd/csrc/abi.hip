@@ -210,8 +210,8 @@ size_t router_bwd_ws(const moe_dims& d, RouterBwdWs* w, void* base) {
   return c.used;
 }
 
-int rowgrouped_grid(const moe_dims& d, int n_tiles) {
-  return kNumXcd * rowgrouped_slots(mt_bound(d), n_tiles);
+int rowgrouped_grid(const moe_dims& d, int n_tiles, bool even_split = false) {
+  return kNumXcd * rowgrouped_slots(mt_bound(d), n_tiles, even_split);
 }
 
 // dW grid: (matrix, row chunk) groups of m-tiles x n-tiles, dealt round-robin
@@ -620,7 +620,7 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   gg.Cf2 = dw_up;
   // the three read only the recompute GEMM's outputs: one launch (no tail
   // between them); then the chunk partials
-  MOE_TRY(launch_bwd_fused(gx, R > 0 ? rowgrouped_grid(d, gx.n_tiles) : 0, gd,
+  MOE_TRY(launch_bwd_fused(gx, R > 0 ? rowgrouped_grid(d, gx.n_tiles, gx.even_split != 0) : 0, gd,
                            dw_grid(1, dw_chunks_bound(d), d.D, d.I), gg,
                            dw_grid(2, dw_chunks_bound(d), d.I, d.D), st));
   MOE_TRY(launch_dw_reduce(DwReduceArgs{w.dw_part_down, dw_down, nullptr, 1, d.D, d.I},

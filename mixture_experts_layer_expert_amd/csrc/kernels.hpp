@@ -199,11 +199,13 @@ struct GemmArgs {
 // Grid: kNumXcd * rowgrouped_slots(m-tile bound, n_tiles), with a.xcd_mt
 // null; kNumXcd * chain_slots(m-tile bound, n_tiles) with the XCD ranges.
 hipError_t launch_gemm(int mode, const GemmArgs& a, int grid, hipStream_t st);
-// Workgroups per XCD of a row-grouped GEMM (the XCDs take equal tile costs,
-// see the tile decode): at most twice an equal share of mt_bound m-tiles of
-// n_tiles tiles each, plus two (no tile costs less than 5/8 of another).
-inline int rowgrouped_slots(int64_t mt_bound, int n_tiles) {
-  return (int)(2 * ((mt_bound * n_tiles + kNumXcd - 1) / kNumXcd) + 2);
+// Workgroups per XCD of a row-grouped GEMM over at most mt_bound m-tiles of
+// n_tiles tiles each: with equal tile counts (even_split) an equal share;
+// with equal tile costs (see the tile decode) at most twice that, plus two
+// (no tile costs less than 5/8 of another).
+inline int rowgrouped_slots(int64_t mt_bound, int n_tiles, bool even_split = false) {
+  const int64_t share = (mt_bound * n_tiles + kNumXcd - 1) / kNumXcd;
+  return (int)(even_split ? share : 2 * share + 2);
 }
 // The chained launches' XCD ranges put an m-tile boundary near every
 // kNumXcd-th of the routed rows, at most kChainSlack m-tiles away from an equal
