@@ -60,11 +60,12 @@ def kernel_work(wl: synth.Workload) -> dict:
         "gemm_fwd_chain": ("mfma", 6 * dir_), "gemm_da_recompute": ("mfma", 6 * dir_),
         # combine: read O (R*D*2), weights and indices (8R), write y (T*D*2)
         "combine": ("hbm", 2.0 * R * D + 8 * R + 2.0 * T * D),
-        # dX reduce: read the fp16 per-row partials (R*D*2), write dX (T*D*2)
-        "reduce_rows": ("hbm", 2.0 * R * D + 2.0 * T * D),
-        # dRouterWeights: read the per-row partials (one per gate/up column tile and wave
-        # column, 4 * ceil(I / 128) per row) and the indices, write one value per row
-        "reduce_partials": ("hbm", 4.0 * R * (4 * math.ceil(I / 128)) + 8 * R),
+        # dX reduce: read the fp16 per-row partials (R*D*2), write dX (T*D*2); in the
+        # same launch dRouterWeights: read the per-row partials (one per gate/up column
+        # tile and wave column, 4 * ceil(I / 128) per row) and the indices, write one
+        # value per row
+        "reduce_rows": ("hbm", 2.0 * R * D + 2.0 * T * D
+                        + 4.0 * R * (4 * math.ceil(I / 128)) + 8 * R),
         "route_topk": ("hbm", 4.0 * T * E + 8 * R),
         "route_hist": ("hbm", 4.0 * R),
         # scatter: read the ids (4R) and the histogram table once, write both permutations (8R)

@@ -628,9 +628,8 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
                            w.pstart, w.cstart, d.E, (int)dw_max_chunked(d), st));
 
   if (R > 0) {
-    MOE_TRY(launch_reduce_rows(w.dxs, w.gscale, dx, d.T, d.K, d.D, st));
-    MOE_TRY(launch_reduce_partials(w.part, flat_to_sorted, d_topk_w, (int)R,
-                                   partials_per_row(d), st));
+    MOE_TRY(launch_reduce_rows(w.dxs, w.gscale, dx, d.T, d.K, d.D, w.part, flat_to_sorted,
+                               d_topk_w, partials_per_row(d), st));
   }
   return MOE_OK;
 }

@@ -9,7 +9,7 @@ namespace moe {
 // ---- per-kernel timing (prof.hip)
 enum KernelId : int {
   kKRouteTopk, kKRouteHist, kKRouteScatter, kKTilemap,
-  kKGemmGateUpH, kKGemmGateUpGU, kKGemmDown, kKGemmDA, kKCombine, kKReduceRows, kKReducePartials, kKRouterLogits,
+  kKGemmGateUpH, kKGemmGateUpGU, kKGemmDown, kKGemmDA, kKCombine, kKReduceRows, kKRouterLogits,
   kKRouterPrep, kKRouterDx, kKRouterDwr, kKRouterDwrSum, kKDwReduce, kKBwdSetup, kKDyAmax,
   kKF16Operands, kKGemmBwdFused, kKGemmFwdChain, kKGemmBwdChain, kNumKernels
 };
@@ -45,11 +45,11 @@ hipError_t launch_tilemap(const int32_t* offsets, int E, int bm, int32_t* tstart
 hipError_t launch_combine(const void* O, const float* w, const int32_t* f2s, void* y, int T,
                           int K, int D, hipStream_t st);
 // dx[t] = (1/s) sum_k dXs[t*K + k] with dXs the fp16 rows of s dXs and 1/s =
-// gscale[1] (fp32 sum, k ascending, one bf16 rounding).
+// gscale[1] (fp32 sum, k ascending, one bf16 rounding); in the same launch
+// d_topk_w[f] = sum_{j<np} part[f2s[f] * np + j] (j ascending).
 hipError_t launch_reduce_rows(const void* dXs, const float* gscale, void* dx, int T, int K, int D,
+                              const float* part, const int32_t* f2s, float* d_topk_w, int np,
                               hipStream_t st);
-hipError_t launch_reduce_partials(const float* part, const int32_t* f2s, float* out, int R,
-                                  int np, hipStream_t st);
 // Largest |v| over the n bf16 values of src (n a multiple of 8): kAmaxBlocks
 // workgroup maxima (bit patterns of |v|, ordered like the values) into part.
 constexpr int kAmaxBlocks = 1024;

@@ -75,15 +75,32 @@ __global__ __launch_bounds__(kPermuteThreads) void combine_kernel(
 // they are read once (non-temporal loads).  Each thread produces 8 outputs
 // from one 16-byte read per routed copy; with KT > 0 all K reads are in
 // flight together.  cpr8 = D / 8.
+//
+// The first npart_blocks workgroups (dispatched first, so they overlap the
+// streaming ones) instead reduce the router-weight gradient partials:
+// d_topk_w[f] = sum_{j<np} part[flat_to_sorted[f] * np + j]   (j ascending).
 template <int KT>
 __global__ __launch_bounds__(kPermuteThreads) void reduce_rows_kernel(
     const u32x4* __restrict__ dXs, const float* __restrict__ gscale, u32x4* __restrict__ dx,
-    int T, int K_, int cpr8) {
+    int T, int K_, int cpr8, const float* __restrict__ part, const int32_t* __restrict__ f2s,
+    float* __restrict__ dtw, int np, int npart_blocks) {
   const int K = KT > 0 ? KT : K_;
+  if ((int)blockIdx.x < npart_blocks) {
+    const int R = T * K;
+    for (int f = blockIdx.x * kPermuteThreads + threadIdx.x; f < R;
+         f += npart_blocks * kPermuteThreads) {
+      const float* pp = part + (size_t)f2s[f] * np;
+      float s = 0.0f;
+      for (int j = 0; j < np; ++j) s += pp[j];
+      dtw[f] = s;
+    }
+    return;
+  }
   const float inv = gscale[1];
   const size_t total = (size_t)T * cpr8;
-  for (size_t c = (size_t)blockIdx.x * kPermuteThreads + threadIdx.x; c < total;
-       c += (size_t)gridDim.x * kPermuteThreads) {
+  const size_t nb = gridDim.x - npart_blocks;
+  for (size_t c = (size_t)(blockIdx.x - npart_blocks) * kPermuteThreads + threadIdx.x; c < total;
+       c += nb * kPermuteThreads) {
     const size_t t = c / cpr8;
     const int j = (int)(c - t * cpr8);
     const u32x4* rows = dXs + t * K * cpr8 + j;
@@ -108,19 +125,6 @@ __global__ __launch_bounds__(kPermuteThreads) void reduce_rows_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) out[q] = pack_bf16x2(a[2 * q] * inv, a[2 * q + 1] * inv);
     dx[c] = out;
-  }
-}
-
-// d_topk_w[f] = sum_{j<np} part[flat_to_sorted[f] * np + j]   (fixed order)
-__global__ __launch_bounds__(kPermuteThreads) void reduce_partials_kernel(
-    const float* __restrict__ part, const int32_t* __restrict__ f2s, float* __restrict__ out,
-    int R, int np) {
-  for (int f = blockIdx.x * kPermuteThreads + threadIdx.x; f < R;
-       f += gridDim.x * kPermuteThreads) {
-    const float* p = part + (size_t)f2s[f] * np;
-    float s = 0.0f;
-    for (int j = 0; j < np; ++j) s += p[j];
-    out[f] = s;
   }
 }
 
@@ -206,13 +210,17 @@ hipError_t launch_combine(const void* O, const float* w, const int32_t* f2s, voi
 }
 
 hipError_t launch_reduce_rows(const void* dXs, const float* gscale, void* dx, int T, int K, int D,
+                              const float* part, const int32_t* f2s, float* d_topk_w, int np,
                               hipStream_t st) {
   const int cpr8 = D / 8;
   if (T == 0) return hipSuccess;
-  const dim3 grid(grid_for((size_t)T * cpr8)), block(kPermuteThreads);
+  const size_t R = (size_t)T * K;
+  // one thread per routed row for the partial sums, at most 256 workgroups
+  const int npart = (int)std::min<size_t>(256, (R + kPermuteThreads - 1) / kPermuteThreads);
+  const dim3 grid(npart + grid_for((size_t)T * cpr8)), block(kPermuteThreads);
 #define MOE_REDUCE(KT)                                                                     \
   MOE_LAUNCH(kKReduceRows, reduce_rows_kernel<KT>, grid, block, 0, st, (const u32x4*)dXs, \
-             gscale, (u32x4*)dx, T, K, cpr8)
+             gscale, (u32x4*)dx, T, K, cpr8, part, f2s, d_topk_w, np, npart)
   switch (K) {
     case 1: MOE_REDUCE(1); break;
     case 2: MOE_REDUCE(2); break;
@@ -221,14 +229,6 @@ hipError_t launch_reduce_rows(const void* dXs, const float* gscale, void* dx, in
     default: MOE_REDUCE(0); break;
   }
 #undef MOE_REDUCE
-  return hipGetLastError();
-}
-
-hipError_t launch_reduce_partials(const float* part, const int32_t* f2s, float* out, int R,
-                                  int np, hipStream_t st) {
-  if (R == 0) return hipSuccess;
-  MOE_LAUNCH(kKReducePartials, reduce_partials_kernel, dim3(grid_for((size_t)R)), dim3(kPermuteThreads), 0,
-                     st, part, f2s, out, R, np);
   return hipGetLastError();
 }
 

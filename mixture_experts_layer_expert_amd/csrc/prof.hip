@@ -38,7 +38,7 @@ const char* const kNames[kNumKernels] = {
     "route_topk",   "route_hist",    "route_scatter", "tilemap",
     "gemm_gateup_h", "gemm_gateup_gu", "gemm_down",    "gemm_da",
     "combine",      "reduce_rows",
-    "reduce_partials", "router_logits", "router_prep",  "router_dx",
+    "router_logits", "router_prep",  "router_dx",
     "router_dwr",   "router_dwr_sum", "dw_reduce",   "bwd_setup",    "dy_amax",
     "f16_operands", "gemm_bwd_fused", "gemm_fwd_chain", "gemm_da_recompute"};
 
