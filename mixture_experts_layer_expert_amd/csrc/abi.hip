@@ -15,6 +15,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxE = 1024;
+static_assert(kMaxE <= kChunkMapMaxE, "the dW chunk map takes one expert per thread");
 constexpr int kMaxK = 64;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -95,7 +96,7 @@ struct BwdWs {
   f16_t *dgu, *hw;        // fp16 operands of the gradient GEMMs (rounded values)
   f16_t *dgu_lo, *hw_lo;  // their low parts (value - rounded value), for the dW GEMMs
   uint32_t* rowoff;       // byte offset of each routed row's token row in x / dy
-  int32_t *cstart, *pstart, *slist;  // dW row-chunk map
+  int32_t *cstart, *pstart, *slist, *corder;  // dW row-chunk map
   int32_t* dw_split;      // per-expert flag: dW operand split hi + lo
   uint32_t* amax_part;    // partial maxima of |dy|
   float* gscale;          // gradient scale {s, 1/s}
@@ -179,6 +180,7 @@ size_t bwd_ws(const moe_dims& d, BwdWs* w, void* base) {
   w->cstart = c.take<int32_t>(d.E + 1);
   w->pstart = c.take<int32_t>(d.E);
   w->slist = c.take<int32_t>(d.E + 1);
+  w->corder = c.take<int32_t>(dw_chunks_bound(d));
   w->dw_split = c.take<int32_t>(d.E);
   w->amax_part = c.take<uint32_t>(kAmaxBlocks);
   w->gscale = c.take<float>(2);
@@ -480,6 +482,7 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   sa.cstart = w.cstart;
   sa.pstart = w.pstart;
   sa.slist = w.slist;
+  sa.corder = w.corder;
   sa.rowoff = w.rowoff;
   const bool chain = use_chain(d);
   sa.zero = w.chain;
@@ -584,6 +587,7 @@ MOE_EXPORT moe_status moe_bwd(const moe_dims* dims, const void* x, const void* w
   gd.E = d.E;
   gd.cstart = w.cstart;
   gd.pstart = w.pstart;
+  gd.corder = w.corder;
   gd.dw_part = w.dw_part_down;
   gd.dw_split = w.dw_split;
   gd.gscale = w.gscale;

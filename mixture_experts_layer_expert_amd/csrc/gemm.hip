@@ -393,19 +393,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int xcd, cons
       nk = p.K / BK;
     } else {
       // dW: the tm x tn tiles of one (matrix, row chunk) group stay on one XCD
-      // (they share the chunk's operands in L2), and the groups are dealt to
-      // the XCDs round-robin, so the heavy chunks of a hot expert spread.
-      // Tiles: (matrix, row chunk, m-tile, n-tile); the chunks of expert e are
-      // cstart[e] .. cstart[e+1]-1
+      // (they share the chunk's operands in L2).  The groups, heaviest chunk
+      // first (corder; a chunk's matrices side by side), are dealt to the
+      // XCDs in snake order (0..7, 7..0, ...), which evens out the XCDs' dW
+      // work when a few hot experts hold most rows; every XCD takes one group
+      // per row of 8 and starts with its heaviest.  The chunks of expert e
+      // are cstart[e] .. cstart[e+1]-1.
       const int tm = ceil_div(p.M, BM), tn = ceil_div(p.N, BN);
       const int per_c = tm * tn;
       const int nchunk = p.cstart[p.E];
-      const int tile = ((slot / per_c) * kNumXcd + xcd) * per_c + slot % per_c;
-      if (tile >= p.nmat * nchunk * per_c) return;
-      mat = tile / (nchunk * per_c);
-      const int rem = tile - mat * nchunk * per_c;
-      const int gc = rem / per_c;
-      const int r2 = rem - gc * per_c;
+      const int row = slot / per_c;
+      const int pos = row * kNumXcd + ((row & 1) ? kNumXcd - 1 - xcd : xcd);
+      if (pos >= p.nmat * nchunk) return;
+      const int rank = pos / p.nmat;
+      mat = pos - rank * p.nmat;
+      const int gc = p.corder[rank];
+      const int r2 = slot - row * per_c;
       e = expert_of(p.cstart, [](int v) { return v; }, gc);  // cstart[e] <= gc < cstart[e+1]
       dw_chunk = gc - p.cstart[e];
       if (dw_chunk > 0) dw_slot = p.pstart[e] + dw_chunk - 1;
@@ -1138,52 +1141,46 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void b
 // dW row chunks: nch_e = max(1, ceil(rows_e / kDwChunkRows)); cstart =
 // exclusive prefix of nch (cstart[E] = total); pstart = exclusive prefix of
 // (nch_e - 1) (the partial slots of chunks 1..); slist = the experts with
-// nch_e > 1 in ascending order, their number in slist[E].  Deterministic
-// (integer scans).
+// nch_e > 1 in ascending order, their number in slist[E].  corder = the chunk
+// ids heaviest first, the order in which the dW grids deal their (matrix,
+// chunk) groups to the XCDs: every chunk of kDwChunkRows rows in chunk order,
+// then each expert's one shorter chunk (rows_e mod kDwChunkRows rows, or its
+// only chunk when it has no rows) by rows descending, ties by expert.
+// Deterministic (integer scans and ranks); one expert per thread, so
+// E <= kChunkMapMaxE.
 __device__ void dw_chunkmap_block(const int32_t* __restrict__ offsets, int E,
                                   int32_t* __restrict__ cstart, int32_t* __restrict__ pstart,
-                                  int32_t* __restrict__ slist) {
-  __shared__ int wsum[3][16];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int carry[3] = {0, 0, 0};
-  for (int e0 = 0; e0 < E; e0 += 1024) {
-    const int e = e0 + tid;
-    const int rows = e < E ? offsets[e + 1] - offsets[e] : 0;
-    const int nch = e < E ? max(1, (rows + kDwChunkRows - 1) / kDwChunkRows) : 0;
-    const int v[3] = {nch, nch > 1 ? nch - 1 : 0, nch > 1 ? 1 : 0};
-    int incl[3], ex[3], tot[3];
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      incl[q] = v[q];
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl[q], off);
-        if (lane >= off) incl[q] += o;
+                                  int32_t* __restrict__ slist, int32_t* __restrict__ corder) {
+  __shared__ int key[kChunkMapMaxE];
+  const int e = threadIdx.x;
+  const int rows = e < E ? offsets[e + 1] - offsets[e] : 0;
+  const int nch = e < E ? max(1, (rows + kDwChunkRows - 1) / kDwChunkRows) : 0;
+  const int full = rows / kDwChunkRows;  // chunks of kDwChunkRows rows
+  int nchunk, npart, nlist, nfull;
+  const int c0 = block_exclusive_scan_1024(nch, &nchunk);
+  const int p0 = block_exclusive_scan_1024(nch > 1 ? nch - 1 : 0, &npart);
+  const int s0 = block_exclusive_scan_1024(nch > 1 ? 1 : 0, &nlist);
+  const int f0 = block_exclusive_scan_1024(full, &nfull);
+  key[e] = nch > full ? rows - full * kDwChunkRows : -1;  // the shorter chunk's rows, if any
+  __syncthreads();
+  if (e < E) {
+    cstart[e] = c0;
+    pstart[e] = p0;
+    if (nch > 1) slist[s0] = e;
+    for (int c = 0; c < full; ++c) corder[f0 + c] = c0 + c;
+    const int k = key[e];
+    if (k >= 0) {
+      int rank = 0;
+      for (int j = 0; j < E; ++j) {
+        const int kj = key[j];
+        rank += kj > k || (kj == k && j < e);
       }
-      if (lane == 63) wsum[q][wv] = incl[q];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      int before = 0;
-      tot[q] = 0;
-      for (int i = 0; i < 16; ++i) {
-        if (i < wv) before += wsum[q][i];
-        tot[q] += wsum[q][i];
-      }
-      ex[q] = carry[q] + before + incl[q] - v[q];
-      carry[q] += tot[q];
-    }
-    __syncthreads();
-    if (e < E) {
-      cstart[e] = ex[0];
-      pstart[e] = ex[1];
-      if (nch > 1) slist[ex[2]] = e;
+      corder[nfull + rank] = c0 + full;
     }
   }
-  if (tid == 0) {
-    cstart[E] = carry[0];
-    slist[E] = carry[2];
+  if (e == 0) {
+    cstart[E] = nchunk;
+    slist[E] = nlist;
   }
 }
 
@@ -1250,7 +1247,7 @@ __global__ __launch_bounds__(1024) void bwd_setup_kernel(BwdSetupArgs a) {
       chain_bounds_block(a.tstart, a.E, a.xcd_mt);
     }
   } else if (b == a.E + 1) {
-    dw_chunkmap_block(a.offsets, a.E, a.cstart, a.pstart, a.slist);
+    dw_chunkmap_block(a.offsets, a.E, a.cstart, a.pstart, a.slist, a.corder);
   } else {
     // rowoff[p] = (s2f[p] / K) * row_bytes
     const int nb = gridDim.x - (a.E + 2);

@@ -101,6 +101,8 @@ constexpr float kDwSplitRows = 100.0f;
 // accumulates into) the output; chunks 1.. write partial tiles that a
 // reduction then adds in chunk order.
 constexpr int kDwChunkRows = 2048;
+// the dW row-chunk map takes one expert per thread of a 1024-thread workgroup
+constexpr int kChunkMapMaxE = 1024;
 // L2 prefetch distance in stages: each stage touches the lines of the stage
 // kGemmPrefetch after the one it loads.
 constexpr int kGemmPrefetch = 1;
@@ -139,6 +141,7 @@ struct GemmArgs {
   // expert's chunks 1..; dw_part partial tiles [slot][nmat][M][N] fp32
   const int32_t* cstart;
   const int32_t* pstart;
+  const int32_t* corder;  // kDW: the chunk ids heaviest first (dw_chunkmap_block)
   float* dw_part;
   const int32_t* dw_split;  // [E] 1: the expert's dW operand is split hi + lo
   // backward gradient scale {s, 1/s} (see launch_bwd_setup), or null (s = 1):
@@ -290,7 +293,8 @@ hipError_t launch_bwd_fused(const GemmArgs& dxs, int g1, const GemmArgs& dw_down
 //     launch_tilemap);
 //   the dW row-chunk map: cstart [E+1] (chunk prefix), pstart [E] (first
 //     partial slot of each expert's chunks 1..), slist [E+1] (the chunked
-//     experts ascending, their number in slist[E]);
+//     experts ascending, their number in slist[E]), corder [chunk bound]
+//     (the chunk ids heaviest first: the dW grids' dealing order);
 //   rowoff [R]: rowoff[p] = (s2f[p] / K) * row_bytes, the byte offset of
 //     routed row p's token row in x16 and dy16.
 struct BwdSetupArgs {
@@ -304,6 +308,7 @@ struct BwdSetupArgs {
   int32_t* cstart;
   int32_t* pstart;
   int32_t* slist;
+  int32_t* corder;  // [dw chunk bound] chunk ids, heaviest first
   uint32_t* rowoff;
   int32_t* zero;  // zero[0 .. nzero) = 0: the chained launch's status word and counters
   int nzero;
