@@ -100,7 +100,7 @@ constexpr float kDwSplitRows = 100.0f;
 // tiles are spread over the GPU like everyone else's.  Chunk 0 writes (or
 // accumulates into) the output; chunks 1.. write partial tiles that a
 // reduction then adds in chunk order.
-constexpr int kDwChunkRows = 2048;
+constexpr int kDwChunkRows = 4096;
 // the dW row-chunk map takes one expert per thread of a 1024-thread workgroup
 constexpr int kChunkMapMaxE = 1024;
 // L2 prefetch distance in stages: each stage touches the lines of the stage

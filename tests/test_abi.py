@@ -71,7 +71,7 @@ def test_operand_size_limit(lib):
 
 
 def test_backward_workspace_holds_dw_chunk_partials(lib):
-    """The backward workspace grows by ceil(R / 2048) partial dW tiles of 3*I*D
+    """The backward workspace grows by ceil(R / 4096) partial dW tiles of 3*I*D
     fp32 (dW_gate | dW_up, and dW_down apart, since the two dW GEMMs run in one
     launch) as the routed rows grow (the dW row chunks of hot experts)."""
     a = moe.moe_workspace_bytes(moe.dims(8192, 2048, 768, 128, 8), 2)

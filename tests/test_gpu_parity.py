@@ -90,12 +90,12 @@ SMALL = {
     "ragged_cols": lambda: _custom(T=300, D=320, I=64, E=16, K=3, score=0, seed=102),
     # many routed copies per token (K = 16 of 64 experts)
     "k16": lambda: _custom(T=96, D=128, I=64, E=64, K=16, score=0, seed=108),
-    # a hot expert of more than 2048 rows (two dW row chunks) beside three
+    # a hot expert of more than 4096 rows (two dW row chunks) beside three
     # smaller ones, all four with the two-pass dW split, every element compared
-    "split_hot": lambda: _custom(T=3000, D=128, I=64, E=4, K=2, score=0, seed=109, hot=0),
-    # every expert above 2048 rows, the hot one above 4096: three and two dW row
+    "split_hot": lambda: _custom(T=6000, D=128, I=64, E=4, K=2, score=0, seed=109, hot=0),
+    # every expert above 4096 rows, the hot one above 8192: three and two dW row
     # chunks (partial tiles added in chunk order), all with the two-pass split
-    "chunks3": lambda: _custom(T=6000, D=128, I=64, E=4, K=2, score=0, seed=112, hot=0),
+    "chunks3": lambda: _custom(T=12500, D=128, I=64, E=4, K=2, score=0, seed=112, hot=0),
     # skewed routing: one hot expert, three experts never chosen
     "skew_empty": lambda: _custom(T=500, D=128, I=128, E=8, K=2, score=0, seed=103, hot=1,
                                   dead=(2, 5, 7)),
@@ -120,7 +120,7 @@ SMALL = {
     # dXs GEMM, 16-stage ones in dA), every expert in one m-tile
     "wide_experts": lambda: _custom(T=300, D=256, I=1024, E=4, K=2, score=0, seed=113),
     # three experts at router weight 1 (K = 1), all with the two-pass dW split:
-    # a hot one of about 5,900 rows (three dW row chunks) beside two of about
+    # a hot one of about 5,900 rows (two dW row chunks) beside two of about
     # 1,500, every element compared
     "split_chunks_k1": lambda: _custom(T=9000, D=64, I=64, E=3, K=1, score=0, seed=130, hot=0),
     # last row tiles at every boundary of the padding-aware stages (64-row A
@@ -129,9 +129,9 @@ SMALL = {
     "tile_boundaries": lambda: _exact_counts([1, 63, 64, 65, 192, 193, 256, 257, 448, 449],
                                              D=128, I=64, seed=131),
     # the skewed-sweep routing (a Zipf(1.2) log-prior over the experts) at a
-    # small size, every element compared: two hot experts above 2048 rows (two
-    # dW row chunks each), 8 experts with the split dW operand and 24 with one
-    # pass, the coldest with 2 rows
+    # small size, every element compared: two hot experts of 2,800 and 2,200
+    # rows, 8 experts with the split dW operand and 24 with one pass, the
+    # coldest with 2 rows
     "zipf_small": lambda: (lambda wl: (wl, synth.generate(wl)))(
         synth.Workload("zipf_small", T=3000, D=128, I=64, E=32, K=4, score=0, seed=132,
                        zipf_s=1.2)),
@@ -144,7 +144,7 @@ SMALL = {
         synth.Workload("chained_zipf", T=3000, D=128, I=64, E=64, K=8, score=0, seed=134,
                        zipf_s=1.2)),
     # chained, one expert of 40,000 rows: its m-tiles span every XCD's range
-    # (20 dW row chunks, the two-pass split: router weight 1)
+    # (10 dW row chunks, the two-pass split: router weight 1)
     "chained_one_expert": lambda: _custom(T=40000, D=64, I=64, E=1, K=1, score=0, seed=135),
     # chained, 256 experts of which 128 are never chosen: the XCD ranges and the
     # tile-cost prefix step over runs of empty experts
@@ -416,7 +416,7 @@ def test_qwen3_30b_a3b_max_tokens():
     """The largest batch at the Qwen3-30B-A3B layer shape: T = 65535 tokens,
     524,280 routed rows, whose widest routed-row operands sit just under the
     2 GiB limit of the GEMMs' 32-bit offsets.  3,688-4,617 rows per expert:
-    every dW tile takes two or three row chunks and the split operand."""
+    one or two dW row chunks, every expert with the split operand."""
     wl = synth.Workload("qwen3_30b_a3b_T65535", T=65535, D=2048, I=768, E=128, K=8,
                         score=synth.SOFTMAX_TOPK, seed=5)
     _sampled_compare(wl, n_tokens=8, n_entries=16)
@@ -511,7 +511,7 @@ def test_stream_and_graph_capture(shape):
     if shape == "small":
         wl, data = _custom(T=384, D=128, I=128, E=8, K=2, score=0, seed=202)
     elif shape == "chunked":
-        wl, data = _custom(T=6000, D=128, I=64, E=4, K=2, score=0, seed=112, hot=0)
+        wl, data = _custom(T=12500, D=128, I=64, E=4, K=2, score=0, seed=112, hot=0)
     else:
         wl, data = SMALL["chained_uniform"]()
         assert 128 <= _m_tile_bound(wl) <= 512

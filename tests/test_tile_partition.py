@@ -23,14 +23,14 @@ Every (m-tile, column tile) must be run exactly once, within the grid, and in
 a chained launch on the XCD whose range holds its m-tile.
 
 The weight-gradient GEMMs (gemm.hip dW decode, dw_chunkmap_block): expert e's
-rows split into chunks of at most 2048 rows (at least one chunk); the chunk
+rows split into chunks of at most 4096 rows (at least one chunk); the chunk
 list runs expert by expert; corder lists the chunks heaviest first (the
-2048-row chunks in list order, then each expert's shorter chunk by rows
+4096-row chunks in list order, then each expert's shorter chunk by rows
 descending, ties by expert); the (chunk, matrix) groups in that order are
 dealt to the XCDs in snake order (row r of 8 groups: XCD x takes group
 8r + x for even r, 8r + 7 - x for odd r), and an XCD's slot s runs tile
 s mod per_c of its group s div per_c.  The grid holds ceil(nmat * (E +
-ceil(R / 2048)) / 8) * per_c slots per XCD.
+ceil(R / 4096)) / 8) * per_c slots per XCD.
 """
 import bisect
 
@@ -188,7 +188,7 @@ def test_scout_routing_costs_balance():
     assert max(costs) <= 1.03 * np.mean(costs)
 
 
-CH = 2048
+CH = 4096
 
 
 def chunk_map(counts):
@@ -246,7 +246,7 @@ def test_dw_snake_dealing_balances_skewed_routing():
     heaviest first in snake order never leaves an XCD more loaded than dealing
     them round-robin in list order, and with at least 32768 routed rows keeps
     every XCD within 3% of the mean (round-robin: 4-9% over).  With fewer rows
-    one 2048-row chunk can outweigh the rest of its XCD's share."""
+    one 4096-row chunk can outweigh the rest of its XCD's share."""
     rng = np.random.default_rng(7)
     p = 1.0 / np.arange(1, 129) ** 1.2
     for R in (8192, 32768, 65536, 131072):
