@@ -1184,9 +1184,10 @@ __device__ void dw_chunkmap_block(const int32_t* __restrict__ offsets, int E,
   }
 }
 
-// Expert e: S = sum of topk_w[s2f[r]]^2 over the expert's n rows r, threads
-// 0..255 each summing a fixed stride of rows, then a fixed tree, and
-// split[e] = S * (1 + kDwSplitRows / n) * dim_factor > kDwSplitW2.
+// Expert e: S = sum of topk_w[s2f[r]]^2 over the expert's n rows r, each of
+// the 1024 threads summing a fixed stride of rows (four loads in flight),
+// then a fixed tree, and split[e] = S * (1 + kDwSplitRows / n) * dim_factor >
+// kDwSplitW2.
 // Workgroup 0 also turns the kAmaxBlocks partial maxima of |dy| into the
 // gradient scale {s, 1/s}: s = 2^(1 - x) for max|dy| = m 2^x, m in [0.5, 1),
 // with x clamped to [-64, 64]; s = 1 when dy is all zero or not finite.
@@ -1194,19 +1195,32 @@ __device__ void bwd_prep_block(int e, const int32_t* __restrict__ offsets,
                                const int32_t* __restrict__ s2f, const float* __restrict__ topk_w,
                                float dim_factor, const uint32_t* __restrict__ amax_part,
                                int32_t* __restrict__ split, float* __restrict__ gscale) {
-  __shared__ float wsum[4];
+  __shared__ float wsum[16];
   __shared__ uint32_t wmax[4];
   const int tid = threadIdx.x;
   const int r0 = offsets[e], r1 = offsets[e + 1];
-  if (tid < 256) {
+  {
     float s = 0.0f;
-    for (int r = r0 + tid; r < r1; r += 256) {
+    int r = r0 + tid;
+    for (; r + 3 * 1024 < r1; r += 4 * 1024) {
+      int f[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = s2f[r + i * 1024];
+      float w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = topk_w[f[i]];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s += w[i] * w[i];
+    }
+    for (; r < r1; r += 1024) {
       const float w = topk_w[s2f[r]];
       s += w * w;
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
     if ((tid & 63) == 0) wsum[tid >> 6] = s;
+  }
+  if (tid < 256) {
     if (e == 0) {
       uint32_t m = 0;
       for (int b = tid; b < kAmaxBlocks; b += 256) m = max(m, amax_part[b]);
@@ -1217,7 +1231,10 @@ __device__ void bwd_prep_block(int e, const int32_t* __restrict__ offsets,
   }
   __syncthreads();
   if (tid == 0) {
-    const float sw2 = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    float q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = (wsum[4 * i] + wsum[4 * i + 1]) + (wsum[4 * i + 2] + wsum[4 * i + 3]);
+    const float sw2 = (q[0] + q[1]) + (q[2] + q[3]);
     const int n = r1 - r0;
     split[e] = n > 0 && sw2 * (1.0f + kDwSplitRows / (float)n) * dim_factor > kDwSplitW2 ? 1 : 0;
   }
@@ -1264,32 +1281,43 @@ hipError_t launch_bwd_setup(const BwdSetupArgs& a, hipStream_t st) {
 }
 
 // The chunked experts' weight gradients, both reductions in one launch:
-// workgroup (i, stripe, z) adds, for the chunked expert e = slist[i] and the
-// reduction z (0: dW_down from part_down, 1: dW_gate and dW_up from part),
-// out_mat[e] += sum_{c >= 1} part[pstart[e] + c - 1][mat]  (c ascending),
-// striding over the expert's nmat * M * N elements, 4 per thread.
+// workgroup (stripe, z) adds, for every chunked expert e = slist[i] in turn
+// and the reduction z (0: dW_down from part_down, 1: dW_gate and dW_up from
+// part), out_mat[e] += sum_{c >= 1} part[pstart[e] + c - 1][mat]  (c
+// ascending), striding over the expert's nmat * M * N elements, 4 per thread
+// and two such groups in flight.  Partial tiles are read once (non-temporal).
+constexpr int kDwReduceStripes = 512;
 __global__ __launch_bounds__(256) void dw_reduce_kernel(DwReduceArgs a0, DwReduceArgs a1,
                                                         const int32_t* __restrict__ slist,
                                                         const int32_t* __restrict__ pstart,
                                                         const int32_t* __restrict__ cstart,
                                                         int E) {
-  const int i = blockIdx.x;
-  if (i >= slist[E]) return;
-  const DwReduceArgs& a = blockIdx.z == 0 ? a0 : a1;
-  const int e = slist[i];
-  const int nch = cstart[e + 1] - cstart[e];
+  const int nlist = slist[E];
+  const DwReduceArgs& a = blockIdx.y == 0 ? a0 : a1;
   const int nmat = a.nmat;
   const size_t mn = (size_t)a.M * a.N;  // a multiple of 4 (N is a multiple of 64)
-  const size_t slot0 = (size_t)pstart[e];
-  for (size_t q = ((size_t)blockIdx.y * 256 + threadIdx.x) * 4; q < nmat * mn;
-       q += (size_t)gridDim.y * 256 * 4) {
+  const size_t total = (size_t)nmat * mn;
+  const size_t step = (size_t)gridDim.x * 256 * 4;
+  auto add = [&](int e, int nch, size_t slot0, size_t q) {
     const int mat = q >= mn ? 1 : 0;
     const size_t idx = q - mat * mn;
+    float* o = (mat == 0 ? a.out0 : a.out1) + (size_t)e * mn + idx;
+    const f32x4 prev = *(const f32x4*)o;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     for (int c = 1; c < nch; ++c)
-      s += *(const f32x4*)(a.part + ((slot0 + c - 1) * nmat + mat) * mn + idx);
-    float* o = (mat == 0 ? a.out0 : a.out1) + (size_t)e * mn + idx;
-    *(f32x4*)o = *(const f32x4*)o + s;
+      s += __builtin_nontemporal_load((const f32x4*)(a.part + ((slot0 + c - 1) * nmat + mat) * mn + idx));
+    *(f32x4*)o = prev + s;
+  };
+  for (int i = 0; i < nlist; ++i) {
+    const int e = slist[i];
+    const int nch = cstart[e + 1] - cstart[e];
+    const size_t slot0 = (size_t)pstart[e];
+    size_t q = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    for (; q + step < total; q += 2 * step) {
+      add(e, nch, slot0, q);
+      add(e, nch, slot0, q + step);
+    }
+    if (q < total) add(e, nch, slot0, q);
   }
 }
 
@@ -1297,7 +1325,7 @@ hipError_t launch_dw_reduce(const DwReduceArgs& down, const DwReduceArgs& gateup
                             const int32_t* slist, const int32_t* pstart, const int32_t* cstart,
                             int E, int max_chunked, hipStream_t st) {
   if (max_chunked <= 0) return hipSuccess;
-  MOE_LAUNCH(kKDwReduce, dw_reduce_kernel, dim3(max_chunked, 64, 2), dim3(256), 0, st, down,
+  MOE_LAUNCH(kKDwReduce, dw_reduce_kernel, dim3(kDwReduceStripes, 2), dim3(256), 0, st, down,
              gateup, slist, pstart, cstart, E);
   return hipGetLastError();
 }
