@@ -128,6 +128,11 @@ SMALL = {
     # 256, 257, 448 and 449 rows
     "tile_boundaries": lambda: _exact_counts([1, 63, 64, 65, 192, 193, 256, 257, 448, 449],
                                              D=128, I=64, seed=131),
+    # experts at the dW row-chunk boundaries (router weight 1, so all take the
+    # split operand): exactly one and two 4096-row chunks (no shorter chunk),
+    # one row over a chunk, one row, and an empty expert; the chunk list then
+    # holds full chunks, a one-row remainder and empty experts' chunks together
+    "chunk_boundaries": lambda: _exact_counts([4096, 8192, 4097, 1, 0], D=64, I=64, seed=137),
     # the skewed-sweep routing (a Zipf(1.2) log-prior over the experts) at a
     # small size, every element compared: two hot experts of 2,800 and 2,200
     # rows, 8 experts with the split dW operand and 24 with one pass, the

@@ -127,7 +127,8 @@ def decode(xcd, slot, nt, tstart, cpre, xcd_mt=None, even=False):
 def routings():
     rng = np.random.default_rng(20)
     out = [[537, 538, 486, 539, 530, 523, 541, 489, 518, 480, 524, 514, 494, 495, 492, 492],
-           [1, 63, 64, 65, 192, 193, 256, 257, 448, 449], [40000], [0, 0, 5, 0]]
+           [1, 63, 64, 65, 192, 193, 256, 257, 448, 449], [40000], [0, 0, 5, 0],
+           [4096, 8192, 4097, 1, 0], [4095, 4096, 12288, 0, 0, 3]]
     for _ in range(24):
         E = int(rng.choice([1, 3, 8, 16, 128, 300]))
         R = int(rng.integers(1, 40000))
