@@ -216,11 +216,11 @@ inline int rowgrouped_slots(int64_t mt_bound, int n_tiles, bool even_split = fal
 // bound per XCD lies in [kChainMinMtPerXcd, kChainMaxMtPerXcd]: with fewer, one
 // m-tile more or less unbalances the XCDs; with more, the last tile wave that
 // chaining fills is a small share of the launch, while the per-tile waits and
-// signals and the coarser XCD split grow with the tile count (measured at the
-// Qwen shape with Zipf-skewed routing over 16384 tokens: +1.1% per step).
+// signals grow with the tile count (measured at the Qwen shape with
+// Zipf-skewed routing over 16384 tokens, 80 m-tiles per XCD: -1.1% per step).
 constexpr int kChainSlack = 3;
 constexpr int kChainMinMtPerXcd = 16;
-constexpr int kChainMaxMtPerXcd = 64;
+constexpr int kChainMaxMtPerXcd = 128;
 inline int chain_slots(int64_t mt_bound, int n_tiles) {
   return (int)(((mt_bound + kNumXcd - 1) / kNumXcd + 2 * kChainSlack) * n_tiles);
 }
