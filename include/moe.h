@@ -170,7 +170,7 @@ moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, cons
  * router-weight gradient come out of that recompute GEMM's epilogue; the
  * routed rows of x and dy are gathered inside the GEMMs' operand loads.  Each
  * weight-gradient tile reduces over its expert's rows in chunks of at most
- * 2048 rows, one workgroup per chunk; the chunks' partial tiles are added in
+ * 4096 rows, one workgroup per chunk; the chunks' partial tiles are added in
  * chunk order (no atomics, deterministic).  The weight-gradient GEMMs multiply
  * fp16 operands; for an expert with n rows whose squared router weights sum
  * to S, with S * (1 + 100 / n) * max(1, 3 D / (8 I)) > 16, the rounded

@@ -216,8 +216,9 @@ int rowgrouped_grid(const moe_dims& d, int n_tiles, bool even_split = false) {
   return kNumXcd * rowgrouped_slots(mt_bound(d), n_tiles, even_split);
 }
 
-// dW grid: (matrix, row chunk) groups of m-tiles x n-tiles, dealt round-robin
-// to the XCDs; enough workgroups per XCD for its share of the chunk bound
+// dW grid: (row chunk, matrix) groups of m-tiles x n-tiles, one group per XCD
+// in every row of kNumXcd groups (snake order); enough workgroups per XCD for
+// its share of the chunk bound
 int dw_grid(int nmat, int64_t chunks, int M, int N) {
   const int64_t per_c = (int64_t)((M + kGemmBM - 1) / kGemmBM) * ((N + kGemmBN - 1) / kGemmBN);
   const int64_t groups = (int64_t)nmat * chunks;

@@ -73,7 +73,8 @@
 //   - XCD-aware tile order: workgroup b runs on XCD b % 8, so each XCD takes a
 //     contiguous range of the (expert, column tile, row tile) list and the
 //     tiles sharing one expert's operands share that XCD's L2; the dW GEMMs
-//     deal their (matrix, row chunk) groups of tiles to the XCDs round-robin;
+//     deal their (row chunk, matrix) groups of tiles to the XCDs heaviest
+//     chunk first, in snake order (XCDs 0..7, then 7..0, ...);
 //   - L2 prefetch: each stage also touches the lines of a later stage (one
 //     4-byte DMA per lane into a scratch LDS area), either every tile its own
 //     lines one stage ahead, or, for gate/up and down when the launch asks

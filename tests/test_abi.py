@@ -75,7 +75,7 @@ def test_backward_workspace_holds_dw_chunk_partials(lib):
     fp32 (dW_gate | dW_up, and dW_down apart, since the two dW GEMMs run in one
     launch) as the routed rows grow (the dW row chunks of hot experts)."""
     a = moe.moe_workspace_bytes(moe.dims(8192, 2048, 768, 128, 8), 2)
-    b = moe.moe_workspace_bytes(moe.dims(8192 + 256, 2048, 768, 128, 8), 2)  # +2048 rows
+    b = moe.moe_workspace_bytes(moe.dims(8192 + 256, 2048, 768, 128, 8), 2)  # +2048 routed rows
     per_row = 2 * 2048 * 2 + 2 * 768 * (4 + 2 * 2 + 2 * 2) + 2048 * 4 + 4 * 4 * 3
     assert b - a >= 3 * 768 * 2048 * 4          # one more partial slot at least
     assert b - a <= 2048 * per_row + 3 * 768 * 2048 * 4 + 4096
