@@ -164,7 +164,9 @@ moe_status moe_fwd(const moe_dims *dims, const void *x, const void *w_gate, cons
  *   dw_up     device fp32 [E, I, D] out: dL/dW_up
  *   dw_down   device fp32 [E, D, I] out: dL/dW_down
  *   d_topk_w  device fp32 [T, K]   out: dL/dtopk_w[t,k] = <dy[t], o[t,k]>
- *   accumulate_dw  0: overwrite dw_*;  1: add into dw_* (fp32)
+ *   accumulate_dw  0: overwrite dw_*;  1: add into dw_* (fp32; for an expert
+ *                  whose rows span several dW row chunks, the first chunk's
+ *                  tile is added, then the sum of the others: two roundings)
  * dA = dOu W_down runs first (fp32); the gate/up activations are then
  * recomputed (not read from the forward), and the SwiGLU backward and the
  * router-weight gradient come out of that recompute GEMM's epilogue; the

@@ -476,6 +476,33 @@ def test_bitwise_determinism_and_overwrite():
         assert torch.equal(out[k], 2 * g1[k]), k
 
 
+def test_accumulate_with_row_chunks():
+    """accumulate_dw on experts whose rows span several dW chunks: the first
+    chunk's tile adds into the gradient, then the chunk reduction adds the
+    other chunks' sum, so dW + dW comes out as 2 dW up to those two fp32
+    roundings; the token-side outputs are bitwise those of an overwriting
+    call, and empty experts keep what the gradient held."""
+    import mixture_experts_layer_expert_amd as moe
+    torch = G.torch_mod()
+    wl, data = SMALL["chunk_boundaries"]()
+    dev = G.DeviceInputs(data)
+    route, _, g1 = G.run_gpu(dev, wl.K, wl.score)
+    out = {k: v.clone() for k, v in g1.items()}
+    moe.moe_bwd(dev.x, dev.w_gate, dev.w_up, dev.w_down, route, dev.dy, wl.K, wl.score, out=out,
+                accumulate_dw=True)
+    torch.cuda.synchronize()
+    for k in ("dx", "d_topk_w"):
+        a, b = g1[k], out[k]
+        if a.dtype == torch.bfloat16:
+            a, b = a.view(torch.int16), b.view(torch.int16)
+        assert torch.equal(a, b), k
+    for k in ("dw_gate", "dw_up", "dw_down"):
+        ref = 2 * g1[k].double()
+        err = (out[k].double() - ref).abs()
+        assert float(err.max()) <= 2.0 ** -21 * float(ref.abs().max()), k
+        assert not out[k][4].any(), f"{k} of the empty expert"
+
+
 @pytest.mark.parametrize("log2c", [-20, 16])
 def test_gradient_scale_invariance(log2c):
     """The backward of dy * 2^c is 2^c times the backward of dy, bit for bit:
